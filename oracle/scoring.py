@@ -1,0 +1,147 @@
+"""Per-block scoring: normalise, EMA/LRFU, touch, priority, tier (fp64).
+
+Steps, each a plain elementwise definition over the per-(sequence, block)
+records:
+
+* normalise: m_hat = mass / max over the sequence's blocks of mass, so the
+  hottest block of each sequence scores 1 (the pages leave the scale of the
+  EMA input open; this is the reading taken).
+* EMA: E <- alpha * m_hat + (1 - alpha) * E, starting from E = 0
+  (Visual Reference Sec. 11, Diagram 11.1 update rule; Diagram 11.2's
+  worked example starts from 0).  alpha is LRFU's LRU/LFU knob.
+* touch: every record of every sequence in the step was read by the
+  decode, so its touch count grows by one and its touch timestamp becomes
+  the caller's step number (GQA Per-Head Scoring Streams, per-block state:
+  touch count and touch timestamp; under dense attention every block of an
+  active sequence is read every step, Visual Reference Sec. 4).
+* priority: P = w_R * R + w_E * E + w_N * N with R = (b + 1) / nb (recency
+  of logical block b among the sequence's nb blocks) and N = 1 for anchor
+  blocks b < anchor_blocks (Visual Reference Sec. 12, Diagram 12.1:
+  0.25 / 0.55 / 0.20).
+* tier: 0 (pinned) when P >= t_high, 1 (HBM evictable) when P >= t_low,
+  else 2 (CXL) (Visual Reference Sec. 12, Diagram 12.2 cut points 0.3 and
+  0.6; Sec. 10 tier names).  Tier 3 is never assigned by P.
+
+A record whose touch timestamp is not older than the new step is left
+unchanged and reported (steps must increase).
+
+Parity pins (tests/test_oracle_scoring.py): the printed EMA worked example,
+the EMA closed form on constant input, the printed half-life, closed-form
+tier sets derived by solving the threshold inequalities, exact cut-point
+inclusivity, touch arithmetic.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+NEVER = np.uint64(0xFFFF_FFFF_FFFF_FFFF)
+UNCLASSIFIED = np.uint8(0xFF)
+
+
+@dataclasses.dataclass(frozen=True)
+class Policy:
+    alpha: float
+    w_recency: float = 0.25
+    w_ema: float = 0.55
+    w_anchor: float = 0.20
+    t_low: float = 0.3
+    t_high: float = 0.6
+    anchor_blocks: int = 1
+
+
+@dataclasses.dataclass
+class ScoreState:
+    """One entry per (sequence, logical block), in record order."""
+    seq_id: np.ndarray      # uint64, identity key part 1
+    block: np.ndarray       # uint64, identity key part 2 (logical block index)
+    nblocks: np.ndarray     # int64, blocks of the owning sequence
+    seq_index: np.ndarray   # int64, batch slot of the owning sequence
+    score: np.ndarray       # float64, EMA E
+    t_touch: np.ndarray     # uint64, NEVER before the first touch
+    touch_count: np.ndarray  # uint32
+    priority: np.ndarray    # float64, last P (0 before the first classify)
+    tier: np.ndarray        # uint8, UNCLASSIFIED before the first classify
+    anchor: np.ndarray      # bool
+
+    def copy(self) -> "ScoreState":
+        return ScoreState(**{f.name: getattr(self, f.name).copy()
+                             for f in dataclasses.fields(self)})
+
+
+def init_state(blocks_per_seq, seq_ids, anchor_blocks: int = 1) -> ScoreState:
+    seq_index = np.concatenate([np.full(nb, s, dtype=np.int64)
+                                for s, nb in enumerate(blocks_per_seq)])
+    block = np.concatenate([np.arange(nb, dtype=np.int64) for nb in blocks_per_seq])
+    nblocks = np.concatenate([np.full(nb, nb, dtype=np.int64) for nb in blocks_per_seq])
+    n = block.size
+    return ScoreState(
+        seq_id=np.asarray(seq_ids, dtype=np.uint64)[seq_index],
+        block=block.astype(np.uint64),
+        nblocks=nblocks,
+        seq_index=seq_index,
+        score=np.zeros(n, dtype=np.float64),
+        t_touch=np.full(n, NEVER, dtype=np.uint64),
+        touch_count=np.zeros(n, dtype=np.uint32),
+        priority=np.zeros(n, dtype=np.float64),
+        tier=np.full(n, UNCLASSIFIED, dtype=np.uint8),
+        anchor=block < anchor_blocks,
+    )
+
+
+def normalise(mass_seq):
+    """Block mass divided by the sequence's largest block mass."""
+    mass_seq = np.asarray(mass_seq, dtype=np.float64)
+    top = mass_seq.max()
+    if top <= 0.0:
+        return np.zeros_like(mass_seq)
+    return mass_seq / top
+
+
+def ema(prev, x, alpha: float):
+    """score_t = alpha * x_t + (1 - alpha) * score_{t-1}."""
+    return alpha * np.asarray(x, dtype=np.float64) + (1.0 - alpha) * np.asarray(prev, dtype=np.float64)
+
+
+def recency(block, nblocks):
+    return (np.asarray(block, dtype=np.float64) + 1.0) / np.asarray(nblocks, dtype=np.float64)
+
+
+def priority(score, block, nblocks, anchor, pol: Policy):
+    return (pol.w_recency * recency(block, nblocks)
+            + pol.w_ema * np.asarray(score, dtype=np.float64)
+            + pol.w_anchor * np.asarray(anchor, dtype=np.float64))
+
+
+def tier_of(p, pol: Policy):
+    p = np.asarray(p, dtype=np.float64)
+    return np.where(p >= pol.t_high, 0, np.where(p >= pol.t_low, 1, 2)).astype(np.uint8)
+
+
+def classify(state: ScoreState, pol: Policy) -> ScoreState:
+    out = state.copy()
+    out.priority = priority(state.score, state.block, state.nblocks, state.anchor, pol)
+    out.tier = tier_of(out.priority, pol)
+    return out
+
+
+def score_update(state: ScoreState, masses, step: int, pol: Policy, do_classify: bool = True):
+    """One scoring step.  masses: list of per-sequence block-mass arrays.
+
+    Returns (new_state, stale) where stale marks records left unchanged
+    because their touch timestamp was not older than `step`.
+    """
+    out = state.copy()
+    m_hat = np.concatenate([normalise(m) for m in masses])
+    step_u = np.uint64(step)
+    stale = (state.t_touch != NEVER) & (state.t_touch >= step_u)
+    upd = ~stale
+    out.score[upd] = ema(state.score[upd], m_hat[upd], pol.alpha)
+    out.touch_count[upd] = state.touch_count[upd] + np.uint32(1)
+    out.t_touch[upd] = step_u
+    if do_classify:
+        p = priority(out.score, out.block, out.nblocks, out.anchor, pol)
+        out.priority[upd] = p[upd]
+        out.tier[upd] = tier_of(p, pol)[upd]
+    return out, stale
