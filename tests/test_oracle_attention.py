@@ -184,3 +184,22 @@ def test_recipe_locality_shows_in_mass():
     middle = mass[8:50].mean()
     assert mass[0] > 1.1 * middle
     assert mass[-6:].mean() > 1.1 * middle
+
+
+def test_saturated_logits_stay_finite():
+    """A logit gap far beyond exp's range must give an exact one-hot weight
+    (the softmax is evaluated relative to its largest logit)."""
+    n, hot = 40, 17
+    m, q = _small([n])
+    pool = m.pool.clone()
+    g = 6
+    for b in range(m.blocks[0]):
+        pool[int(m.table_host[0, b]), 0, 0, g] = 0.0
+    pid_hot = int(m.table_host[0, hot // 16])
+    pool[pid_hot, 0, 0, g, hot % 16, 0] = 60000.0
+    q = torch.zeros_like(q)
+    q[0, 0, 8 * g, 0] = 60000.0
+    out, masses = OA.decode_step(q.numpy(), pool.numpy(), m.table_host, m.lens, SCALE)
+    _, V = _loop_gather(pool.numpy(), m.table_host[0], n, 0, g)
+    assert np.array_equal(out[0, 0, 8 * g], V[hot])
+    assert np.isfinite(masses[0]).all()
