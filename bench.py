@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Benchmark of one paged GQA decode + block-scoring step on one MI355X.
+
+A step is the whole hot path over one batch: paged decode attention with
+per-block mass (kvs_decode_step), then the fused score update and
+classification of every per-block record (kvs_score_update, classify=1).
+Inputs (pool, tables, the step's queries) are resident in HBM before the
+timed region starts.
+
+Prints one JSON line:
+  value          KV GB/s: logical K+V bytes one step reads / step time
+  blocks_per_s   records scored per second
+  roofline       the decode kernel alone, timed with HIP events recorded by
+                 the library around its launch on the bench's stream
+  cpu_baseline   the fp64 oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import resource
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, published
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SRC = os.path.join(ROOT, "paged_gqa_kv_amd", "csrc", "kvs_kernels.hip")
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=16)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="decode-80L-128K")
+    ap.add_argument("--alpha", type=float, default=None)
+    ap.add_argument("--split-blocks", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="approximate CPU time budget of the oracle baseline (0 = skip)")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime already loaded by torch."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return ev.value
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+def _traffic(workload: str, split_blocks: int):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"paged_decode_gqa_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    with open(KERNEL_SRC, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("kernel_sha256") != digest or rec.get("split_blocks") != split_blocks:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def _cpu_baseline(m, alpha, budget_s):
+    """The fp64 oracle (as it stands) on the first layers of step 0 of the same
+    workload, until about budget_s seconds of work; scaled to KV GB/s."""
+    import numpy as np
+    import torch
+
+    import workload as W
+    from oracle import attention as OA
+    from oracle import scoring as OS
+
+    q = W.make_query(m, 0).cpu().numpy()
+    scale = 1.0 / math.sqrt(128.0)
+    L = m.num_layers
+    r0 = resource.getrusage(resource.RUSAGE_SELF)
+    t0 = time.perf_counter()
+    copy_s = 0.0
+    layers_done = 0
+    kv_bytes = 0
+    masses = [np.zeros(nb) for nb in m.blocks]
+    for layer in range(L):
+        tc = time.perf_counter()
+        pool_l = {}
+        # device -> host copy of this layer's blocks (reported apart from the oracle time)
+        for s in range(m.batch):
+            pids = torch.from_numpy(m.table_host[s, :m.blocks[s]].astype(np.int64)).to(m.pool.device)
+            pool_l[s] = m.pool[pids, layer].cpu().numpy()[:, None]   # [nb][1][2][8][16][128]
+        copy_s += time.perf_counter() - tc
+        for s in range(m.batch):
+            tbl = np.arange(m.blocks[s])
+            _, ms = OA.decode_layer(q[s, layer], pool_l[s], tbl, m.lens[s], 0, scale)
+            masses[s] += ms
+            kv_bytes += m.lens[s] * 8 * 128 * 2 * 2
+        layers_done += 1
+        if time.perf_counter() - t0 - copy_s >= budget_s:
+            break
+    st = OS.init_state(m.blocks, list(range(m.batch)))
+    OS.score_update(st, masses, 0, OS.Policy(alpha=alpha))
+    wall = time.perf_counter() - t0 - copy_s
+    r1 = resource.getrusage(resource.RUSAGE_SELF)
+    cpu = (r1.ru_utime - r0.ru_utime) + (r1.ru_stime - r0.ru_stime)
+    cores = max(1, round(cpu / max(wall + copy_s, 1e-9)))
+    return {
+        "value": kv_bytes / wall / 1e9,
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"fp64 oracle decode of layers 0..{layers_done - 1} of {L} for all "
+                   f"{m.batch} sequence(s) of step 0, plus scoring of all {m.total_blocks} "
+                   f"records; {wall:.1f} s of oracle time excluding {copy_s:.1f} s of "
+                   f"device-to-host copy; host has {os.cpu_count()} logical CPUs"),
+        "seconds": wall,
+        "step_seconds_extrapolated": wall * L / layers_done,
+    }
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this path shards by "
+              "sequence or by block range across GPUs, which is not built here.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workload as W
+    from paged_gqa_kv_amd import api
+    from paged_gqa_kv_amd.session import DecodeSession
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
+        sys.exit(1)
+    wl = W.WORKLOADS[args.workload]
+    alpha = args.alpha if args.alpha is not None else wl.alphas[0]
+    print(f"[bench] materialising {wl.name} on cuda:0", file=sys.stderr, flush=True)
+    t0 = time.time()
+    m = W.materialise(wl, "cuda")
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready in {time.time() - t0:.1f} s; pool {m.pool.numel() * 2 / 2**30:.2f} GiB",
+          file=sys.stderr, flush=True)
+    sess = DecodeSession(m, split_blocks=args.split_blocks)
+    pol = api.policy(alpha)
+    n_q = args.warmup + args.steps
+    queries = [W.make_query(m, k) for k in range(n_q)]
+    torch.cuda.synchronize()
+
+    ev = HipEvents()
+    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+
+    # warm-up on the same buffers; records are re-initialised afterwards so the
+    # timed steps start from fresh records with steps 0..K-1
+    for k in range(args.warmup):
+        sess.step(queries[k], k, pol)
+    torch.cuda.synchronize()
+    sess.reset_meta()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for k in range(args.steps):
+        api.set_decode_events(*pairs[k])
+        sess.step(queries[args.warmup + k], k, pol)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    api.set_decode_events(None, None)
+    total_ms = start.elapsed_time(end)
+    decode_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+
+    status = sess.status()
+    if status:
+        raise RuntimeError(f"device status bits set: {status:#x}")
+    # sanity: every (layer, head) softmax sums to one, so each sequence's block
+    # mass sums to layers x 64
+    mass = sess.mass.cpu().numpy().astype(np.float64)
+    offs = m.meta_offsets.cpu().numpy()
+    for s in range(m.batch):
+        tot = mass[offs[s]:offs[s + 1]].sum()
+        if not math.isclose(tot, m.num_layers * 64, rel_tol=1e-4):
+            raise RuntimeError(f"block mass of sequence {s} sums to {tot}")
+    rec = sess.records()
+    if not (rec["touch_count"] == args.steps).all() or not (rec["t_touch"] == args.steps - 1).all():
+        raise RuntimeError("touch counts / timestamps do not match the steps run")
+
+    kv_bytes = sess.kv_bytes_per_step
+    unique_bytes = m.unique_blocks * 16 * m.num_layers * 8 * 128 * 2 * 2
+    t_step = total_ms / 1e3 / args.steps
+    value = kv_bytes / t_step / 1e9
+    dec_avg = sum(decode_ms) / len(decode_ms) / 1e3
+    achieved = kv_bytes / dec_avg / 1e9
+    if achieved > HBM_PEAK_GBPS and unique_bytes == kv_bytes:
+        raise RuntimeError(f"measured {achieved:.0f} GB/s exceeds the HBM peak: a timing bug")
+    traffic = _traffic(wl.name, sess.split_blocks)
+    tiers = np.bincount(rec["tier"], minlength=3)[:3].tolist()
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        print("[bench] timing the oracle baseline", file=sys.stderr, flush=True)
+        cpu = _cpu_baseline(m, alpha, args.cpu_seconds)
+
+    line = {
+        "metric": "KV GB/s read + blocks scored/s per decode step; % of MI355X HBM peak",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "layers": m.num_layers,
+            "batch": m.batch,
+            "context_tokens": int(sum(m.lens)),
+            "records": m.total_blocks,
+            "alpha": alpha,
+            "split_blocks": sess.split_blocks,
+            "kv_bytes_per_step": kv_bytes,
+            "unique_kv_bytes_per_step": unique_bytes,
+            "parallelism": "single GPU",
+        },
+        "blocks_scored_per_s": round(m.total_blocks / t_step, 1),
+        "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
+        "decode_kernel_ms": round(dec_avg * 1e3, 4),
+        "decode_share_of_step": round(dec_avg / t_step, 4),
+        "tier_counts": tiers,
+        "host_wall_s": round(wall, 4),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_decode_gqa",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

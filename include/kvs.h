@@ -1,0 +1,245 @@
+/*
+ * kvs.h -- C ABI of the MI355X (gfx950) paged GQA decode + block-scoring library.
+ *
+ * What the library computes, per decode step:
+ *
+ *  1. Paged decode attention.  For every sequence s, layer l and query head h,
+ *     the step's query attends over all n_s cached positions of the sequence.
+ *     Position t lives in physical block block_table[s][t / 16] at slot t % 16
+ *     ("KV cache offload" architecture post, "Top row": fixed-size blocks and a
+ *     per-sequence table from logical positions to physical block ids).  Query
+ *     head h reads KV head h / 8 (GQA Per-Head Scoring Streams, panel 1:
+ *     Q0-Q7 -> KV-head 0 ... Q56-Q63 -> KV-head 7).  out = softmax(scale q.K) V
+ *     (KV-Cache Offloading for LLM Inference -- Visual Reference, Sec. 2,
+ *     Diagram 2.2).  No mask other than the sequence length; no rotary encoding.
+ *
+ *  2. Block mass.  In the same step the probability mass that every
+ *     (layer, query head) puts on each 16-token block is summed into one fp32
+ *     number per (sequence, logical block): the 640 (layer, KV-head) streams of
+ *     the 80-layer model reduced to one score per block (GQA Per-Head Scoring
+ *     Streams, panel 2).  The sum over streams is this library's reading of the
+ *     page's unnamed aggregation.
+ *
+ *  3. Scoring.  Per (sequence, block) record: normalise the mass by the
+ *     sequence's largest block mass, EMA/LRFU update
+ *     E <- alpha m_hat + (1 - alpha) E (Visual Reference Sec. 11, Diagram 11.1),
+ *     touch count += 1, touch timestamp = step, priority
+ *     P = w_R (b+1)/nb + w_E E + w_N anchor (Sec. 12, Diagram 12.1) and tier
+ *     0 if P >= t_high, 1 if P >= t_low, else 2 (Sec. 12, Diagram 12.2).
+ *
+ * Conventions for every entry point:
+ *  - Device pointers are caller-owned device memory.  The library allocates
+ *    nothing, frees nothing and keeps no device state between calls.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *    compute call only enqueues work on that stream; results are valid once the
+ *    stream reaches them.  Only kvs_device_status() synchronises.
+ *  - Return value: KVS_OK (0) or a negative kvs_status.  Every argument that can
+ *    be checked on the host is checked before anything is enqueued; on error
+ *    nothing is launched and kvs_last_error() holds a message (thread-local).
+ *  - Errors only visible in device data (a physical block id outside the pool,
+ *    a sequence longer than its table row, inconsistent record offsets, a step
+ *    that does not advance) never cause an out-of-bounds access: the offending
+ *    block, sequence or record is skipped and a bit is OR-ed into a sticky
+ *    status word at the start of the workspace (read it with
+ *    kvs_device_status()).
+ *  - Calls on different streams are safe when their outputs and workspaces are
+ *    disjoint.
+ */
+#ifndef KVS_H
+#define KVS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KVS_OK = 0,
+    KVS_E_NULL = -1,       /* a required pointer is NULL */
+    KVS_E_SHAPE = -2,      /* head shape other than 64 / 8 / 128 / 16, or num_layers < 1 */
+    KVS_E_RANGE = -3,      /* a count or index argument is out of range */
+    KVS_E_ALIGN = -4,      /* a tensor is not 16-byte aligned */
+    KVS_E_WORKSPACE = -5,  /* workspace smaller than the matching *_workspace_bytes() */
+    KVS_E_POLICY = -6,     /* alpha not in (0, 1], a negative weight, cut points not 0 <= t_low <= t_high */
+    KVS_E_HIP = -7         /* the HIP runtime reported an error while enqueuing */
+} kvs_status;
+
+/* Sticky device status bits (kvs_device_status). */
+#define KVS_DEV_BAD_BLOCK_ID   0x1u  /* a table entry outside [0, pool_blocks): block skipped */
+#define KVS_DEV_BAD_SEQ_LEN    0x2u  /* seq_len < 0 or > 16 * max_blocks_per_seq: sequence skipped */
+#define KVS_DEV_BAD_OFFSETS    0x4u  /* meta_offsets inconsistent with seq_lens / total_blocks */
+#define KVS_DEV_STALE_STEP     0x8u  /* step <= a record's touch timestamp: record left unchanged */
+
+/* Model head shape.  The kernels support num_q_heads 64, num_kv_heads 8,
+ * head_dim 128, block_tokens 16 and any num_layers >= 1 (Visual Reference
+ * Sec. 1, Architecture Parameters). */
+typedef struct {
+    int32_t num_layers;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t block_tokens;
+} kvs_shape;
+
+/* Scoring parameters.  The pages call every one of these uncalibrated and
+ * illustrative (Visual Reference Sec. 12), so all are runtime values.
+ * Defaults from the pages: w_recency 0.25, w_ema 0.55, w_anchor 0.20,
+ * t_low 0.3, t_high 0.6; alpha 0.05 (simulated optimum) or 0.15 (specified),
+ * Sec. 11. */
+typedef struct {
+    double alpha;
+    double w_recency;
+    double w_ema;
+    double w_anchor;
+    double t_low;
+    double t_high;
+} kvs_policy;
+
+/* The 64-byte per-block record (GQA Per-Head Scoring Streams, "Per-block state
+ * (64 bytes)": 16 B identity key, 8 B score, 8 B touch timestamp, 4 B touch
+ * count, reserved).  The library keeps the tier label, an anchor flag and the
+ * last priority inside the reserved bytes. */
+typedef struct {
+    uint64_t key[2];       /*  0: identity {seq_id, logical block index}; survives eviction */
+    double   score;        /* 16: EMA/LRFU score E, starts at 0 */
+    uint64_t t_touch;      /* 24: step of the last touch; UINT64_MAX = never touched */
+    uint32_t touch_count;  /* 32: decode steps that read the block */
+    uint8_t  tier;         /* 36: 0 pinned HBM, 1 evictable HBM, 2 CXL; 0xFF = unclassified */
+    uint8_t  flags;        /* 37: bit 0 = anchor-zone block */
+    uint16_t reserved0;    /* 38 */
+    double   priority;     /* 40: last P; 0 before the first classification */
+    uint8_t  reserved1[16];/* 48 */
+} kvs_block_meta;
+
+#define KVS_NEVER_TOUCHED  UINT64_MAX
+#define KVS_UNCLASSIFIED   0xFFu
+#define KVS_FLAG_ANCHOR    0x1u
+
+/* ---- host-only helpers (no GPU needed) ---------------------------------- */
+
+/* KV bytes of one token: 2 (K and V) x layers x KV heads x head_dim x 2 B
+ * (Visual Reference Sec. 3, Diagram 3.1).  0 if shape is NULL. */
+size_t kvs_bytes_per_token(const kvs_shape* shape);
+
+/* Bytes of one physical block: block_tokens x kvs_bytes_per_token(). */
+size_t kvs_block_bytes(const kvs_shape* shape);
+
+/* sizeof(kvs_block_meta) (64).  When offsets != NULL and n >= 9, writes the byte
+ * offsets of key, score, t_touch, touch_count, tier, flags, reserved0,
+ * priority, reserved1. */
+size_t kvs_meta_layout(size_t* offsets, int n);
+
+/* Blocks per split used by kvs_decode_step for this problem when
+ * split_blocks == 0 is passed (a power of two in [16, 256]); otherwise
+ * split_blocks itself if valid, or 0 if invalid. */
+int32_t kvs_decode_split_blocks(const kvs_shape* shape, int32_t batch,
+                                int32_t max_blocks_per_seq, int32_t layer_begin,
+                                int32_t layer_end, int32_t split_blocks);
+
+/* Workspace bytes kvs_decode_step needs for these sizes (0 on invalid input).
+ * The workspace holds a 256-byte status header, the per-split softmax
+ * statistics and partial outputs, and the per-(layer, head, block) mass
+ * partials: about 4 x 64 x (layer_end - layer_begin) x total_blocks bytes. */
+size_t kvs_decode_workspace_bytes(const kvs_shape* shape, int32_t batch,
+                                  int32_t max_blocks_per_seq, int64_t total_blocks,
+                                  int32_t layer_begin, int32_t layer_end,
+                                  int32_t split_blocks);
+
+/* Workspace bytes kvs_score_update needs (status header + per-chunk maxima). */
+size_t kvs_score_workspace_bytes(int32_t batch, int32_t max_blocks_per_seq);
+
+const char* kvs_status_string(int code);
+const char* kvs_last_error(void);
+
+/* Measurement hook.  With both events non-NULL (hipEvent_t passed as void*),
+ * every later kvs_decode_step call on this host thread records `before` on its
+ * stream just before the paged decode kernel and `after` just after it, so a
+ * caller can time that kernel alone.  kvs_set_decode_events(NULL, NULL) turns
+ * it off.  Returns KVS_E_NULL when exactly one event is NULL. */
+int kvs_set_decode_events(void* before, void* after);
+
+/* ---- device entry points ------------------------------------------------- */
+
+/* Zero the 256-byte status header of a workspace (decode or score).  Call once
+ * after allocating a workspace.  Enqueues one small kernel. */
+int kvs_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/* Waits for `stream`, copies the sticky status word of `workspace` to *bits and
+ * clears it.  The only synchronising call. */
+int kvs_device_status(void* workspace, void* stream, uint32_t* bits);
+
+/* One paged GQA decode step plus block mass, for layers [layer_begin, layer_end).
+ *
+ *  q             fp16 [batch][num_layers][64][128], device, 16-B aligned.
+ *  kv_pool       fp16 [pool_blocks][num_layers][2][8][16][128], device, 16-B
+ *                aligned.  Index [p][l][0] holds keys, [p][l][1] values; slot
+ *                o of block p is position 16 b + o of every sequence whose
+ *                table maps logical block b to p.
+ *  block_table   int32 [batch][max_blocks_per_seq], device: physical block id
+ *                of each logical block.  Entries past a sequence's end are not read.
+ *  seq_lens      int32 [batch], device: tokens per sequence (0 allowed).
+ *  meta_offsets  int32 [batch + 1], device: record index of (s, b) is
+ *                meta_offsets[s] + b; meta_offsets[s+1] - meta_offsets[s] must be
+ *                ceil(seq_lens[s] / 16) and meta_offsets[batch] <= total_blocks.
+ *  total_blocks  host copy of the number of records.
+ *  scale         softmax scale (1/sqrt(128) for the pages' model).
+ *  out           fp16 [batch][num_layers][64][128], device: rows of layers in
+ *                range are overwritten; other rows are not touched.
+ *  block_mass    fp32 [total_blocks], device: sum over layers in range, all 64
+ *                query heads and the block's tokens of the softmax probability.
+ *                accumulate == 0 overwrites, 1 adds (for per-layer-range calls).
+ *  split_blocks  blocks per split-K work item; 0 = library choice.  Must match
+ *                the value given to kvs_decode_workspace_bytes.
+ *  workspace     device scratch of kvs_decode_workspace_bytes() bytes, 256-B
+ *                aligned, status header zeroed once by kvs_workspace_init().
+ */
+int kvs_decode_step(const kvs_shape* shape,
+                    const void* q,
+                    const void* kv_pool, int64_t pool_blocks,
+                    const int32_t* block_table, int32_t max_blocks_per_seq,
+                    const int32_t* seq_lens, const int32_t* meta_offsets,
+                    int32_t batch, int64_t total_blocks,
+                    int32_t layer_begin, int32_t layer_end,
+                    float scale,
+                    void* out, float* block_mass, int accumulate,
+                    int32_t split_blocks,
+                    void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Initialise records [0, total_blocks): key = {seq_ids[s], b}, score 0,
+ * t_touch = KVS_NEVER_TOUCHED, touch_count 0, tier = KVS_UNCLASSIFIED,
+ * flags = KVS_FLAG_ANCHOR when b < anchor_blocks, priority 0, reserved 0.
+ * seq_ids: uint64 [batch], device.  anchor_blocks >= 0. */
+int kvs_meta_init(kvs_block_meta* meta, const int32_t* meta_offsets,
+                  const uint64_t* seq_ids, int32_t batch,
+                  int32_t max_blocks_per_seq, int64_t total_blocks,
+                  int32_t anchor_blocks, void* stream);
+
+/* One scoring step over every record of every sequence in the batch:
+ * m_hat = block_mass / max over the sequence's blocks (0 if that max is 0),
+ * E <- alpha m_hat + (1 - alpha) E in fp64, touch_count += 1, t_touch = step.
+ * With classify != 0 also priority and tier (as kvs_classify).  A record whose
+ * t_touch is not KVS_NEVER_TOUCHED and >= step is left unchanged
+ * (KVS_DEV_STALE_STEP).  workspace: kvs_score_workspace_bytes() bytes. */
+int kvs_score_update(kvs_block_meta* meta, const float* block_mass,
+                     const int32_t* meta_offsets, int32_t batch,
+                     int32_t max_blocks_per_seq, int64_t total_blocks,
+                     uint64_t step, const kvs_policy* policy, int classify,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Priority and tier of every record from its current score, without touching
+ * it: P = w_recency (b + 1) / nb + w_ema score + w_anchor [flags & ANCHOR],
+ * tier = 0 if P >= t_high, 1 if P >= t_low, else 2, where b is the record's
+ * logical block and nb its sequence's record count.  Writes priority and tier
+ * into the records and, when tiers_out != NULL, tier into tiers_out[record]. */
+int kvs_classify(kvs_block_meta* meta, const int32_t* meta_offsets, int32_t batch,
+                 int32_t max_blocks_per_seq, int64_t total_blocks,
+                 const kvs_policy* policy, uint8_t* tiers_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVS_H */

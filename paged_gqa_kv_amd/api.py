@@ -1,0 +1,147 @@
+"""Thin Python binding of the C ABI (argument marshalling only).
+
+Names follow include/kvs.h without the ``kvs_`` prefix.  Tensor arguments are
+torch tensors on the GPU (their data pointers are passed) or plain integers
+(raw device addresses); ``stream`` defaults to torch's current stream.  Every
+step of the computation runs in the HIP library; nothing here computes.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _abi
+from ._abi import META_DTYPE, KvsError, Policy, Shape, check, lib  # noqa: F401
+
+DEFAULT_SCALE = 1.0 / math.sqrt(128.0)
+
+
+def shape(num_layers: int) -> Shape:
+    return Shape(num_layers, 64, 8, 128, 16)
+
+
+def policy(alpha: float, w_recency: float = 0.25, w_ema: float = 0.55, w_anchor: float = 0.20,
+           t_low: float = 0.3, t_high: float = 0.6) -> Policy:
+    return Policy(alpha, w_recency, w_ema, w_anchor, t_low, t_high)
+
+
+def _p(x):
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        return ctypes.c_void_p(x.data_ptr())
+    return ctypes.c_void_p(int(x))
+
+
+def _s(stream):
+    if stream is None:
+        if not torch.cuda.is_available():
+            return None
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream)) if stream else None
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+# ---- host-only helpers ------------------------------------------------------
+
+def bytes_per_token(shp: Shape) -> int:
+    return lib().kvs_bytes_per_token(ctypes.byref(shp))
+
+
+def block_bytes(shp: Shape) -> int:
+    return lib().kvs_block_bytes(ctypes.byref(shp))
+
+
+def meta_layout():
+    offs = (ctypes.c_size_t * 9)()
+    size = lib().kvs_meta_layout(offs, 9)
+    return size, list(offs)
+
+
+def decode_split_blocks(shp: Shape, batch: int, max_blocks: int, layer_begin: int,
+                        layer_end: int, split_blocks: int = 0) -> int:
+    return lib().kvs_decode_split_blocks(ctypes.byref(shp), batch, max_blocks, layer_begin,
+                                         layer_end, split_blocks)
+
+
+def decode_workspace_bytes(shp: Shape, batch: int, max_blocks: int, total_blocks: int,
+                           layer_begin: int, layer_end: int, split_blocks: int = 0) -> int:
+    return lib().kvs_decode_workspace_bytes(ctypes.byref(shp), batch, max_blocks, total_blocks,
+                                            layer_begin, layer_end, split_blocks)
+
+
+def score_workspace_bytes(batch: int, max_blocks: int) -> int:
+    return lib().kvs_score_workspace_bytes(batch, max_blocks)
+
+
+def status_string(code: int) -> str:
+    return lib().kvs_status_string(code).decode()
+
+
+def last_error() -> str:
+    return lib().kvs_last_error().decode()
+
+
+# ---- device entry points ----------------------------------------------------
+
+def set_decode_events(before, after) -> None:
+    """Raw hipEvent_t handles (ints) recorded around the decode kernel, or None, None."""
+    check(lib().kvs_set_decode_events(_p(before), _p(after)))
+
+
+def workspace_init(workspace, nbytes=None, stream=None) -> None:
+    n = _nbytes(workspace) if nbytes is None else nbytes
+    check(lib().kvs_workspace_init(_p(workspace), n, _s(stream)))
+
+
+def device_status(workspace, stream=None) -> int:
+    bits = ctypes.c_uint32(0)
+    check(lib().kvs_device_status(_p(workspace), _s(stream), ctypes.byref(bits)))
+    return bits.value
+
+
+def decode_step(shp: Shape, q, kv_pool, pool_blocks: int, block_table, max_blocks: int,
+                seq_lens, meta_offsets, batch: int, total_blocks: int, layer_begin: int,
+                layer_end: int, scale: float, out, block_mass, accumulate: int,
+                split_blocks: int, workspace, workspace_bytes=None, stream=None) -> None:
+    ws_bytes = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    check(lib().kvs_decode_step(ctypes.byref(shp), _p(q), _p(kv_pool), pool_blocks,
+                                _p(block_table), max_blocks, _p(seq_lens), _p(meta_offsets),
+                                batch, total_blocks, layer_begin, layer_end, scale, _p(out),
+                                _p(block_mass), accumulate, split_blocks, _p(workspace),
+                                ws_bytes, _s(stream)))
+
+
+def meta_init(meta, meta_offsets, seq_ids, batch: int, max_blocks: int, total_blocks: int,
+              anchor_blocks: int = 1, stream=None) -> None:
+    check(lib().kvs_meta_init(_p(meta), _p(meta_offsets), _p(seq_ids), batch, max_blocks,
+                              total_blocks, anchor_blocks, _s(stream)))
+
+
+def score_update(meta, block_mass, meta_offsets, batch: int, max_blocks: int,
+                 total_blocks: int, step: int, pol: Policy, classify: int, workspace,
+                 workspace_bytes=None, stream=None) -> None:
+    ws_bytes = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    check(lib().kvs_score_update(_p(meta), _p(block_mass), _p(meta_offsets), batch, max_blocks,
+                                 total_blocks, step, ctypes.byref(pol), classify, _p(workspace),
+                                 ws_bytes, _s(stream)))
+
+
+def classify(meta, meta_offsets, batch: int, max_blocks: int, total_blocks: int, pol: Policy,
+             tiers_out=None, stream=None) -> None:
+    check(lib().kvs_classify(_p(meta), _p(meta_offsets), batch, max_blocks, total_blocks,
+                             ctypes.byref(pol), _p(tiers_out), _s(stream)))
+
+
+def records(meta: torch.Tensor):
+    """Copy a device record array (uint8 [n][64] or any 64-byte-row tensor) to a
+    numpy structured array with META_DTYPE."""
+    raw = meta.detach().contiguous().view(torch.uint8).cpu().numpy()
+    return raw.view(META_DTYPE).reshape(-1)

@@ -1,0 +1,429 @@
+// C-ABI host side: argument validation, workspace layout, launches.
+// Every host-checkable error returns before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstddef>
+#include <cstdint>
+#include <cstdio>
+
+#include "kvs.h"
+#include "kvs_internal.h"
+
+static_assert(sizeof(kvs_block_meta) == 64, "record must be 64 bytes");
+static_assert(offsetof(kvs_block_meta, key) == 0, "");
+static_assert(offsetof(kvs_block_meta, score) == 16, "");
+static_assert(offsetof(kvs_block_meta, t_touch) == 24, "");
+static_assert(offsetof(kvs_block_meta, touch_count) == 32, "");
+static_assert(offsetof(kvs_block_meta, tier) == 36, "");
+static_assert(offsetof(kvs_block_meta, flags) == 37, "");
+static_assert(offsetof(kvs_block_meta, reserved0) == 38, "");
+static_assert(offsetof(kvs_block_meta, priority) == 40, "");
+static_assert(offsetof(kvs_block_meta, reserved1) == 48, "");
+
+namespace {
+
+thread_local char g_err[512] = "";
+thread_local hipEvent_t g_ev_before = nullptr;
+thread_local hipEvent_t g_ev_after = nullptr;
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return KVS_OK;
+}
+
+constexpr size_t kHeader = 256;
+constexpr size_t kAlign = 256;
+constexpr uint64_t kTargetWaves = 16384;  // >= 4 full rounds of the chip at 16 waves / CU
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_shape(const kvs_shape* s) {
+  if (!s) return fail(KVS_E_NULL, "shape is NULL");
+  if (s->num_layers < 1 || s->num_q_heads != 64 || s->num_kv_heads != 8 || s->head_dim != 128 ||
+      s->block_tokens != 16)
+    return fail(KVS_E_SHAPE,
+                "unsupported shape {layers=%d, q_heads=%d, kv_heads=%d, head_dim=%d, block=%d}; "
+                "kernels support 64/8/128/16 with layers >= 1",
+                s->num_layers, s->num_q_heads, s->num_kv_heads, s->head_dim, s->block_tokens);
+  return KVS_OK;
+}
+
+int check_policy(const kvs_policy* p) {
+  if (!p) return fail(KVS_E_NULL, "policy is NULL");
+  const double v[6] = {p->alpha, p->w_recency, p->w_ema, p->w_anchor, p->t_low, p->t_high};
+  for (double x : v)
+    if (!std::isfinite(x)) return fail(KVS_E_POLICY, "policy holds a non-finite value");
+  if (!(p->alpha > 0.0 && p->alpha <= 1.0))
+    return fail(KVS_E_POLICY, "alpha %.17g not in (0, 1]", p->alpha);
+  if (p->w_recency < 0 || p->w_ema < 0 || p->w_anchor < 0)
+    return fail(KVS_E_POLICY, "negative weight");
+  if (!(p->t_low >= 0.0 && p->t_low <= p->t_high && p->t_high <= 1.0))
+    return fail(KVS_E_POLICY, "cut points must satisfy 0 <= t_low <= t_high <= 1");
+  return KVS_OK;
+}
+
+kvs::ScorePolicy to_score_policy(const kvs_policy* p) {
+  return kvs::ScorePolicy{p->alpha, p->w_recency, p->w_ema, p->w_anchor, p->t_low, p->t_high};
+}
+
+int32_t choose_split(int32_t batch, int32_t max_nb, int32_t n_layers) {
+  const uint64_t items = (uint64_t)batch * (uint64_t)n_layers * 8u;
+  for (int32_t cand = 128; cand >= 16; cand >>= 1) {
+    const uint64_t waves = items * (uint64_t)((max_nb + cand - 1) / cand);
+    if (waves >= kTargetWaves) return cand;
+  }
+  return 16;
+}
+
+bool split_valid(int32_t sb) { return sb >= 4 && sb <= 512; }
+
+struct DecodeLayout {
+  size_t ml, wsplit, opart, pi, total;
+  int32_t split_blocks, n_splits;
+};
+
+// Returns false on invalid sizes (no message).
+bool decode_layout(const kvs_shape* shape, int32_t batch, int32_t max_nb, int64_t total_blocks,
+                   int32_t lb, int32_t le, int32_t split_blocks, DecodeLayout* L) {
+  if (!shape || batch < 1 || max_nb < 1 || total_blocks < 0 || total_blocks > INT32_MAX ||
+      lb < 0 || le <= lb || le > shape->num_layers)
+    return false;
+  const int32_t nl = le - lb;
+  const int32_t sb = split_blocks == 0 ? choose_split(batch, max_nb, nl) : split_blocks;
+  if (!split_valid(sb)) return false;
+  const uint64_t nsplit = (uint64_t)(max_nb + sb - 1) / sb;
+  const uint64_t stats = (uint64_t)batch * nl * 64u * nsplit;
+  size_t off = kHeader;
+  L->ml = off;
+  off = align_up(off + stats * 8u);
+  L->wsplit = off;
+  off = align_up(off + stats * 4u);
+  L->opart = off;
+  off = align_up(off + stats * 128u * 4u);
+  L->pi = off;
+  off = align_up(off + (uint64_t)nl * 64u * (uint64_t)total_blocks * 4u);
+  L->total = off;
+  L->split_blocks = sb;
+  L->n_splits = (int32_t)nsplit;
+  return true;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(KVS_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvs_status_string(int code) {
+  switch (code) {
+    case KVS_OK: return "ok";
+    case KVS_E_NULL: return "null pointer";
+    case KVS_E_SHAPE: return "unsupported shape";
+    case KVS_E_RANGE: return "argument out of range";
+    case KVS_E_ALIGN: return "misaligned pointer";
+    case KVS_E_WORKSPACE: return "workspace too small";
+    case KVS_E_POLICY: return "invalid policy";
+    case KVS_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* kvs_last_error(void) { return g_err; }
+
+size_t kvs_bytes_per_token(const kvs_shape* s) {
+  if (!s || s->num_layers < 1 || s->num_kv_heads < 1 || s->head_dim < 1) return 0;
+  return (size_t)2 * (size_t)s->num_layers * (size_t)s->num_kv_heads * (size_t)s->head_dim * 2u;
+}
+
+size_t kvs_block_bytes(const kvs_shape* s) {
+  if (!s || s->block_tokens < 1) return 0;
+  return (size_t)s->block_tokens * kvs_bytes_per_token(s);
+}
+
+size_t kvs_meta_layout(size_t* offsets, int n) {
+  if (offsets && n >= 9) {
+    offsets[0] = offsetof(kvs_block_meta, key);
+    offsets[1] = offsetof(kvs_block_meta, score);
+    offsets[2] = offsetof(kvs_block_meta, t_touch);
+    offsets[3] = offsetof(kvs_block_meta, touch_count);
+    offsets[4] = offsetof(kvs_block_meta, tier);
+    offsets[5] = offsetof(kvs_block_meta, flags);
+    offsets[6] = offsetof(kvs_block_meta, reserved0);
+    offsets[7] = offsetof(kvs_block_meta, priority);
+    offsets[8] = offsetof(kvs_block_meta, reserved1);
+  }
+  return sizeof(kvs_block_meta);
+}
+
+int32_t kvs_decode_split_blocks(const kvs_shape* shape, int32_t batch, int32_t max_blocks_per_seq,
+                                int32_t layer_begin, int32_t layer_end, int32_t split_blocks) {
+  DecodeLayout L;
+  if (!decode_layout(shape, batch, max_blocks_per_seq, 0, layer_begin, layer_end, split_blocks, &L))
+    return 0;
+  return L.split_blocks;
+}
+
+size_t kvs_decode_workspace_bytes(const kvs_shape* shape, int32_t batch, int32_t max_blocks_per_seq,
+                                  int64_t total_blocks, int32_t layer_begin, int32_t layer_end,
+                                  int32_t split_blocks) {
+  DecodeLayout L;
+  if (!decode_layout(shape, batch, max_blocks_per_seq, total_blocks, layer_begin, layer_end,
+                     split_blocks, &L))
+    return 0;
+  return L.total;
+}
+
+size_t kvs_score_workspace_bytes(int32_t batch, int32_t max_blocks_per_seq) {
+  if (batch < 1 || max_blocks_per_seq < 1) return 0;
+  const uint64_t chunks = (uint64_t)(max_blocks_per_seq + kvs::kScoreThreads - 1) / kvs::kScoreThreads;
+  return align_up(kHeader + (uint64_t)batch * chunks * 4u);
+}
+
+int kvs_set_decode_events(void* before, void* after) {
+  if ((before == nullptr) != (after == nullptr))
+    return fail(KVS_E_NULL, "both events or neither must be given");
+  g_ev_before = static_cast<hipEvent_t>(before);
+  g_ev_after = static_cast<hipEvent_t>(after);
+  return ok();
+}
+
+int kvs_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace) return fail(KVS_E_NULL, "workspace is NULL");
+  if (!aligned(workspace, kAlign)) return fail(KVS_E_ALIGN, "workspace must be 256-byte aligned");
+  if (workspace_bytes < kHeader)
+    return fail(KVS_E_WORKSPACE, "workspace of %zu bytes is smaller than its %zu-byte header",
+                workspace_bytes, kHeader);
+  hipError_t e = kvs::launch_clear(static_cast<uint32_t*>(workspace), (int)(kHeader / 4),
+                                   static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "clear_words launch");
+  return ok();
+}
+
+int kvs_device_status(void* workspace, void* stream, uint32_t* bits) {
+  if (!workspace || !bits) return fail(KVS_E_NULL, "workspace and bits must be non-NULL");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t host = 0;
+  hipError_t e = hipMemcpyAsync(&host, workspace, sizeof(host), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "reading the status word");
+  e = kvs::launch_clear(static_cast<uint32_t*>(workspace), 1, st);
+  if (e != hipSuccess) return hip_fail(e, "clearing the status word");
+  *bits = host;
+  return ok();
+}
+
+int kvs_decode_step(const kvs_shape* shape, const void* q, const void* kv_pool, int64_t pool_blocks,
+                    const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                    const int32_t* meta_offsets, int32_t batch, int64_t total_blocks,
+                    int32_t layer_begin, int32_t layer_end, float scale, void* out,
+                    float* block_mass, int accumulate, int32_t split_blocks, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!q || !kv_pool || !block_table || !seq_lens || !meta_offsets || !out || !block_mass ||
+      !workspace)
+    return fail(KVS_E_NULL, "a required pointer is NULL");
+  if (batch < 1) return fail(KVS_E_RANGE, "batch %d < 1", batch);
+  if (max_blocks_per_seq < 1) return fail(KVS_E_RANGE, "max_blocks_per_seq %d < 1", max_blocks_per_seq);
+  if (pool_blocks < 1) return fail(KVS_E_RANGE, "pool_blocks %lld < 1", (long long)pool_blocks);
+  if (pool_blocks > INT32_MAX) return fail(KVS_E_RANGE, "pool_blocks exceeds int32 block ids");
+  if (total_blocks < 0 || total_blocks > INT32_MAX)
+    return fail(KVS_E_RANGE, "total_blocks %lld out of range", (long long)total_blocks);
+  if (layer_begin < 0 || layer_end <= layer_begin || layer_end > shape->num_layers)
+    return fail(KVS_E_RANGE, "layer range [%d, %d) not inside [0, %d)", layer_begin, layer_end,
+                shape->num_layers);
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(KVS_E_RANGE, "scale must be finite and > 0");
+  if (accumulate != 0 && accumulate != 1) return fail(KVS_E_RANGE, "accumulate must be 0 or 1");
+  if (split_blocks != 0 && !split_valid(split_blocks))
+    return fail(KVS_E_RANGE, "split_blocks %d not in [4, 512]", split_blocks);
+  if (!aligned(q, 16) || !aligned(kv_pool, 16) || !aligned(out, 16))
+    return fail(KVS_E_ALIGN, "q, kv_pool and out must be 16-byte aligned");
+  if (!aligned(block_mass, 4) || !aligned(block_table, 4) || !aligned(seq_lens, 4) ||
+      !aligned(meta_offsets, 4))
+    return fail(KVS_E_ALIGN, "int32 / fp32 arrays must be 4-byte aligned");
+  if (!aligned(workspace, kAlign)) return fail(KVS_E_ALIGN, "workspace must be 256-byte aligned");
+  DecodeLayout L;
+  if (!decode_layout(shape, batch, max_blocks_per_seq, total_blocks, layer_begin, layer_end,
+                     split_blocks, &L))
+    return fail(KVS_E_RANGE, "inconsistent sizes");
+  if (workspace_bytes < L.total)
+    return fail(KVS_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
+  const int32_t nl = layer_end - layer_begin;
+  const uint64_t wgs = (uint64_t)batch * (uint64_t)L.n_splits * (uint64_t)nl * 8u;
+  if (wgs * 64u >= (1ull << 32))
+    return fail(KVS_E_RANGE, "problem too large for one launch (%llu work-groups)",
+                (unsigned long long)wgs);
+  if ((uint64_t)batch * nl * 64u >= (1ull << 32))
+    return fail(KVS_E_RANGE, "batch x layers too large for one launch");
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint32_t* status = reinterpret_cast<uint32_t*>(ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  kvs::DecodeArgs d{};
+  d.q = static_cast<const uint16_t*>(q);
+  d.pool = static_cast<const uint8_t*>(kv_pool);
+  d.table = block_table;
+  d.seq_lens = seq_lens;
+  d.meta_off = meta_offsets;
+  d.pool_blocks = pool_blocks;
+  d.total_blocks = total_blocks;
+  d.max_nb = max_blocks_per_seq;
+  d.num_layers = shape->num_layers;
+  d.layer_begin = layer_begin;
+  d.n_layers = nl;
+  d.split_blocks = L.split_blocks;
+  d.n_splits = L.n_splits;
+  d.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  d.ml = reinterpret_cast<float2*>(ws + L.ml);
+  d.opart = reinterpret_cast<float*>(ws + L.opart);
+  d.pi = reinterpret_cast<float*>(ws + L.pi);
+  d.status = status;
+
+  kvs::CombineArgs c{};
+  c.seq_lens = seq_lens;
+  c.meta_off = meta_offsets;
+  c.ml = d.ml;
+  c.opart = d.opart;
+  c.wsplit = reinterpret_cast<float*>(ws + L.wsplit);
+  c.out = static_cast<uint16_t*>(out);
+  c.total_blocks = total_blocks;
+  c.max_nb = max_blocks_per_seq;
+  c.num_layers = shape->num_layers;
+  c.layer_begin = layer_begin;
+  c.n_layers = nl;
+  c.split_blocks = L.split_blocks;
+  c.n_splits = L.n_splits;
+  c.status = status;
+
+  kvs::MassArgs m{};
+  m.seq_lens = seq_lens;
+  m.meta_off = meta_offsets;
+  m.pi = d.pi;
+  m.wsplit = c.wsplit;
+  m.mass = block_mass;
+  m.total_blocks = total_blocks;
+  m.max_nb = max_blocks_per_seq;
+  m.n_layers = nl;
+  m.split_blocks = L.split_blocks;
+  m.n_splits = L.n_splits;
+  m.accumulate = accumulate;
+  m.status = status;
+
+  hipError_t e = hipSuccess;
+  if (g_ev_before) {
+    e = hipEventRecord(g_ev_before, st);
+    if (e != hipSuccess) return hip_fail(e, "recording the before-decode event");
+  }
+  e = kvs::launch_decode(d, batch, st);
+  if (e != hipSuccess) return hip_fail(e, "paged_decode_gqa launch");
+  if (g_ev_after) {
+    e = hipEventRecord(g_ev_after, st);
+    if (e != hipSuccess) return hip_fail(e, "recording the after-decode event");
+  }
+  e = kvs::launch_combine(c, batch, st);
+  if (e != hipSuccess) return hip_fail(e, "combine_splits launch");
+  if (total_blocks > 0) {
+    e = kvs::launch_mass(m, batch, st);
+    if (e != hipSuccess) return hip_fail(e, "block_mass launch");
+  }
+  return ok();
+}
+
+int kvs_meta_init(kvs_block_meta* meta, const int32_t* meta_offsets, const uint64_t* seq_ids,
+                  int32_t batch, int32_t max_blocks_per_seq, int64_t total_blocks,
+                  int32_t anchor_blocks, void* stream) {
+  if (!meta || !meta_offsets || !seq_ids) return fail(KVS_E_NULL, "a required pointer is NULL");
+  if (batch < 1 || max_blocks_per_seq < 1 || total_blocks < 0 || total_blocks > INT32_MAX ||
+      anchor_blocks < 0)
+    return fail(KVS_E_RANGE, "batch, max_blocks_per_seq, total_blocks or anchor_blocks out of range");
+  if (!aligned(meta, 16) || !aligned(seq_ids, 8)) return fail(KVS_E_ALIGN, "meta or seq_ids misaligned");
+  kvs::MetaInitArgs a{};
+  a.meta = meta;
+  a.meta_off = meta_offsets;
+  a.seq_ids = seq_ids;
+  a.total_blocks = total_blocks;
+  a.max_nb = max_blocks_per_seq;
+  a.max_chunks = (max_blocks_per_seq + kvs::kScoreThreads - 1) / kvs::kScoreThreads;
+  a.anchor_blocks = anchor_blocks;
+  a.status = nullptr;
+  hipError_t e = kvs::launch_meta_init(a, batch, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "meta_init launch");
+  return ok();
+}
+
+int kvs_score_update(kvs_block_meta* meta, const float* block_mass, const int32_t* meta_offsets,
+                     int32_t batch, int32_t max_blocks_per_seq, int64_t total_blocks, uint64_t step,
+                     const kvs_policy* policy, int classify, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (!meta || !block_mass || !meta_offsets || !workspace)
+    return fail(KVS_E_NULL, "a required pointer is NULL");
+  int rc = check_policy(policy);
+  if (rc) return rc;
+  if (batch < 1 || max_blocks_per_seq < 1 || total_blocks < 0 || total_blocks > INT32_MAX)
+    return fail(KVS_E_RANGE, "batch, max_blocks_per_seq or total_blocks out of range");
+  if (classify != 0 && classify != 1) return fail(KVS_E_RANGE, "classify must be 0 or 1");
+  if (step == KVS_NEVER_TOUCHED) return fail(KVS_E_RANGE, "step UINT64_MAX is reserved");
+  if (!aligned(meta, 16)) return fail(KVS_E_ALIGN, "meta must be 16-byte aligned");
+  if (!aligned(workspace, kAlign)) return fail(KVS_E_ALIGN, "workspace must be 256-byte aligned");
+  const size_t need = kvs_score_workspace_bytes(batch, max_blocks_per_seq);
+  if (workspace_bytes < need)
+    return fail(KVS_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  kvs::ScoreArgs a{};
+  a.meta = meta;
+  a.mass = block_mass;
+  a.meta_off = meta_offsets;
+  a.chunk_max = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kHeader);
+  a.tiers_out = nullptr;
+  a.total_blocks = total_blocks;
+  a.step = step;
+  a.pol = to_score_policy(policy);
+  a.max_nb = max_blocks_per_seq;
+  a.max_chunks = (max_blocks_per_seq + kvs::kScoreThreads - 1) / kvs::kScoreThreads;
+  a.classify = classify;
+  a.status = static_cast<uint32_t*>(workspace);
+  if (total_blocks == 0) return ok();
+  hipError_t e = kvs::launch_score(a, batch, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "score_update launch");
+  return ok();
+}
+
+int kvs_classify(kvs_block_meta* meta, const int32_t* meta_offsets, int32_t batch,
+                 int32_t max_blocks_per_seq, int64_t total_blocks, const kvs_policy* policy,
+                 uint8_t* tiers_out, void* stream) {
+  if (!meta || !meta_offsets) return fail(KVS_E_NULL, "a required pointer is NULL");
+  int rc = check_policy(policy);
+  if (rc) return rc;
+  if (batch < 1 || max_blocks_per_seq < 1 || total_blocks < 0 || total_blocks > INT32_MAX)
+    return fail(KVS_E_RANGE, "batch, max_blocks_per_seq or total_blocks out of range");
+  if (!aligned(meta, 16)) return fail(KVS_E_ALIGN, "meta must be 16-byte aligned");
+  kvs::ScoreArgs a{};
+  a.meta = meta;
+  a.meta_off = meta_offsets;
+  a.tiers_out = tiers_out;
+  a.total_blocks = total_blocks;
+  a.pol = to_score_policy(policy);
+  a.max_nb = max_blocks_per_seq;
+  a.max_chunks = (max_blocks_per_seq + kvs::kScoreThreads - 1) / kvs::kScoreThreads;
+  a.status = nullptr;
+  if (total_blocks == 0) return ok();
+  hipError_t e = kvs::launch_classify(a, batch, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "classify launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+// Internal interface between the C-ABI host code and the device kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvs.h"
+
+namespace kvs {
+
+constexpr int kMassThreads = 1024;   // 16 waves share one 64-block column
+constexpr int kScoreThreads = 256;   // records per scoring work-group
+
+struct DecodeArgs {
+  const uint16_t* q;        // fp16 bits [B][num_layers][64][128]
+  const uint8_t* pool;      // fp16 [P][num_layers][2][8][16][128]
+  const int32_t* table;     // [B][max_nb]
+  const int32_t* seq_lens;  // [B]
+  const int32_t* meta_off;  // [B + 1]
+  int64_t pool_blocks;
+  int64_t total_blocks;
+  int32_t max_nb;
+  int32_t num_layers;
+  int32_t layer_begin;
+  int32_t n_layers;         // layers in range
+  int32_t split_blocks;
+  int32_t n_splits;
+  float scale_log2;         // softmax scale * log2(e)
+  float2* ml;               // [B][n_layers][64][n_splits]: (running max, sum), base 2
+  float* opart;             // [B][n_layers][64][n_splits][128]
+  float* pi;                // [n_layers][64][total_blocks]
+  uint32_t* status;
+};
+
+struct CombineArgs {
+  const int32_t* seq_lens;
+  const int32_t* meta_off;
+  const float2* ml;
+  const float* opart;
+  float* wsplit;            // [B][n_layers][64][n_splits]
+  uint16_t* out;            // fp16 bits [B][num_layers][64][128]
+  int64_t total_blocks;
+  int32_t max_nb;
+  int32_t num_layers;
+  int32_t layer_begin;
+  int32_t n_layers;
+  int32_t split_blocks;
+  int32_t n_splits;
+  uint32_t* status;
+};
+
+struct MassArgs {
+  const int32_t* seq_lens;
+  const int32_t* meta_off;
+  const float* pi;
+  const float* wsplit;
+  float* mass;
+  int64_t total_blocks;
+  int32_t max_nb;
+  int32_t n_layers;
+  int32_t split_blocks;
+  int32_t n_splits;
+  int32_t accumulate;
+  uint32_t* status;
+};
+
+struct ScorePolicy {
+  double alpha, w_recency, w_ema, w_anchor, t_low, t_high;
+};
+
+struct ScoreArgs {
+  kvs_block_meta* meta;
+  const float* mass;
+  const int32_t* meta_off;
+  float* chunk_max;         // [B][max_chunks]
+  uint8_t* tiers_out;
+  int64_t total_blocks;
+  uint64_t step;
+  ScorePolicy pol;
+  int32_t max_nb;
+  int32_t max_chunks;
+  int32_t classify;
+  uint32_t* status;
+};
+
+struct MetaInitArgs {
+  kvs_block_meta* meta;
+  const int32_t* meta_off;
+  const uint64_t* seq_ids;
+  int64_t total_blocks;
+  int32_t max_nb;
+  int32_t max_chunks;
+  int32_t anchor_blocks;
+  uint32_t* status;         // may be a scratch word; init reports nothing
+};
+
+hipError_t launch_decode(const DecodeArgs& a, int batch, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, int batch, hipStream_t stream);
+hipError_t launch_mass(const MassArgs& a, int batch, hipStream_t stream);
+hipError_t launch_score(const ScoreArgs& a, int batch, hipStream_t stream);
+hipError_t launch_classify(const ScoreArgs& a, int batch, hipStream_t stream);
+hipError_t launch_meta_init(const MetaInitArgs& a, int batch, hipStream_t stream);
+hipError_t launch_clear(uint32_t* p, int n, hipStream_t stream);
+
+}  // namespace kvs

@@ -1,0 +1,531 @@
+// Device kernels of the paged GQA decode + block-scoring library (gfx950 only).
+//
+// Kernels, in the order one decode step runs them:
+//   paged_decode_gqa  split-K decode: one wave per (sequence, layer, KV head,
+//                     split of blocks); QK^T and PV on MFMA; online softmax;
+//                     per-(layer, head, block) probability-mass partials.
+//   combine_splits    merges the splits of each (sequence, layer, head) into the
+//                     fp16 output and the per-split normalising weights.
+//   block_mass        sums the mass partials of every (layer, query head) into
+//                     one fp32 number per (sequence, block), in a fixed order.
+//   seq_chunk_max /   the scoring step: per-sequence maximum, then normalise,
+//   score_update      EMA, touch, priority and tier per 64-byte record (fp64).
+//   classify_records, meta_init, clear_status: the remaining entry points.
+//
+// Sources: "KV-Cache Offloading for LLM Inference -- Visual Reference"
+// Sec. 2 (attention), Sec. 11 (EMA), Sec. 12 (priority, cut points);
+// "GQA Per-Head Scoring Streams" (head grouping, stream aggregation, the
+// 64-byte record); "KV cache offload" post, "Top row" (block tables).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "kvs.h"
+#include "kvs_internal.h"
+
+namespace kvs {
+
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kHeadDim = 128;
+constexpr int kGroup = 8;                 // query heads per KV head
+constexpr int kQHeads = 64;
+constexpr int kTileBytes = 16 * kHeadDim * 2;          // one (layer, K|V, KV head) tile: 4 KiB
+constexpr int64_t kLayerBytes = 2 * 8 * kTileBytes;    // one block, one layer: 64 KiB
+
+__device__ __forceinline__ float xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+
+__device__ __forceinline__ void flag(uint32_t* status, uint32_t bit) {
+  atomicOr(status, bit);
+}
+
+// Shared validity check of one sequence's device-side description.  Returns the
+// number of blocks, or -1 (and sets a status bit from lane 0 of the first wave
+// that sees it) when the sequence must be skipped.
+__device__ __forceinline__ int seq_blocks(const int32_t* seq_lens, const int32_t* meta_off,
+                                          int s, int max_nb, int64_t total_blocks,
+                                          uint32_t* status, bool report, int* r0_out) {
+  const int n = seq_lens[s];
+  const int r0 = meta_off[s];
+  const int r1 = meta_off[s + 1];
+  if (n < 0 || n > 16 * max_nb) {
+    if (report) flag(status, KVS_DEV_BAD_SEQ_LEN);
+    return -1;
+  }
+  const int nb = (n + 15) >> 4;
+  if (r0 < 0 || r1 - r0 != nb || (int64_t)r1 > total_blocks) {
+    if (report) flag(status, KVS_DEV_BAD_OFFSETS);
+    return -1;
+  }
+  *r0_out = r0;
+  return nb;
+}
+
+// ---------------------------------------------------------------------------
+// paged_decode_gqa
+//
+// One 64-lane wave owns (s, layer, g, split).  Lane l = 16 j + c.
+//  QK:  S^T[token][head] = K[token][:] . q[head][:] on v_mfma_f32_16x16x32_f16,
+//       A = the 16x128 key tile (lane reads 64 contiguous bytes of row c), B =
+//       the 8 queries of the group padded to 16 columns.  The result gives
+//       lane (j, c) the logits of head c for tokens 4j..4j+3.
+//  PV:  O^T[d][head] += V^T[d][token] P^T[token][head] on
+//       v_mfma_f32_16x16x16_f16.  P^T is exactly the QK result layout (after
+//       rounding to fp16).  V^T needs the value tile transposed: it is staged
+//       through 4 KiB of LDS, each lane reads 4 rows x 16 bytes, and byte
+//       permutes build the operand of each of the 8 output tiles.  Output tile
+//       k holds d = 8 m + k, so lane (j, c) ends with the 32 contiguous values
+//       d in [32 j, 32 j + 32) of head c.
+//  Online softmax in base 2: logits are scaled by scale * log2(e); a running
+//  maximum per head; the per-block mass of head c is kept in LDS relative to
+//  the current maximum and rescaled whenever that maximum grows.
+// ---------------------------------------------------------------------------
+struct BlockRegs {
+  u4_t k[4];
+  u4_t v[4];
+};
+
+__device__ __forceinline__ void load_block(BlockRegs& r, const uint8_t* base, bool ok,
+                                           int lane, int c, int j) {
+  if (ok) {
+    const uint8_t* kp = base + c * 256 + j * 64;
+    const uint8_t* vp = base + 8 * kTileBytes + lane * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.k[i] = *reinterpret_cast<const u4_t*>(kp + i * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.v[i] = *reinterpret_cast<const u4_t*>(vp + i * 1024);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r.k[i] = u4_t{0u, 0u, 0u, 0u};
+      r.v[i] = u4_t{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+__global__ void __launch_bounds__(64, 2) paged_decode_gqa(DecodeArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int SB = a.split_blocks;
+  float* pi_lds = reinterpret_cast<float*>(smem);                 // [8][SB]
+  u4_t* vstage = reinterpret_cast<u4_t*>(smem + 8 * SB * 4);      // 16 rows x 16 chunks of 16 B
+
+  const int lane = threadIdx.x;
+  const int c = lane & 15;
+  const int j = lane >> 4;
+
+  uint32_t w = blockIdx.x;
+  const uint32_t lg_count = (uint32_t)a.n_layers * 8u;
+  const int lg = (int)(w % lg_count);
+  w /= lg_count;
+  const int split = (int)(w % (uint32_t)a.n_splits);
+  const int s = (int)(w / (uint32_t)a.n_splits);
+  const int lr = lg >> 3;
+  const int g = lg & 7;
+  const int layer = a.layer_begin + lr;
+
+  int r0 = 0;
+  const bool report = (lane == 0) && split == 0 && lg == 0;
+  const int nb = seq_blocks(a.seq_lens, a.meta_off, s, a.max_nb, a.total_blocks, a.status,
+                            report, &r0);
+  const int b0 = split * SB;
+  if (nb < 0 || b0 >= nb) return;
+  const int b1 = min(nb, b0 + SB);
+  const int n = a.seq_lens[s];
+
+  // B operand of QK: queries of the group, rows 8..15 zero.
+  h8_t qb[4];
+  if (c < kGroup) {
+    const h8_t* qp = reinterpret_cast<const h8_t*>(
+        a.q + ((((size_t)s * a.num_layers + layer) * kQHeads + kGroup * g + c) * kHeadDim) + 32 * j);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qb[i] = qp[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qb[i] = h8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+
+  const size_t block_stride = (size_t)a.num_layers * kLayerBytes;
+  const size_t tile_off = (size_t)layer * kLayerBytes + (size_t)g * kTileBytes;
+  const int32_t* trow = a.table + (size_t)s * a.max_nb;
+
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  f4_t acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = f4_t{0.f, 0.f, 0.f, 0.f};
+
+  BlockRegs cur, nxt;
+  int pid = trow[b0];
+  bool cur_ok = pid >= 0 && (int64_t)pid < a.pool_blocks;
+  load_block(cur, a.pool + (size_t)(cur_ok ? pid : 0) * block_stride + tile_off, cur_ok, lane, c, j);
+
+  for (int b = b0; b < b1; ++b) {
+    bool nxt_ok = false;
+    if (b + 1 < b1) {
+      const int pn = trow[b + 1];
+      nxt_ok = pn >= 0 && (int64_t)pn < a.pool_blocks;
+      load_block(nxt, a.pool + (size_t)(nxt_ok ? pn : 0) * block_stride + tile_off, nxt_ok,
+                 lane, c, j);
+    }
+    if (!cur_ok && lane == 0) flag(a.status, KVS_DEV_BAD_BLOCK_ID);
+    const int valid = cur_ok ? min(16, n - 16 * b) : 0;
+
+    // ---- logits of 16 tokens x 16 (8 real) heads
+    f4_t sacc = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, cur.k[i]), qb[i],
+                                                    sacc, 0, 0, 0);
+    float sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = (4 * j + i < valid) ? sacc[i] * a.scale_log2 : -INFINITY;
+
+    // ---- online softmax (per head = per c; the 4 lanes j share a head)
+    float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    bm = fmaxf(bm, xor_f(bm, 16));
+    bm = fmaxf(bm, xor_f(bm, 32));
+    const float m_new = fmaxf(m_run, bm);
+    const bool live = m_new != -INFINITY;
+    const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+    float pv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pv[i] = live ? __builtin_amdgcn_exp2f(sv[i] - m_new) : 0.f;
+    const float ps = (pv[0] + pv[1]) + (pv[2] + pv[3]);
+    l_run = l_run * alpha + ps;
+    float bs = ps + xor_f(ps, 16);
+    bs += xor_f(bs, 32);
+
+    if (__ballot(c < kGroup && alpha != 1.f) != 0ull) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] *= alpha;
+      if (c < kGroup)
+        for (int idx = j; idx < b - b0; idx += 4) pi_lds[c * SB + idx] *= alpha;
+    }
+    if (c < kGroup && j == 0) pi_lds[c * SB + (b - b0)] = bs;
+    m_run = m_new;
+
+    // ---- value tile: transpose through LDS
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vstage[i * 64 + lane] = cur.v[i];
+    u4_t R[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      R[i] = vstage[(4 * j + i) * 16 + c];
+      if (4 * j + i >= valid) R[i] = u4_t{0u, 0u, 0u, 0u};
+    }
+    const h4_t pb = h4_t{(_Float16)pv[0], (_Float16)pv[1], (_Float16)pv[2], (_Float16)pv[3]};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t lo01 = __builtin_amdgcn_perm(R[1][q], R[0][q], 0x05040100u);
+      const uint32_t lo23 = __builtin_amdgcn_perm(R[3][q], R[2][q], 0x05040100u);
+      const uint32_t hi01 = __builtin_amdgcn_perm(R[1][q], R[0][q], 0x07060302u);
+      const uint32_t hi23 = __builtin_amdgcn_perm(R[3][q], R[2][q], 0x07060302u);
+      acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+          __builtin_bit_cast(h4_t, u2_t{lo01, lo23}), pb, acc[2 * q], 0, 0, 0);
+      acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+          __builtin_bit_cast(h4_t, u2_t{hi01, hi23}), pb, acc[2 * q + 1], 0, 0, 0);
+    }
+
+    cur = nxt;
+    cur_ok = nxt_ok;
+  }
+
+  // ---- split epilogue: statistics, partial output, mass partials
+  float lt = l_run + xor_f(l_run, 16);
+  lt += xor_f(lt, 32);
+  const size_t st = (((size_t)s * a.n_layers + lr) * kQHeads + kGroup * g + c) * a.n_splits + split;
+  if (c < kGroup) {
+    if (j == 0) a.ml[st] = make_float2(m_run, lt);
+    float* op = a.opart + st * kHeadDim + 32 * j;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<f4_t*>(op + 8 * i) = f4_t{acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
+      *reinterpret_cast<f4_t*>(op + 8 * i + 4) = f4_t{acc[4][i], acc[5][i], acc[6][i], acc[7][i]};
+    }
+  }
+  __syncthreads();
+  const int cnt = b1 - b0;
+  for (int hh = 0; hh < kGroup; ++hh) {
+    float* dst = a.pi + ((size_t)lr * kQHeads + kGroup * g + hh) * a.total_blocks + r0 + b0;
+    for (int bb = lane; bb < cnt; bb += 64) dst[bb] = pi_lds[hh * SB + bb];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// combine_splits: one wave per (s, layer, head).  Lane handles d = 2 lane, +1.
+//   M = max_k m_k, Lambda = sum_k l_k 2^(m_k - M), w_k = 2^(m_k - M) / Lambda,
+//   out = sum_k w_k o_k (fp16), and w_k is kept for the mass reduction.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(64) combine_splits(CombineArgs a) {
+  const int lane = threadIdx.x;
+  uint32_t w = blockIdx.x;
+  const int h = (int)(w % kQHeads);
+  w /= kQHeads;
+  const int lr = (int)(w % (uint32_t)a.n_layers);
+  const int s = (int)(w / (uint32_t)a.n_layers);
+  const int layer = a.layer_begin + lr;
+  uint32_t* outp = reinterpret_cast<uint32_t*>(
+      a.out + ((((size_t)s * a.num_layers + layer) * kQHeads + h) * kHeadDim));
+
+  int r0 = 0;
+  const int nb = seq_blocks(a.seq_lens, a.meta_off, s, a.max_nb, a.total_blocks, a.status,
+                            false, &r0);
+  if (nb <= 0) {
+    outp[lane] = 0u;
+    return;
+  }
+  const int nsp = (nb + a.split_blocks - 1) / a.split_blocks;
+  const size_t base = (((size_t)s * a.n_layers + lr) * kQHeads + h) * a.n_splits;
+
+  float M = -INFINITY;
+  for (int k = lane; k < nsp; k += 64) M = fmaxf(M, a.ml[base + k].x);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, xor_f(M, m));
+  double L = 0.0;
+  if (M != -INFINITY)
+    for (int k = lane; k < nsp; k += 64) {
+      const float2 v = a.ml[base + k];
+      L += (double)v.y * (double)__builtin_amdgcn_exp2f(v.x - M);
+    }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) L += __shfl_xor(L, m, 64);
+  const bool dead = !(L > 0.0);
+  const double invL = dead ? 0.0 : 1.0 / L;
+
+  for (int k = lane; k < nsp; k += 64) {
+    const float2 v = a.ml[base + k];
+    a.wsplit[base + k] = dead ? 0.f : (float)((double)__builtin_amdgcn_exp2f(v.x - M) * invL);
+  }
+  float o0 = 0.f, o1 = 0.f;
+  for (int k = 0; k < nsp; ++k) {
+    const float2 v = a.ml[base + k];
+    const float wk = dead ? 0.f : (float)((double)__builtin_amdgcn_exp2f(v.x - M) * invL);
+    const float2 ov = reinterpret_cast<const float2*>(a.opart + (base + k) * kHeadDim)[lane];
+    o0 = fmaf(wk, ov.x, o0);
+    o1 = fmaf(wk, ov.y, o1);
+  }
+  const _Float16 h0 = (_Float16)o0, h1 = (_Float16)o1;
+  outp[lane] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// block_mass: mass[s, b] = sum over (layer, query head) of pi * w_split, fp64
+// accumulation in a fixed order (row order within each wave, then waves in
+// order), so the result depends only on logical indices.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kMassThreads) block_mass(MassArgs a) {
+  __shared__ double red[kMassThreads / 64][64];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  constexpr int kWaves = kMassThreads / 64;
+  const int s = blockIdx.y;
+  int r0 = 0;
+  const int nb = seq_blocks(a.seq_lens, a.meta_off, s, a.max_nb, a.total_blocks, a.status,
+                            false, &r0);
+  if (nb <= 0 || (int)blockIdx.x * 64 >= nb) return;
+  const int b = blockIdx.x * 64 + lane;
+  const bool act = b < nb;
+  const int r = r0 + (act ? b : 0);
+  const int split = (act ? b : 0) / a.split_blocks;
+  const int rows = a.n_layers * kQHeads;
+  double acc = 0.0;
+  if (act) {
+    const float* pcol = a.pi + r;
+    const float* wcol = a.wsplit + (size_t)s * a.n_layers * kQHeads * a.n_splits + split;
+#pragma unroll 8
+    for (int row = wv; row < rows; row += kWaves)
+      acc += (double)pcol[(size_t)row * a.total_blocks] * (double)wcol[(size_t)row * a.n_splits];
+  }
+  red[wv][lane] = acc;
+  __syncthreads();
+  if (wv == 0 && act) {
+    double t = 0.0;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) t += red[k][lane];
+    if (a.accumulate) t += (double)a.mass[r];
+    a.mass[r] = (float)t;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Scoring kernels.  Grid (chunk of kScoreThreads records, sequence).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int seq_records(const int32_t* off, int s, int max_nb,
+                                           int64_t total_blocks, uint32_t* status, bool report,
+                                           int* r0_out) {
+  const int r0 = off[s];
+  const int r1 = off[s + 1];
+  if (r0 < 0 || r1 < r0 || r1 - r0 > max_nb || (int64_t)r1 > total_blocks) {
+    if (report) flag(status, KVS_DEV_BAD_OFFSETS);
+    return -1;
+  }
+  *r0_out = r0;
+  return r1 - r0;
+}
+
+__device__ __forceinline__ float block_reduce_max(float v, float* red) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, xor_f(v, m));
+  const int wv = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wv] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int k = 1; k < kScoreThreads / 64; ++k) r = fmaxf(r, red[k]);
+  __syncthreads();
+  return r;
+}
+
+__global__ void __launch_bounds__(kScoreThreads) seq_chunk_max(ScoreArgs a) {
+  __shared__ float red[kScoreThreads / 64];
+  const int s = blockIdx.y;
+  const int chunk = blockIdx.x;
+  int r0 = 0;
+  const int nb = seq_records(a.meta_off, s, a.max_nb, a.total_blocks, a.status,
+                             threadIdx.x == 0 && chunk == 0, &r0);
+  if (nb <= 0 || chunk * kScoreThreads >= nb) return;
+  const int b = chunk * kScoreThreads + threadIdx.x;
+  float v = b < nb ? a.mass[r0 + b] : 0.f;
+  v = block_reduce_max(v, red);
+  if (threadIdx.x == 0) a.chunk_max[(size_t)s * a.max_chunks + chunk] = v;
+}
+
+__device__ __forceinline__ void priority_and_tier(const ScorePolicy& p, int b, int nb, double score,
+                                                  uint8_t flags, double* P, uint8_t* tier) {
+  const double R = (double)(b + 1) / (double)nb;
+  const double N = (flags & KVS_FLAG_ANCHOR) ? 1.0 : 0.0;
+  const double pr = p.w_recency * R + p.w_ema * score + p.w_anchor * N;
+  *P = pr;
+  *tier = pr >= p.t_high ? 0 : (pr >= p.t_low ? 1 : 2);
+}
+
+__global__ void __launch_bounds__(kScoreThreads) score_update(ScoreArgs a) {
+  __shared__ float red[kScoreThreads / 64];
+  const int s = blockIdx.y;
+  const int chunk = blockIdx.x;
+  int r0 = 0;
+  const int nb = seq_records(a.meta_off, s, a.max_nb, a.total_blocks, a.status, false, &r0);
+  if (nb <= 0 || chunk * kScoreThreads >= nb) return;
+  const int nch = (nb + kScoreThreads - 1) / kScoreThreads;
+  float M = 0.f;
+  for (int k = threadIdx.x; k < nch; k += kScoreThreads)
+    M = fmaxf(M, a.chunk_max[(size_t)s * a.max_chunks + k]);
+  M = block_reduce_max(M, red);
+
+  const int b = chunk * kScoreThreads + threadIdx.x;
+  bool stale = false;
+  if (b < nb) {
+    kvs_block_meta* rec = a.meta + r0 + b;
+    const uint64_t tt = rec->t_touch;
+    if (tt != KVS_NEVER_TOUCHED && tt >= a.step) {
+      stale = true;
+    } else {
+      const double mh = M > 0.f ? (double)a.mass[r0 + b] / (double)M : 0.0;
+      const double e = a.pol.alpha * mh + (1.0 - a.pol.alpha) * rec->score;
+      rec->score = e;
+      rec->touch_count = rec->touch_count + 1u;
+      rec->t_touch = a.step;
+      if (a.classify) {
+        double P;
+        uint8_t tier;
+        priority_and_tier(a.pol, b, nb, e, rec->flags, &P, &tier);
+        rec->priority = P;
+        rec->tier = tier;
+      }
+    }
+  }
+  if (__ballot(stale) != 0ull && (threadIdx.x & 63) == 0) flag(a.status, KVS_DEV_STALE_STEP);
+}
+
+__global__ void __launch_bounds__(kScoreThreads) classify_records(ScoreArgs a) {
+  const int s = blockIdx.y;
+  int r0 = 0;
+  const int nb = seq_records(a.meta_off, s, a.max_nb, a.total_blocks, a.status, false, &r0);
+  const int b = blockIdx.x * kScoreThreads + threadIdx.x;
+  if (nb <= 0 || b >= nb) return;
+  kvs_block_meta* rec = a.meta + r0 + b;
+  double P;
+  uint8_t tier;
+  priority_and_tier(a.pol, b, nb, rec->score, rec->flags, &P, &tier);
+  rec->priority = P;
+  rec->tier = tier;
+  if (a.tiers_out) a.tiers_out[r0 + b] = tier;
+}
+
+__global__ void __launch_bounds__(kScoreThreads) meta_init(MetaInitArgs a) {
+  const int s = blockIdx.y;
+  int r0 = 0;
+  const int nb = seq_records(a.meta_off, s, a.max_nb, a.total_blocks, a.status, false, &r0);
+  const int b = blockIdx.x * kScoreThreads + threadIdx.x;
+  if (nb <= 0 || b >= nb) return;
+  kvs_block_meta rec;
+  rec.key[0] = a.seq_ids[s];
+  rec.key[1] = (uint64_t)b;
+  rec.score = 0.0;
+  rec.t_touch = KVS_NEVER_TOUCHED;
+  rec.touch_count = 0u;
+  rec.tier = KVS_UNCLASSIFIED;
+  rec.flags = b < a.anchor_blocks ? KVS_FLAG_ANCHOR : 0u;
+  rec.reserved0 = 0u;
+  rec.priority = 0.0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) rec.reserved1[i] = 0u;
+  a.meta[r0 + b] = rec;
+}
+
+__global__ void __launch_bounds__(64) clear_words(uint32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += 64) p[i] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_decode(const DecodeArgs& a, int batch, hipStream_t stream) {
+  const uint64_t wgs = (uint64_t)batch * a.n_splits * a.n_layers * 8;
+  const size_t lds = (size_t)8 * a.split_blocks * 4 + kTileBytes;
+  hipLaunchKernelGGL(paged_decode_gqa, dim3((uint32_t)wgs), dim3(64), lds, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineArgs& a, int batch, hipStream_t stream) {
+  const uint64_t wgs = (uint64_t)batch * a.n_layers * kQHeads;
+  hipLaunchKernelGGL(combine_splits, dim3((uint32_t)wgs), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_mass(const MassArgs& a, int batch, hipStream_t stream) {
+  const dim3 grid((a.max_nb + 63) / 64, batch);
+  hipLaunchKernelGGL(block_mass, grid, dim3(kMassThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_score(const ScoreArgs& a, int batch, hipStream_t stream) {
+  const dim3 grid(a.max_chunks, batch);
+  hipLaunchKernelGGL(seq_chunk_max, grid, dim3(kScoreThreads), 0, stream, a);
+  hipLaunchKernelGGL(score_update, grid, dim3(kScoreThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_classify(const ScoreArgs& a, int batch, hipStream_t stream) {
+  const dim3 grid(a.max_chunks, batch);
+  hipLaunchKernelGGL(classify_records, grid, dim3(kScoreThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_meta_init(const MetaInitArgs& a, int batch, hipStream_t stream) {
+  const dim3 grid(a.max_chunks, batch);
+  hipLaunchKernelGGL(meta_init, grid, dim3(kScoreThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_clear(uint32_t* p, int n, hipStream_t stream) {
+  hipLaunchKernelGGL(clear_words, dim3(1), dim3(64), 0, stream, p, n);
+  return hipGetLastError();
+}
+
+}  // namespace kvs

@@ -1,0 +1,78 @@
+"""Device-memory plumbing around the C ABI for one materialised workload.
+
+Allocates (with torch) the output, block-mass, record and workspace buffers a
+decode + scoring step needs, and calls the library.  No arithmetic here.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import api
+
+
+class DecodeSession:
+    def __init__(self, m, layer_begin: int = 0, layer_end=None, split_blocks: int = 0,
+                 anchor_blocks: int = 1, stream=None):
+        self.m = m
+        self.stream = stream
+        L = m.num_layers
+        self.layer_begin = layer_begin
+        self.layer_end = L if layer_end is None else layer_end
+        self.shape = api.shape(L)
+        dev = m.pool.device
+        B = m.batch
+        self.split_blocks = api.decode_split_blocks(self.shape, B, m.max_blocks, self.layer_begin,
+                                                    self.layer_end, split_blocks)
+        if self.split_blocks == 0:
+            raise ValueError(f"invalid split_blocks {split_blocks}")
+        self.out = torch.zeros((B, L, 64, 128), dtype=torch.float16, device=dev)
+        self.mass = torch.zeros(max(m.total_blocks, 1), dtype=torch.float32, device=dev)
+        ws_bytes = api.decode_workspace_bytes(self.shape, B, m.max_blocks, m.total_blocks,
+                                              self.layer_begin, self.layer_end, self.split_blocks)
+        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        api.workspace_init(self.ws, stream=stream)
+        self.meta = torch.empty((max(m.total_blocks, 1), 64), dtype=torch.uint8, device=dev)
+        self.score_ws = torch.empty(api.score_workspace_bytes(B, m.max_blocks), dtype=torch.uint8,
+                                    device=dev)
+        api.workspace_init(self.score_ws, stream=stream)
+        self.anchor_blocks = anchor_blocks
+        self.reset_meta()
+
+    @property
+    def kv_bytes_per_step(self) -> int:
+        """Logical KV bytes one decode step reads (keys and values, every token)."""
+        return sum(self.m.lens) * (self.layer_end - self.layer_begin) * 8 * 128 * 2 * 2
+
+    def reset_meta(self):
+        m = self.m
+        api.meta_init(self.meta, m.meta_offsets, m.seq_ids, m.batch, m.max_blocks, m.total_blocks,
+                      self.anchor_blocks, stream=self.stream)
+
+    def decode(self, q, accumulate: int = 0, layer_begin=None, layer_end=None, scale=None):
+        m = self.m
+        lb = self.layer_begin if layer_begin is None else layer_begin
+        le = self.layer_end if layer_end is None else layer_end
+        api.decode_step(self.shape, q, m.pool, m.pool_blocks, m.block_table, m.max_blocks,
+                        m.seq_lens, m.meta_offsets, m.batch, m.total_blocks, lb, le,
+                        api.DEFAULT_SCALE if scale is None else scale, self.out, self.mass,
+                        accumulate, self.split_blocks, self.ws, stream=self.stream)
+
+    def score(self, step: int, pol, classify: int = 1):
+        m = self.m
+        api.score_update(self.meta, self.mass, m.meta_offsets, m.batch, m.max_blocks,
+                         m.total_blocks, step, pol, classify, self.score_ws, stream=self.stream)
+
+    def classify(self, pol, tiers_out=None):
+        m = self.m
+        api.classify(self.meta, m.meta_offsets, m.batch, m.max_blocks, m.total_blocks, pol,
+                     tiers_out, stream=self.stream)
+
+    def step(self, q, step: int, pol, classify: int = 1):
+        self.decode(q)
+        self.score(step, pol, classify)
+
+    def status(self) -> int:
+        return api.device_status(self.ws, self.stream) | api.device_status(self.score_ws, self.stream)
+
+    def records(self):
+        return api.records(self.meta[: self.m.total_blocks])

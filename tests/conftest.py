@@ -15,3 +15,14 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def repo_root():
     return ROOT
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _built_library():
+    """Build the HIP library in-tree when it is absent (hipcc cross-compiles
+    for gfx950 without a GPU).  A present library is used as it is."""
+    lib = os.path.join(ROOT, "paged_gqa_kv_amd", "libkvs.so")
+    if not os.path.exists(lib) and os.path.exists("/opt/rocm/bin/hipcc"):
+        from paged_gqa_kv_amd import build
+        build.build()
+    yield

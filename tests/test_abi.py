@@ -1,0 +1,157 @@
+"""The C-ABI library loads, exports what include/kvs.h declares, and rejects
+every host-checkable bad argument before launching anything (no GPU needed:
+none of these calls reaches the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_gqa_kv_amd import _abi, api
+from paged_gqa_kv_amd._abi import (KVS_E_ALIGN, KVS_E_NULL, KVS_E_POLICY, KVS_E_RANGE,
+                                   KVS_E_SHAPE, KVS_E_WORKSPACE, KvsError)
+from oracle import arithmetic as A
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "kvs.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"\b(kvs_[a-z_]+)\s*\(", src))
+
+
+def test_every_declared_function_is_exported():
+    lib = _abi.lib()
+    declared = _declared()
+    assert declared == set(_abi.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_byte_accounting_matches_oracle():
+    for L in (1, 4, 32, 80):
+        shp = api.shape(L)
+        assert api.bytes_per_token(shp) == A.kv_bytes_per_token(L, 8, 128, 2)
+        assert api.block_bytes(shp) == A.block_bytes(L, 8, 128, 2, 16)
+    assert api.bytes_per_token(api.shape(80)) == 327_680
+    assert api.block_bytes(api.shape(80)) == 5 * 2**20
+
+
+def test_record_layout():
+    size, offs = api.meta_layout()
+    assert size == 64 == _abi.META_DTYPE.itemsize
+    names = _abi.META_DTYPE.names
+    assert offs == [_abi.META_DTYPE.fields[n][1] for n in names]
+
+
+def test_workspace_sizing():
+    shp = api.shape(80)
+    sb = api.decode_split_blocks(shp, 1, 8192, 0, 80)
+    assert sb in (16, 32, 64, 128)
+    ws = api.decode_workspace_bytes(shp, 1, 8192, 8192, 0, 80, sb)
+    # dominated by the mass partials: 4 B x 64 heads x 80 layers x 8192 blocks
+    assert ws >= 4 * 64 * 80 * 8192
+    assert ws < 4 * 64 * 80 * 8192 * 3
+    assert api.decode_workspace_bytes(shp, 1, 8192, 8192, 0, 81, 0) == 0
+    assert api.decode_split_blocks(shp, 1, 8192, 0, 80, 3) == 0
+    assert api.decode_split_blocks(shp, 1, 8192, 0, 80, 64) == 64
+    assert api.score_workspace_bytes(1, 65536) >= 256 + 4 * 256
+    assert api.score_workspace_bytes(0, 10) == 0
+
+
+def _decode_args(**over):
+    base = dict(shp=api.shape(2), q=0x1000, kv_pool=0x2000, pool_blocks=10, block_table=0x3000,
+                max_blocks=4, seq_lens=0x4000, meta_offsets=0x5000, batch=2, total_blocks=8,
+                layer_begin=0, layer_end=2, scale=0.088, out=0x6000, block_mass=0x7000,
+                accumulate=0, split_blocks=0, workspace=0x10000, workspace_bytes=1)
+    base.update(over)
+    return base
+
+
+def _decode(**over):
+    a = _decode_args(**over)
+    return api.decode_step(a["shp"], a["q"], a["kv_pool"], a["pool_blocks"], a["block_table"],
+                           a["max_blocks"], a["seq_lens"], a["meta_offsets"], a["batch"],
+                           a["total_blocks"], a["layer_begin"], a["layer_end"], a["scale"],
+                           a["out"], a["block_mass"], a["accumulate"], a["split_blocks"],
+                           a["workspace"], a["workspace_bytes"], stream=0)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=0), KVS_E_NULL),
+    (dict(kv_pool=0), KVS_E_NULL),
+    (dict(block_mass=0), KVS_E_NULL),
+    (dict(workspace=0), KVS_E_NULL),
+    (dict(shp=api.Shape(2, 32, 8, 128, 16)), KVS_E_SHAPE),
+    (dict(shp=api.Shape(2, 64, 8, 64, 16)), KVS_E_SHAPE),
+    (dict(shp=api.Shape(0, 64, 8, 128, 16)), KVS_E_SHAPE),
+    (dict(batch=0), KVS_E_RANGE),
+    (dict(max_blocks=0), KVS_E_RANGE),
+    (dict(pool_blocks=0), KVS_E_RANGE),
+    (dict(layer_begin=1, layer_end=1), KVS_E_RANGE),
+    (dict(layer_end=3), KVS_E_RANGE),
+    (dict(scale=float("nan")), KVS_E_RANGE),
+    (dict(accumulate=2), KVS_E_RANGE),
+    (dict(split_blocks=1000), KVS_E_RANGE),
+    (dict(total_blocks=-1), KVS_E_RANGE),
+    (dict(q=0x1008), KVS_E_ALIGN),
+    (dict(workspace=0x10010), KVS_E_ALIGN),
+    (dict(), KVS_E_WORKSPACE),
+])
+def test_decode_rejects_before_launch(over, code):
+    with pytest.raises(KvsError) as e:
+        _decode(**over)
+    assert e.value.code == code
+    assert api.last_error()
+
+
+def test_score_and_classify_validation():
+    pol = api.policy(0.15)
+    ok_ws = api.score_workspace_bytes(2, 4)
+    args = (0x1000, 0x2000, 0x3000, 2, 4, 8)
+    with pytest.raises(KvsError) as e:
+        api.score_update(*args, 0, api.policy(0.0), 1, 0x10000, ok_ws, stream=0)
+    assert e.value.code == KVS_E_POLICY
+    with pytest.raises(KvsError) as e:
+        api.score_update(*args, 0, api.policy(0.15, t_low=0.7, t_high=0.6), 1, 0x10000, ok_ws,
+                         stream=0)
+    assert e.value.code == KVS_E_POLICY
+    with pytest.raises(KvsError) as e:
+        api.score_update(*args, 0, api.policy(0.15, w_ema=-1.0), 1, 0x10000, ok_ws, stream=0)
+    assert e.value.code == KVS_E_POLICY
+    with pytest.raises(KvsError) as e:
+        api.score_update(*args, 0, pol, 1, 0x10000, ok_ws - 4, stream=0)
+    assert e.value.code == KVS_E_WORKSPACE
+    with pytest.raises(KvsError) as e:
+        api.score_update(*args, 2**64 - 1, pol, 1, 0x10000, ok_ws, stream=0)
+    assert e.value.code == KVS_E_RANGE
+    with pytest.raises(KvsError) as e:
+        api.score_update(0, 0x2000, 0x3000, 2, 4, 8, 0, pol, 1, 0x10000, ok_ws, stream=0)
+    assert e.value.code == KVS_E_NULL
+    with pytest.raises(KvsError) as e:
+        api.classify(0x1000, 0x3000, 0, 4, 8, pol, stream=0)
+    assert e.value.code == KVS_E_RANGE
+    with pytest.raises(KvsError) as e:
+        api.meta_init(0x1000, 0x3000, 0x5000, 2, 4, 8, anchor_blocks=-1, stream=0)
+    assert e.value.code == KVS_E_RANGE
+    with pytest.raises(KvsError) as e:
+        api.workspace_init(0x10000, 100, stream=0)
+    assert e.value.code == KVS_E_WORKSPACE
+    with pytest.raises(KvsError) as e:
+        api.device_status(0, stream=0)
+    assert e.value.code == KVS_E_NULL
+
+
+def test_status_strings():
+    for code in range(-7, 1):
+        assert api.status_string(code) and api.status_string(code) != "unknown status"
+    assert api.status_string(-99) == "unknown status"
+
+
+def test_binding_requires_the_library(monkeypatch):
+    monkeypatch.setattr(_abi, "_LIB", None)
+    monkeypatch.setattr(_abi, "LIB_PATH", "/nonexistent/libkvs.so")
+    with pytest.raises(ImportError):
+        _abi.lib()
