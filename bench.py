@@ -41,6 +41,9 @@ def _parse():
     ap.add_argument("--split-blocks", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="approximate CPU time budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--copy-probe-gib", type=float, default=4.0,
+                    help="buffer size of the device copy probe (0 = skip)")
+    ap.add_argument("--copy-probe-reps", type=int, default=20)
     return ap.parse_args()
 
 
@@ -85,6 +88,33 @@ def _traffic(workload: str, split_blocks: int):
     if rec.get("kernel_sha256") != digest or rec.get("split_blocks") != split_blocks:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def _copy_probe(gib: float, reps: int):
+    """Achievable streaming bandwidth: device-to-device copy of gib-GiB buffers,
+    median of reps, counting bytes read plus bytes written (the method the
+    Visual Reference's measurement box describes for its 87 %-of-spec figure)."""
+    import torch
+
+    n = int(gib * 2**30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    times = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b) / 1e3)
+    times.sort()
+    med = times[len(times) // 2]
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_per_copy": 2 * n * 4, "median_s": med, "gbps": 2 * n * 4 / med / 1e9,
+            "reps": reps}
 
 
 def _cpu_baseline(m, alpha, budget_s):
@@ -229,6 +259,11 @@ def main():
     traffic = _traffic(wl.name, sess.split_blocks)
     tiers = np.bincount(rec["tier"], minlength=3)[:3].tolist()
 
+    probe = None
+    if args.copy_probe_gib > 0:
+        print("[bench] copy probe", file=sys.stderr, flush=True)
+        probe = _copy_probe(args.copy_probe_gib, args.copy_probe_reps)
+
     cpu = None
     if args.cpu_seconds > 0:
         print("[bench] timing the oracle baseline", file=sys.stderr, flush=True)
@@ -265,6 +300,8 @@ def main():
         "decode_share_of_step": round(dec_avg / t_step, 4),
         "tier_counts": tiers,
         "host_wall_s": round(wall, 4),
+        "copy_probe": probe,
+        "frac_of_copy_probe": round(value / probe["gbps"], 4) if probe else None,
         "roofline": {
             "bound": "hbm",
             "kernel": "paged_decode_gqa",

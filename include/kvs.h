@@ -132,7 +132,7 @@ size_t kvs_block_bytes(const kvs_shape* shape);
 size_t kvs_meta_layout(size_t* offsets, int n);
 
 /* Blocks per split used by kvs_decode_step for this problem when
- * split_blocks == 0 is passed (a power of two in [16, 256]); otherwise
+ * split_blocks == 0 is passed (a power of two in [16, 512]); otherwise
  * split_blocks itself if valid, or 0 if invalid. */
 int32_t kvs_decode_split_blocks(const kvs_shape* shape, int32_t batch,
                                 int32_t max_blocks_per_seq, int32_t layer_begin,
@@ -161,6 +161,19 @@ const char* kvs_last_error(void);
 int kvs_set_decode_events(void* before, void* after);
 
 /* ---- device entry points ------------------------------------------------- */
+
+/* Bandwidth probe: the achievable-HBM reference that throughput figures are
+ * compared with (the pages measure achievable streaming bandwidth with a plain
+ * copy of large buffers, median of several runs: Visual Reference Sec. 4 and 9,
+ * measurement notes).  Not part of the decode path.
+ *  mode 0 (read):  reads `bytes` from src with 16-byte loads, every lane folding
+ *                  what it read into one 32-bit word written to dst (dst holds
+ *                  grid x 256 words).
+ *  mode 1 (copy):  copies `bytes` from src to dst.
+ * bytes must be a non-zero multiple of 16; src and dst 16-byte aligned;
+ * grid = number of 256-lane work-groups (0 = library choice). */
+int kvs_stream_probe(const void* src, void* dst, size_t bytes, int mode, int32_t grid,
+                     void* stream);
 
 /* Zero the 256-byte status header of a workspace (decode or score).  Call once
  * after allocating a workspace.  Enqueues one small kernel. */

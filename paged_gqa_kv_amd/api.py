@@ -96,6 +96,10 @@ def set_decode_events(before, after) -> None:
     check(lib().kvs_set_decode_events(_p(before), _p(after)))
 
 
+def stream_probe(src, dst, nbytes: int, mode: int, grid: int = 0, stream=None) -> None:
+    check(lib().kvs_stream_probe(_p(src), _p(dst), nbytes, mode, grid, _s(stream)))
+
+
 def workspace_init(workspace, nbytes=None, stream=None) -> None:
     n = _nbytes(workspace) if nbytes is None else nbytes
     check(lib().kvs_workspace_init(_p(workspace), n, _s(stream)))

@@ -43,7 +43,10 @@ int ok() {
 
 constexpr size_t kHeader = 256;
 constexpr size_t kAlign = 256;
-constexpr uint64_t kTargetWaves = 16384;  // >= 4 full rounds of the chip at 16 waves / CU
+// Split-K sizing: the largest split (fewest partial results, longest streams)
+// that still gives at least this many decode waves, about three rounds of the
+// chip at the decode kernel's 12 resident waves per CU.
+constexpr uint64_t kTargetWaves = 8192;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -80,14 +83,16 @@ kvs::ScorePolicy to_score_policy(const kvs_policy* p) {
 
 int32_t choose_split(int32_t batch, int32_t max_nb, int32_t n_layers) {
   const uint64_t items = (uint64_t)batch * (uint64_t)n_layers * 8u;
-  for (int32_t cand = 128; cand >= 16; cand >>= 1) {
+  for (int32_t cand = 512; cand >= 16; cand >>= 1) {
     const uint64_t waves = items * (uint64_t)((max_nb + cand - 1) / cand);
     if (waves >= kTargetWaves) return cand;
   }
   return 16;
 }
 
-bool split_valid(int32_t sb) { return sb >= 4 && sb <= 512; }
+// Upper bound keeps the decode work-group's LDS (36 B per block + 4 KiB) far
+// below the 64 KiB a work-group may request.
+bool split_valid(int32_t sb) { return sb >= 4 && sb <= 1024; }
 
 struct DecodeLayout {
   size_t ml, wsplit, opart, pi, total;
@@ -201,6 +206,19 @@ int kvs_set_decode_events(void* before, void* after) {
   return ok();
 }
 
+int kvs_stream_probe(const void* src, void* dst, size_t bytes, int mode, int32_t grid,
+                     void* stream) {
+  if (!src || !dst) return fail(KVS_E_NULL, "src and dst must be non-NULL");
+  if (bytes == 0 || bytes % 16) return fail(KVS_E_RANGE, "bytes must be a non-zero multiple of 16");
+  if (mode != 0 && mode != 1) return fail(KVS_E_RANGE, "mode must be 0 (read) or 1 (copy)");
+  if (grid < 0 || grid > (1 << 20)) return fail(KVS_E_RANGE, "grid out of range");
+  if (!aligned(src, 16) || !aligned(dst, 16)) return fail(KVS_E_ALIGN, "src/dst must be 16-byte aligned");
+  const int g = grid == 0 ? 256 * 8 : grid;
+  hipError_t e = kvs::launch_probe(src, dst, bytes, mode, g, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "stream probe launch");
+  return ok();
+}
+
 int kvs_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
   if (!workspace) return fail(KVS_E_NULL, "workspace is NULL");
   if (!aligned(workspace, kAlign)) return fail(KVS_E_ALIGN, "workspace must be 256-byte aligned");
@@ -249,7 +267,7 @@ int kvs_decode_step(const kvs_shape* shape, const void* q, const void* kv_pool, 
   if (!std::isfinite(scale) || !(scale > 0.f)) return fail(KVS_E_RANGE, "scale must be finite and > 0");
   if (accumulate != 0 && accumulate != 1) return fail(KVS_E_RANGE, "accumulate must be 0 or 1");
   if (split_blocks != 0 && !split_valid(split_blocks))
-    return fail(KVS_E_RANGE, "split_blocks %d not in [4, 512]", split_blocks);
+    return fail(KVS_E_RANGE, "split_blocks %d not in [4, 1024]", split_blocks);
   if (!aligned(q, 16) || !aligned(kv_pool, 16) || !aligned(out, 16))
     return fail(KVS_E_ALIGN, "q, kv_pool and out must be 16-byte aligned");
   if (!aligned(block_mass, 4) || !aligned(block_table, 4) || !aligned(seq_lens, 4) ||

@@ -10,6 +10,7 @@ namespace kvs {
 
 constexpr int kMassThreads = 1024;   // 16 waves share one 64-block column
 constexpr int kScoreThreads = 256;   // records per scoring work-group
+constexpr size_t kMaxDecodeLds = 65536;  // dynamic LDS a decode work-group may request
 
 struct DecodeArgs {
   const uint16_t* q;        // fp16 bits [B][num_layers][64][128]
@@ -101,5 +102,7 @@ hipError_t launch_score(const ScoreArgs& a, int batch, hipStream_t stream);
 hipError_t launch_classify(const ScoreArgs& a, int batch, hipStream_t stream);
 hipError_t launch_meta_init(const MetaInitArgs& a, int batch, hipStream_t stream);
 hipError_t launch_clear(uint32_t* p, int n, hipStream_t stream);
+hipError_t launch_probe(const void* src, void* dst, size_t bytes, int mode, int grid,
+                        hipStream_t stream);
 
 }  // namespace kvs

@@ -84,57 +84,75 @@ __device__ __forceinline__ int seq_blocks(const int32_t* seq_lens, const int32_t
 //  maximum per head; the per-block mass of head c is kept in LDS relative to
 //  the current maximum and rescaled whenever that maximum grows.
 // ---------------------------------------------------------------------------
+// K/V tiles are read exactly once per step; plain loads measured faster on
+// gfx950 than non-temporal ones for this access pattern.
+__device__ __forceinline__ u4_t stream_load(const u4_t* p) { return *p; }
+
 struct BlockRegs {
   u4_t k[4];
   u4_t v[4];
 };
 
-__device__ __forceinline__ void load_block(BlockRegs& r, const uint8_t* base, bool ok,
-                                           int lane, int c, int j) {
-  if (ok) {
-    const uint8_t* kp = base + c * 256 + j * 64;
-    const uint8_t* vp = base + 8 * kTileBytes + lane * 16;
+// Issues exactly eight 16-byte loads (four of the key tile in the QK operand
+// layout, four of the value tile in plain row order).  Always issuing the same
+// number of loads on every path lets the compiler wait for one ring slot
+// precisely instead of draining every load in flight.
+__device__ __forceinline__ void load_block(BlockRegs& r, const uint8_t* base, int lane, int c,
+                                           int j) {
+  const uint8_t* kp = base + c * 256 + j * 64;
+  const uint8_t* vp = base + 8 * kTileBytes + lane * 16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.k[i] = *reinterpret_cast<const u4_t*>(kp + i * 16);
+  for (int i = 0; i < 4; ++i) r.k[i] = stream_load(reinterpret_cast<const u4_t*>(kp + i * 16));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.v[i] = *reinterpret_cast<const u4_t*>(vp + i * 1024);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      r.k[i] = u4_t{0u, 0u, 0u, 0u};
-      r.v[i] = u4_t{0u, 0u, 0u, 0u};
-    }
-  }
+  for (int i = 0; i < 4; ++i) r.v[i] = stream_load(reinterpret_cast<const u4_t*>(vp + i * 1024));
 }
 
-__global__ void __launch_bounds__(64, 2) paged_decode_gqa(DecodeArgs a) {
+// Blocks whose loads are in flight per wave: the ring slot being processed
+// plus kRing - 1 ahead (32 VGPRs per slot).  Deeper rings at lower occupancy
+// measured no faster on gfx950.
+constexpr int kRing = 2;
+constexpr int kWavesPerSimd = 3;
+// Waves per work-group (each takes one KV head).  Work-groups of 4 or 8 waves
+// reading neighbouring heads of the same blocks measured no faster than 1.
+constexpr int kWpw = 1;
+
+__global__ void __launch_bounds__(64 * kWpw, kWavesPerSimd) paged_decode_gqa(DecodeArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int SB = a.split_blocks;
-  float* pi_lds = reinterpret_cast<float*>(smem);                 // [8][SB]
-  u4_t* vstage = reinterpret_cast<u4_t*>(smem + 8 * SB * 4);      // 16 rows x 16 chunks of 16 B
+  const int wave = threadIdx.x >> 6;
+  int32_t* tbl = reinterpret_cast<int32_t*>(smem);                          // [SB] block ids
+  uint8_t* wave_lds = smem + (size_t)4 * SB + (size_t)wave * (32 * SB + kTileBytes);
+  float* pi_lds = reinterpret_cast<float*>(wave_lds);                       // [8][SB]
+  u4_t* vstage = reinterpret_cast<u4_t*>(wave_lds + 32 * SB);               // 16 x 16 chunks of 16 B
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int c = lane & 15;
   const int j = lane >> 4;
 
   uint32_t w = blockIdx.x;
-  const uint32_t lg_count = (uint32_t)a.n_layers * 8u;
-  const int lg = (int)(w % lg_count);
-  w /= lg_count;
+  const uint32_t lgg_count = (uint32_t)a.n_layers * (8u / kWpw);
+  const int lgg = (int)(w % lgg_count);
+  w /= lgg_count;
   const int split = (int)(w % (uint32_t)a.n_splits);
   const int s = (int)(w / (uint32_t)a.n_splits);
-  const int lr = lg >> 3;
-  const int g = lg & 7;
+  const int lr = lgg / (8 / kWpw);
+  const int g = (lgg % (8 / kWpw)) * kWpw + wave;
   const int layer = a.layer_begin + lr;
 
   int r0 = 0;
-  const bool report = (lane == 0) && split == 0 && lg == 0;
+  const bool report = (threadIdx.x == 0) && split == 0 && lgg == 0;
   const int nb = seq_blocks(a.seq_lens, a.meta_off, s, a.max_nb, a.total_blocks, a.status,
                             report, &r0);
   const int b0 = split * SB;
   if (nb < 0 || b0 >= nb) return;
   const int b1 = min(nb, b0 + SB);
   const int n = a.seq_lens[s];
+
+  // The split's block ids go to LDS once, so that no later block-id read waits
+  // on the vector-memory counter behind the in-flight K/V loads.
+  for (int i = threadIdx.x; i < b1 - b0; i += 64 * kWpw)
+    tbl[i] = a.table[(size_t)s * a.max_nb + b0 + i];
+  __syncthreads();
 
   // B operand of QK: queries of the group, rows 8..15 zero.
   h8_t qb[4];
@@ -150,89 +168,110 @@ __global__ void __launch_bounds__(64, 2) paged_decode_gqa(DecodeArgs a) {
 
   const size_t block_stride = (size_t)a.num_layers * kLayerBytes;
   const size_t tile_off = (size_t)layer * kLayerBytes + (size_t)g * kTileBytes;
-  const int32_t* trow = a.table + (size_t)s * a.max_nb;
-
   float m_run = -INFINITY;
   float l_run = 0.f;
   f4_t acc[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = f4_t{0.f, 0.f, 0.f, 0.f};
 
-  BlockRegs cur, nxt;
-  int pid = trow[b0];
-  bool cur_ok = pid >= 0 && (int64_t)pid < a.pool_blocks;
-  load_block(cur, a.pool + (size_t)(cur_ok ? pid : 0) * block_stride + tile_off, cur_ok, lane, c, j);
+  // Physical block of logical block bidx of this split; positions past the
+  // split's end reuse its last block (a cached, in-bounds tile whose data is
+  // masked), and ids outside the pool read block 0 and are masked.
+  auto slot_block = [&](int bidx, bool* ok) -> const uint8_t* {
+    const int clamped = min(bidx, b1 - 1);
+    const int pid = tbl[clamped - b0];
+    const bool in_pool = pid >= 0 && (int64_t)pid < a.pool_blocks;
+    *ok = in_pool && bidx < b1;
+    return a.pool + (size_t)(in_pool ? pid : 0) * block_stride + tile_off;
+  };
 
-  for (int b = b0; b < b1; ++b) {
-    bool nxt_ok = false;
-    if (b + 1 < b1) {
-      const int pn = trow[b + 1];
-      nxt_ok = pn >= 0 && (int64_t)pn < a.pool_blocks;
-      load_block(nxt, a.pool + (size_t)(nxt_ok ? pn : 0) * block_stride + tile_off, nxt_ok,
-                 lane, c, j);
+  BlockRegs ring[kRing];
+  bool ring_ok[kRing];
+#pragma unroll
+  for (int k = 0; k < kRing; ++k)
+    load_block(ring[k], slot_block(b0 + k, &ring_ok[k]), lane, c, j);
+
+  bool saw_bad = false;
+  for (int bbase = b0; bbase < b1; bbase += kRing) {
+#pragma unroll
+    for (int k = 0; k < kRing; ++k) {
+      const int b = bbase + k;
+      const bool active = b < b1;
+      const bool cur_ok = ring_ok[k];
+      saw_bad |= active && !cur_ok;
+      const int valid = cur_ok ? min(16, n - 16 * b) : 0;
+
+      // ---- value tile to LDS (the slot's value registers are free after this)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vstage[i * 64 + lane] = ring[k].v[i];
+
+      // ---- logits of 16 tokens x 16 (8 real) heads
+      f4_t sacc = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, ring[k].k[i]),
+                                                      qb[i], sacc, 0, 0, 0);
+
+      // ---- refill this slot with the block kRing ahead
+      load_block(ring[k], slot_block(b + kRing, &ring_ok[k]), lane, c, j);
+
+      float sv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[i] = sacc[i] * a.scale_log2;
+      if (valid < 16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * j + i >= valid) sv[i] = -INFINITY;
+      }
+
+      // ---- online softmax (per head = per c; the 4 lanes j share a head)
+      float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      bm = fmaxf(bm, xor_f(bm, 16));
+      bm = fmaxf(bm, xor_f(bm, 32));
+      const float m_new = fmaxf(m_run, bm);
+      const bool live = m_new != -INFINITY;
+      const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      float pv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pv[i] = live ? __builtin_amdgcn_exp2f(sv[i] - m_new) : 0.f;
+      const float ps = (pv[0] + pv[1]) + (pv[2] + pv[3]);
+      l_run = l_run * alpha + ps;
+      float bs = ps + xor_f(ps, 16);
+      bs += xor_f(bs, 32);
+
+      if (__ballot(c < kGroup && alpha != 1.f) != 0ull) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] *= alpha;
+        if (c < kGroup)
+          for (int idx = j; idx < b - b0; idx += 4) pi_lds[c * SB + idx] *= alpha;
+      }
+      if (active && c < kGroup && j == 0) pi_lds[c * SB + (b - b0)] = bs;
+      m_run = m_new;
+
+      // ---- PV: transposed value rows from LDS
+      u4_t R[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) R[i] = vstage[(4 * j + i) * 16 + c];
+      if (valid < 16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * j + i >= valid) R[i] = u4_t{0u, 0u, 0u, 0u};
+      }
+      const h4_t pb = h4_t{(_Float16)pv[0], (_Float16)pv[1], (_Float16)pv[2], (_Float16)pv[3]};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo01 = __builtin_amdgcn_perm(R[1][q], R[0][q], 0x05040100u);
+        const uint32_t lo23 = __builtin_amdgcn_perm(R[3][q], R[2][q], 0x05040100u);
+        const uint32_t hi01 = __builtin_amdgcn_perm(R[1][q], R[0][q], 0x07060302u);
+        const uint32_t hi23 = __builtin_amdgcn_perm(R[3][q], R[2][q], 0x07060302u);
+        acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+            __builtin_bit_cast(h4_t, u2_t{lo01, lo23}), pb, acc[2 * q], 0, 0, 0);
+        acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+            __builtin_bit_cast(h4_t, u2_t{hi01, hi23}), pb, acc[2 * q + 1], 0, 0, 0);
+      }
     }
-    if (!cur_ok && lane == 0) flag(a.status, KVS_DEV_BAD_BLOCK_ID);
-    const int valid = cur_ok ? min(16, n - 16 * b) : 0;
-
-    // ---- logits of 16 tokens x 16 (8 real) heads
-    f4_t sacc = f4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, cur.k[i]), qb[i],
-                                                    sacc, 0, 0, 0);
-    float sv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sv[i] = (4 * j + i < valid) ? sacc[i] * a.scale_log2 : -INFINITY;
-
-    // ---- online softmax (per head = per c; the 4 lanes j share a head)
-    float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    bm = fmaxf(bm, xor_f(bm, 16));
-    bm = fmaxf(bm, xor_f(bm, 32));
-    const float m_new = fmaxf(m_run, bm);
-    const bool live = m_new != -INFINITY;
-    const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-    float pv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pv[i] = live ? __builtin_amdgcn_exp2f(sv[i] - m_new) : 0.f;
-    const float ps = (pv[0] + pv[1]) + (pv[2] + pv[3]);
-    l_run = l_run * alpha + ps;
-    float bs = ps + xor_f(ps, 16);
-    bs += xor_f(bs, 32);
-
-    if (__ballot(c < kGroup && alpha != 1.f) != 0ull) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] *= alpha;
-      if (c < kGroup)
-        for (int idx = j; idx < b - b0; idx += 4) pi_lds[c * SB + idx] *= alpha;
-    }
-    if (c < kGroup && j == 0) pi_lds[c * SB + (b - b0)] = bs;
-    m_run = m_new;
-
-    // ---- value tile: transpose through LDS
-#pragma unroll
-    for (int i = 0; i < 4; ++i) vstage[i * 64 + lane] = cur.v[i];
-    u4_t R[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      R[i] = vstage[(4 * j + i) * 16 + c];
-      if (4 * j + i >= valid) R[i] = u4_t{0u, 0u, 0u, 0u};
-    }
-    const h4_t pb = h4_t{(_Float16)pv[0], (_Float16)pv[1], (_Float16)pv[2], (_Float16)pv[3]};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t lo01 = __builtin_amdgcn_perm(R[1][q], R[0][q], 0x05040100u);
-      const uint32_t lo23 = __builtin_amdgcn_perm(R[3][q], R[2][q], 0x05040100u);
-      const uint32_t hi01 = __builtin_amdgcn_perm(R[1][q], R[0][q], 0x07060302u);
-      const uint32_t hi23 = __builtin_amdgcn_perm(R[3][q], R[2][q], 0x07060302u);
-      acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-          __builtin_bit_cast(h4_t, u2_t{lo01, lo23}), pb, acc[2 * q], 0, 0, 0);
-      acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-          __builtin_bit_cast(h4_t, u2_t{hi01, hi23}), pb, acc[2 * q + 1], 0, 0, 0);
-    }
-
-    cur = nxt;
-    cur_ok = nxt_ok;
   }
+  if (saw_bad && lane == 0) flag(a.status, KVS_DEV_BAD_BLOCK_ID);
 
   // ---- split epilogue: statistics, partial output, mass partials
   float lt = l_run + xor_f(l_run, 16);
@@ -483,12 +522,51 @@ __global__ void __launch_bounds__(64) clear_words(uint32_t* p, int n) {
 }
 
 // ---------------------------------------------------------------------------
+// stream probe: grid-stride 16-byte loads, 8 in flight per lane.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) stream_read(const u4_t* __restrict__ src, size_t n16,
+                                                  uint32_t* __restrict__ sink) {
+  const size_t tid = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * 256;
+  uint32_t acc = 0;
+  size_t i = tid;
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    u4_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (; i < n16; i += stride) {
+    const u4_t v = src[i];
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  sink[tid] = acc;
+}
+
+__global__ void __launch_bounds__(256) stream_copy(const u4_t* __restrict__ src, size_t n16,
+                                                  u4_t* __restrict__ dst) {
+  const size_t tid = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * 256;
+  size_t i = tid;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    u4_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) __builtin_nontemporal_store(v[u], dst + i + u * stride);
+  }
+  for (; i < n16; i += stride) dst[i] = src[i];
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_decode(const DecodeArgs& a, int batch, hipStream_t stream) {
-  const uint64_t wgs = (uint64_t)batch * a.n_splits * a.n_layers * 8;
-  const size_t lds = (size_t)8 * a.split_blocks * 4 + kTileBytes;
-  hipLaunchKernelGGL(paged_decode_gqa, dim3((uint32_t)wgs), dim3(64), lds, stream, a);
+  const uint64_t wgs = (uint64_t)batch * a.n_splits * a.n_layers * (8 / kWpw);
+  const size_t lds = (size_t)4 * a.split_blocks + (size_t)kWpw * (32 * a.split_blocks + kTileBytes);
+  if (lds > kMaxDecodeLds) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(paged_decode_gqa, dim3((uint32_t)wgs), dim3(64 * kWpw), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -525,6 +603,18 @@ hipError_t launch_meta_init(const MetaInitArgs& a, int batch, hipStream_t stream
 
 hipError_t launch_clear(uint32_t* p, int n, hipStream_t stream) {
   hipLaunchKernelGGL(clear_words, dim3(1), dim3(64), 0, stream, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe(const void* src, void* dst, size_t bytes, int mode, int grid,
+                        hipStream_t stream) {
+  const size_t n16 = bytes / 16;
+  if (mode == 0)
+    hipLaunchKernelGGL(stream_read, dim3(grid), dim3(256), 0, stream,
+                       static_cast<const u4_t*>(src), n16, static_cast<uint32_t*>(dst));
+  else
+    hipLaunchKernelGGL(stream_copy, dim3(grid), dim3(256), 0, stream,
+                       static_cast<const u4_t*>(src), n16, static_cast<u4_t*>(dst));
   return hipGetLastError();
 }
 
