@@ -81,6 +81,18 @@ kvs::ScorePolicy to_score_policy(const kvs_policy* p) {
   return kvs::ScorePolicy{p->alpha, p->w_recency, p->w_ema, p->w_anchor, p->t_low, p->t_high};
 }
 
+// Batch is a grid dimension of the per-sequence kernels; block counts are
+// scaled by 16 tokens in 32-bit device arithmetic.
+constexpr int32_t kMaxBatch = 65535;
+constexpr int32_t kMaxBlocksPerSeq = 1 << 26;
+
+int check_counts(int32_t batch, int32_t max_blocks) {
+  if (batch < 1 || batch > kMaxBatch) return fail(KVS_E_RANGE, "batch %d not in [1, %d]", batch, kMaxBatch);
+  if (max_blocks < 1 || max_blocks > kMaxBlocksPerSeq)
+    return fail(KVS_E_RANGE, "max_blocks_per_seq %d not in [1, %d]", max_blocks, kMaxBlocksPerSeq);
+  return KVS_OK;
+}
+
 int32_t choose_split(int32_t batch, int32_t max_nb, int32_t n_layers) {
   const uint64_t items = (uint64_t)batch * (uint64_t)n_layers * 8u;
   for (int32_t cand = 512; cand >= 16; cand >>= 1) {
@@ -102,8 +114,8 @@ struct DecodeLayout {
 // Returns false on invalid sizes (no message).
 bool decode_layout(const kvs_shape* shape, int32_t batch, int32_t max_nb, int64_t total_blocks,
                    int32_t lb, int32_t le, int32_t split_blocks, DecodeLayout* L) {
-  if (!shape || batch < 1 || max_nb < 1 || total_blocks < 0 || total_blocks > INT32_MAX ||
-      lb < 0 || le <= lb || le > shape->num_layers)
+  if (!shape || batch < 1 || batch > kMaxBatch || max_nb < 1 || max_nb > kMaxBlocksPerSeq ||
+      total_blocks < 0 || total_blocks > INT32_MAX || lb < 0 || le <= lb || le > shape->num_layers)
     return false;
   const int32_t nl = le - lb;
   const int32_t sb = split_blocks == 0 ? choose_split(batch, max_nb, nl) : split_blocks;
@@ -255,8 +267,8 @@ int kvs_decode_step(const kvs_shape* shape, const void* q, const void* kv_pool, 
   if (!q || !kv_pool || !block_table || !seq_lens || !meta_offsets || !out || !block_mass ||
       !workspace)
     return fail(KVS_E_NULL, "a required pointer is NULL");
-  if (batch < 1) return fail(KVS_E_RANGE, "batch %d < 1", batch);
-  if (max_blocks_per_seq < 1) return fail(KVS_E_RANGE, "max_blocks_per_seq %d < 1", max_blocks_per_seq);
+  rc = check_counts(batch, max_blocks_per_seq);
+  if (rc) return rc;
   if (pool_blocks < 1) return fail(KVS_E_RANGE, "pool_blocks %lld < 1", (long long)pool_blocks);
   if (pool_blocks > INT32_MAX) return fail(KVS_E_RANGE, "pool_blocks exceeds int32 block ids");
   if (total_blocks < 0 || total_blocks > INT32_MAX)
@@ -366,9 +378,10 @@ int kvs_meta_init(kvs_block_meta* meta, const int32_t* meta_offsets, const uint6
                   int32_t batch, int32_t max_blocks_per_seq, int64_t total_blocks,
                   int32_t anchor_blocks, void* stream) {
   if (!meta || !meta_offsets || !seq_ids) return fail(KVS_E_NULL, "a required pointer is NULL");
-  if (batch < 1 || max_blocks_per_seq < 1 || total_blocks < 0 || total_blocks > INT32_MAX ||
-      anchor_blocks < 0)
-    return fail(KVS_E_RANGE, "batch, max_blocks_per_seq, total_blocks or anchor_blocks out of range");
+  int rc = check_counts(batch, max_blocks_per_seq);
+  if (rc) return rc;
+  if (total_blocks < 0 || total_blocks > INT32_MAX || anchor_blocks < 0)
+    return fail(KVS_E_RANGE, "total_blocks or anchor_blocks out of range");
   if (!aligned(meta, 16) || !aligned(seq_ids, 8)) return fail(KVS_E_ALIGN, "meta or seq_ids misaligned");
   kvs::MetaInitArgs a{};
   a.meta = meta;
@@ -392,8 +405,10 @@ int kvs_score_update(kvs_block_meta* meta, const float* block_mass, const int32_
     return fail(KVS_E_NULL, "a required pointer is NULL");
   int rc = check_policy(policy);
   if (rc) return rc;
-  if (batch < 1 || max_blocks_per_seq < 1 || total_blocks < 0 || total_blocks > INT32_MAX)
-    return fail(KVS_E_RANGE, "batch, max_blocks_per_seq or total_blocks out of range");
+  rc = check_counts(batch, max_blocks_per_seq);
+  if (rc) return rc;
+  if (total_blocks < 0 || total_blocks > INT32_MAX)
+    return fail(KVS_E_RANGE, "total_blocks out of range");
   if (classify != 0 && classify != 1) return fail(KVS_E_RANGE, "classify must be 0 or 1");
   if (step == KVS_NEVER_TOUCHED) return fail(KVS_E_RANGE, "step UINT64_MAX is reserved");
   if (!aligned(meta, 16)) return fail(KVS_E_ALIGN, "meta must be 16-byte aligned");
@@ -426,8 +441,10 @@ int kvs_classify(kvs_block_meta* meta, const int32_t* meta_offsets, int32_t batc
   if (!meta || !meta_offsets) return fail(KVS_E_NULL, "a required pointer is NULL");
   int rc = check_policy(policy);
   if (rc) return rc;
-  if (batch < 1 || max_blocks_per_seq < 1 || total_blocks < 0 || total_blocks > INT32_MAX)
-    return fail(KVS_E_RANGE, "batch, max_blocks_per_seq or total_blocks out of range");
+  rc = check_counts(batch, max_blocks_per_seq);
+  if (rc) return rc;
+  if (total_blocks < 0 || total_blocks > INT32_MAX)
+    return fail(KVS_E_RANGE, "total_blocks out of range");
   if (!aligned(meta, 16)) return fail(KVS_E_ALIGN, "meta must be 16-byte aligned");
   kvs::ScoreArgs a{};
   a.meta = meta;

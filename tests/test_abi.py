@@ -88,6 +88,8 @@ def _decode(**over):
     (dict(shp=api.Shape(2, 64, 8, 64, 16)), KVS_E_SHAPE),
     (dict(shp=api.Shape(0, 64, 8, 128, 16)), KVS_E_SHAPE),
     (dict(batch=0), KVS_E_RANGE),
+    (dict(batch=65536), KVS_E_RANGE),
+    (dict(max_blocks=1 << 27), KVS_E_RANGE),
     (dict(max_blocks=0), KVS_E_RANGE),
     (dict(pool_blocks=0), KVS_E_RANGE),
     (dict(layer_begin=1, layer_end=1), KVS_E_RANGE),
