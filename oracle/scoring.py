@@ -14,6 +14,17 @@ records:
   the caller's step number (GQA Per-Head Scoring Streams, per-block state:
   touch count and touch timestamp; under dense attention every block of an
   active sequence is read every step, Visual Reference Sec. 4).
+* lazy decay: a block that is not touched on a step receives input 0, so
+  after a gap of g steps since its last touch its score is
+  S_touch * (1 - alpha)^g (RETRACTIONS Sec. 3: the decaying score whose order
+  the key K = ln S_touch + t_touch * (-ln(1 - alpha)) preserves).  The update
+  at a touch therefore decays the stored score by (1 - alpha)^(step - t_touch);
+  for consecutive steps that is the plain one-step EMA.
+* eviction candidate: per sequence, the block with the lowest decayed score
+  at the current step, ties to the lowest logical block (GQA Per-Head Scoring
+  Streams, panel 3: one ordering per sequence, the coldest block is the
+  eviction candidate; RETRACTIONS Sec. 3: the victim is audited against a
+  brute-force argmin).  Pinned (tier 0) blocks can be excluded.
 * priority: P = w_R * R + w_E * E + w_N * N with R = (b + 1) / nb (recency
   of logical block b among the sequence's nb blocks) and N = 1 for anchor
   blocks b < anchor_blocks (Visual Reference Sec. 12, Diagram 12.1:
@@ -28,7 +39,8 @@ unchanged and reported (steps must increase).
 Parity pins (tests/test_oracle_scoring.py): the printed EMA worked example,
 the EMA closed form on constant input, the printed half-life, closed-form
 tier sets derived by solving the threshold inequalities, exact cut-point
-inclusivity, touch arithmetic.
+inclusivity, touch arithmetic, the decay closed form across gaps, and the
+printed key's ordering against the decayed score.
 """
 from __future__ import annotations
 
@@ -137,7 +149,8 @@ def score_update(state: ScoreState, masses, step: int, pol: Policy, do_classify:
     step_u = np.uint64(step)
     stale = (state.t_touch != NEVER) & (state.t_touch >= step_u)
     upd = ~stale
-    out.score[upd] = ema(state.score[upd], m_hat[upd], pol.alpha)
+    prev = decayed(state, step - 1, pol.alpha)   # input 0 on every step since the last touch
+    out.score[upd] = ema(prev[upd], m_hat[upd], pol.alpha)
     out.touch_count[upd] = state.touch_count[upd] + np.uint32(1)
     out.t_touch[upd] = step_u
     if do_classify:
@@ -145,3 +158,50 @@ def score_update(state: ScoreState, masses, step: int, pol: Policy, do_classify:
         out.priority[upd] = p[upd]
         out.tier[upd] = tier_of(p, pol)[upd]
     return out, stale
+
+
+def decayed(state: ScoreState, t: int, alpha: float):
+    """Score of every record at step t, given input 0 on the steps after its
+    last touch: S_touch * (1 - alpha)^(t - t_touch).  Records never touched
+    keep their (zero) score; records touched after t are returned unchanged."""
+    touched = state.t_touch != NEVER
+    gap = np.zeros(state.score.shape, dtype=np.float64)
+    tt = state.t_touch[touched].astype(np.float64)
+    gap[touched] = np.maximum(0.0, float(t) - tt)
+    return state.score * (1.0 - alpha) ** gap
+
+
+def order_key(state: ScoreState, alpha: float):
+    """The printed order-preserving key K = ln S_touch + t_touch * (-ln(1 - alpha));
+    -inf for a zero score."""
+    with np.errstate(divide="ignore"):
+        k = np.log(state.score) + state.t_touch.astype(np.float64) * (-np.log1p(-alpha))
+    return np.where(state.score > 0.0, k, -np.inf)
+
+
+def eviction_candidates(state: ScoreState, t: int, alpha: float, active=None,
+                        exclude_pinned: bool = False):
+    """Per sequence, the record with the lowest decayed score at step t (brute
+    force over its records; ties to the lowest logical block).  Returns
+    (block index or -1, decayed score or +inf) per sequence; inactive
+    sequences and sequences with no eligible record give (-1, +inf)."""
+    s_now = decayed(state, t, alpha)
+    nseq = int(state.seq_index.max()) + 1 if state.seq_index.size else 0
+    blocks = np.full(nseq, -1, dtype=np.int64)
+    scores = np.full(nseq, np.inf)
+    for s in range(nseq):
+        if active is not None and not active[s]:
+            continue
+        rows = np.nonzero(state.seq_index == s)[0]
+        best = -1
+        for r in rows:
+            if exclude_pinned and state.tier[r] == 0:
+                continue
+            if state.t_touch[r] != NEVER and int(state.t_touch[r]) > t:
+                continue
+            if best < 0 or s_now[r] < s_now[best]:
+                best = r
+        if best >= 0:
+            blocks[s] = int(state.block[best])
+            scores[s] = s_now[best]
+    return blocks, scores

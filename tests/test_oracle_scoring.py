@@ -168,3 +168,73 @@ def test_classify_without_update_is_pure():
         c.priority, 0.25 * np.arange(1, 7) / 6 + 0.55 * 0.15 * np.arange(1, 7) / 6
         + 0.2 * (np.arange(6) == 0), rtol=1e-14)
     assert np.array_equal(c.score, st.score)
+
+
+def test_decay_across_a_gap_closed_form():
+    """A block touched at step 0 and next at step 5 decays by (1 - alpha)^5
+    between the two touches (input 0 on the untouched steps)."""
+    alpha, c5 = 0.15, 0.4
+    st = S.init_state([1], [0])
+    st, _ = S.score_update(st, [np.array([1.0])], 0, S.Policy(alpha=alpha))
+    assert math.isclose(st.score[0], alpha * 1.0)
+    # scores are normalised per sequence, so a one-block sequence always sees 1
+    st5, _ = S.score_update(st, [np.array([c5])], 5, S.Policy(alpha=alpha))
+    expect = alpha * 1.0 + (1 - alpha) ** 5 * (alpha * 1.0)
+    assert math.isclose(st5.score[0], expect, rel_tol=1e-14)
+    # decayed() between touches is the closed form
+    for t in range(0, 6):
+        assert math.isclose(float(S.decayed(st, t, alpha)[0]), alpha * (1 - alpha) ** t,
+                            rel_tol=1e-14)
+
+
+def test_printed_key_orders_like_the_decayed_score():
+    """K = ln S_touch + t_touch * (-ln(1 - alpha)) orders records exactly as their
+    decayed scores at any later step (RETRACTIONS Sec. 3)."""
+    rng = np.random.default_rng(5)
+    for alpha in (0.01, 0.05, 0.15, 0.5):
+        st = S.init_state([200], [0])
+        st.score = rng.uniform(1e-4, 1.0, 200)
+        st.t_touch = rng.integers(0, 40, 200).astype(np.uint64)
+        k = S.order_key(st, alpha)
+        for t in (40, 41, 57, 100):
+            d = S.decayed(st, t, alpha)
+            # same order, and K - t * (-ln(1 - alpha)) is ln of the decayed score
+            assert np.array_equal(np.argsort(k, kind="stable"), np.argsort(d, kind="stable"))
+            np.testing.assert_allclose(k - t * (-math.log1p(-alpha)), np.log(d), rtol=0,
+                                       atol=1e-10)
+
+
+def test_stale_high_keys_mislead_a_lazy_heap():
+    """The defect the printed key fixes: judged by stored scores, the block
+    touched long ago looks hotter than it is; judged by the decayed score
+    (or the key), it is the coldest."""
+    alpha = 0.15
+    st = S.init_state([2], [0])
+    st.score = np.array([0.5, 0.3])
+    st.t_touch = np.array([0, 30], dtype=np.uint64)
+    assert np.argmin(st.score) == 1
+    blocks, scores = S.eviction_candidates(st, 30, alpha)
+    assert blocks[0] == 0
+    assert math.isclose(scores[0], 0.5 * (1 - alpha) ** 30)
+    assert np.argmin(S.order_key(st, alpha)) == 0
+
+
+def test_eviction_candidates_ties_masks_and_pins():
+    st = S.init_state([4, 3], [0, 1])
+    st.score = np.array([0.2, 0.1, 0.1, 0.4, 0.3, 0.3, 0.9])
+    st.t_touch = np.full(7, 10, dtype=np.uint64)
+    st.tier = np.array([1, 0, 1, 1, 2, 2, 0], dtype=np.uint8)
+    b, _ = S.eviction_candidates(st, 10, 0.1)
+    assert b.tolist() == [1, 0]                       # ties go to the lowest block
+    b, _ = S.eviction_candidates(st, 10, 0.1, exclude_pinned=True)
+    assert b.tolist() == [2, 0]
+    b, sc = S.eviction_candidates(st, 10, 0.1, active=[False, True])
+    assert b.tolist() == [-1, 0] and sc[0] == np.inf
+    st.tier[:] = 0
+    b, _ = S.eviction_candidates(st, 10, 0.1, exclude_pinned=True)
+    assert b.tolist() == [-1, -1]
+    # a never-touched record (score 0) is the coldest
+    st2 = S.init_state([3], [0])
+    st2.score = np.array([0.3, 0.0, 0.2])
+    st2.t_touch = np.array([5, S.NEVER, 5], dtype=np.uint64)
+    assert S.eviction_candidates(st2, 6, 0.1)[0].tolist() == [1]
