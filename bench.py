@@ -248,6 +248,21 @@ def main():
     if not (rec["touch_count"] == args.steps).all() or not (rec["t_touch"] == args.steps - 1).all():
         raise RuntimeError("touch counts / timestamps do not match the steps run")
 
+    # eviction candidates over the same records (the step after classification;
+    # timed on its own, outside the step)
+    ev_ms = []
+    for _ in range(5):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        blk, _key = sess.evict_candidates(args.steps - 1, alpha)
+        e1.record(stream)
+        e1.synchronize()
+        ev_ms.append(e0.elapsed_time(e1))
+    ev_ms.sort()
+    if int(blk.min().item()) < 0:
+        raise RuntimeError("a sequence got no eviction candidate")
+
     kv_bytes = sess.kv_bytes_per_step
     unique_bytes = m.unique_blocks * 16 * m.num_layers * 8 * 128 * 2 * 2
     t_step = total_ms / 1e3 / args.steps
@@ -299,6 +314,7 @@ def main():
         "decode_kernel_ms": round(dec_avg * 1e3, 4),
         "decode_share_of_step": round(dec_avg / t_step, 4),
         "tier_counts": tiers,
+        "evict_candidates_us": round(ev_ms[len(ev_ms) // 2] * 1e3, 2),
         "host_wall_s": round(wall, 4),
         "copy_probe": probe,
         "frac_of_copy_probe": round(value / probe["gbps"], 4) if probe else None,

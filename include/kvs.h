@@ -232,7 +232,10 @@ int kvs_meta_init(kvs_block_meta* meta, const int32_t* meta_offsets,
 
 /* One scoring step over every record of every sequence in the batch:
  * m_hat = block_mass / max over the sequence's blocks (0 if that max is 0),
- * E <- alpha m_hat + (1 - alpha) E in fp64, touch_count += 1, t_touch = step.
+ * E <- alpha m_hat + (1 - alpha) E_prev in fp64, where E_prev is the stored
+ * score decayed by (1 - alpha)^(step - t_touch - 1) for a record whose last
+ * touch is older than the previous step (input 0 on untouched steps;
+ * RETRACTIONS, Sec. 3), touch_count += 1, t_touch = step.
  * With classify != 0 also priority and tier (as kvs_classify).  A record whose
  * t_touch is not KVS_NEVER_TOUCHED and >= step is left unchanged
  * (KVS_DEV_STALE_STEP).  workspace: kvs_score_workspace_bytes() bytes. */
@@ -250,6 +253,30 @@ int kvs_score_update(kvs_block_meta* meta, const float* block_mass,
 int kvs_classify(kvs_block_meta* meta, const int32_t* meta_offsets, int32_t batch,
                  int32_t max_blocks_per_seq, int64_t total_blocks,
                  const kvs_policy* policy, uint8_t* tiers_out, void* stream);
+
+/* Workspace bytes kvs_evict_candidates needs (status header + per-chunk partials). */
+size_t kvs_evict_workspace_bytes(int32_t batch, int32_t max_blocks_per_seq);
+
+/* Eviction candidate of each sequence at step `now`: the record with the lowest
+ * decayed score, where a record's score decays by (1 - alpha) on every step
+ * after its last touch (RETRACTIONS, Sec. 3; GQA Per-Head Scoring Streams,
+ * panel 3: one ordering per sequence, the coldest block is the candidate).
+ * The order is taken on the key K = ln score + t_touch * (-ln(1 - alpha)),
+ * which orders records exactly as their decayed scores at any time; a zero
+ * score (never attended) ranks lowest.  Ties go to the lowest logical block.
+ *  active          uint8 [batch], device, nullable: sequences with 0 get no
+ *                  candidate (out_block -1, out_key +inf).
+ *  exclude_pinned  1: tier-0 records are never candidates.
+ *  out_block       int32 [batch], device: logical block, or -1 if none.
+ *  out_key         double [batch], device: the candidate's K, or +inf.
+ * Records with t_touch > now are skipped (KVS_DEV_STALE_STEP).  alpha in (0, 1).
+ * workspace: kvs_evict_workspace_bytes() bytes, 256-B aligned, header zeroed
+ * once by kvs_workspace_init(). */
+int kvs_evict_candidates(const kvs_block_meta* meta, const int32_t* meta_offsets,
+                         const uint8_t* active, int32_t batch, int32_t max_blocks_per_seq,
+                         int64_t total_blocks, uint64_t now, double alpha, int exclude_pinned,
+                         int32_t* out_block, double* out_key, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

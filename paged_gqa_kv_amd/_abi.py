@@ -33,7 +33,7 @@ EXPORTS = (
     "kvs_decode_workspace_bytes", "kvs_score_workspace_bytes", "kvs_status_string",
     "kvs_last_error", "kvs_workspace_init", "kvs_device_status", "kvs_decode_step",
     "kvs_meta_init", "kvs_score_update", "kvs_classify", "kvs_set_decode_events",
-    "kvs_stream_probe",
+    "kvs_stream_probe", "kvs_evict_workspace_bytes", "kvs_evict_candidates",
 )
 
 
@@ -83,6 +83,10 @@ _SIGS = {
     "kvs_classify": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i64, ctypes.POINTER(Policy), _vp, _vp]),
     "kvs_set_decode_events": (ctypes.c_int, [_vp, _vp]),
     "kvs_stream_probe": (ctypes.c_int, [_vp, _vp, _sz, ctypes.c_int, _i32, _vp]),
+    "kvs_evict_workspace_bytes": (_sz, [_i32, _i32]),
+    "kvs_evict_candidates": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i64, ctypes.c_uint64,
+                                            ctypes.c_double, ctypes.c_int, _vp, _vp, _vp, _sz,
+                                            _vp]),
 }
 
 _LIB = None

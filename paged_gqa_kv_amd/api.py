@@ -144,6 +144,19 @@ def classify(meta, meta_offsets, batch: int, max_blocks: int, total_blocks: int,
                              ctypes.byref(pol), _p(tiers_out), _s(stream)))
 
 
+def evict_workspace_bytes(batch: int, max_blocks: int) -> int:
+    return lib().kvs_evict_workspace_bytes(batch, max_blocks)
+
+
+def evict_candidates(meta, meta_offsets, active, batch: int, max_blocks: int, total_blocks: int,
+                     now: int, alpha: float, exclude_pinned: int, out_block, out_key, workspace,
+                     workspace_bytes=None, stream=None) -> None:
+    ws_bytes = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    check(lib().kvs_evict_candidates(_p(meta), _p(meta_offsets), _p(active), batch, max_blocks,
+                                     total_blocks, now, alpha, exclude_pinned, _p(out_block),
+                                     _p(out_key), _p(workspace), ws_bytes, _s(stream)))
+
+
 def records(meta: torch.Tensor):
     """Copy a device record array (uint8 [n][64] or any 64-byte-row tensor) to a
     numpy structured array with META_DTYPE."""

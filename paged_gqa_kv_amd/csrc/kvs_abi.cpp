@@ -435,6 +435,57 @@ int kvs_score_update(kvs_block_meta* meta, const float* block_mass, const int32_
   return ok();
 }
 
+size_t kvs_evict_workspace_bytes(int32_t batch, int32_t max_blocks_per_seq) {
+  if (batch < 1 || batch > kMaxBatch || max_blocks_per_seq < 1 || max_blocks_per_seq > kMaxBlocksPerSeq)
+    return 0;
+  const uint64_t chunks = (uint64_t)(max_blocks_per_seq + kvs::kScoreThreads - 1) / kvs::kScoreThreads;
+  return align_up(align_up(kHeader + (uint64_t)batch * chunks * 8u) + (uint64_t)batch * chunks * 4u);
+}
+
+int kvs_evict_candidates(const kvs_block_meta* meta, const int32_t* meta_offsets,
+                         const uint8_t* active, int32_t batch, int32_t max_blocks_per_seq,
+                         int64_t total_blocks, uint64_t now, double alpha, int exclude_pinned,
+                         int32_t* out_block, double* out_key, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!meta || !meta_offsets || !out_block || !out_key || !workspace)
+    return fail(KVS_E_NULL, "a required pointer is NULL");
+  int rc = check_counts(batch, max_blocks_per_seq);
+  if (rc) return rc;
+  if (total_blocks < 0 || total_blocks > INT32_MAX)
+    return fail(KVS_E_RANGE, "total_blocks out of range");
+  if (exclude_pinned != 0 && exclude_pinned != 1)
+    return fail(KVS_E_RANGE, "exclude_pinned must be 0 or 1");
+  if (now == KVS_NEVER_TOUCHED) return fail(KVS_E_RANGE, "now UINT64_MAX is reserved");
+  if (!std::isfinite(alpha) || !(alpha > 0.0 && alpha < 1.0))
+    return fail(KVS_E_POLICY, "alpha %.17g not in (0, 1)", alpha);
+  if (!aligned(meta, 16) || !aligned(out_key, 8) || !aligned(out_block, 4))
+    return fail(KVS_E_ALIGN, "meta, out_key or out_block misaligned");
+  if (!aligned(workspace, kAlign)) return fail(KVS_E_ALIGN, "workspace must be 256-byte aligned");
+  const size_t need = kvs_evict_workspace_bytes(batch, max_blocks_per_seq);
+  if (workspace_bytes < need)
+    return fail(KVS_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  const int32_t chunks = (max_blocks_per_seq + kvs::kScoreThreads - 1) / kvs::kScoreThreads;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  kvs::EvictArgs a{};
+  a.meta = meta;
+  a.meta_off = meta_offsets;
+  a.active = active;
+  a.part_key = reinterpret_cast<double*>(ws + kHeader);
+  a.part_idx = reinterpret_cast<int32_t*>(ws + align_up(kHeader + (size_t)batch * chunks * 8u));
+  a.out_block = out_block;
+  a.out_key = out_key;
+  a.total_blocks = total_blocks;
+  a.now = now;
+  a.neg_log_keep = -std::log1p(-alpha);
+  a.max_nb = max_blocks_per_seq;
+  a.max_chunks = chunks;
+  a.exclude_pinned = exclude_pinned;
+  a.status = static_cast<uint32_t*>(workspace);
+  hipError_t e = kvs::launch_evict(a, batch, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "eviction-candidate launch");
+  return ok();
+}
+
 int kvs_classify(kvs_block_meta* meta, const int32_t* meta_offsets, int32_t batch,
                  int32_t max_blocks_per_seq, int64_t total_blocks, const kvs_policy* policy,
                  uint8_t* tiers_out, void* stream) {

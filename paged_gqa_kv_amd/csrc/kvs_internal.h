@@ -84,6 +84,23 @@ struct ScoreArgs {
   uint32_t* status;
 };
 
+struct EvictArgs {
+  const kvs_block_meta* meta;
+  const int32_t* meta_off;
+  const uint8_t* active;    // nullable
+  double* part_key;         // [B][max_chunks]
+  int32_t* part_idx;        // [B][max_chunks]
+  int32_t* out_block;       // [B]
+  double* out_key;          // [B]
+  int64_t total_blocks;
+  uint64_t now;
+  double neg_log_keep;      // -ln(1 - alpha)
+  int32_t max_nb;
+  int32_t max_chunks;
+  int32_t exclude_pinned;
+  uint32_t* status;
+};
+
 struct MetaInitArgs {
   kvs_block_meta* meta;
   const int32_t* meta_off;
@@ -101,6 +118,7 @@ hipError_t launch_mass(const MassArgs& a, int batch, hipStream_t stream);
 hipError_t launch_score(const ScoreArgs& a, int batch, hipStream_t stream);
 hipError_t launch_classify(const ScoreArgs& a, int batch, hipStream_t stream);
 hipError_t launch_meta_init(const MetaInitArgs& a, int batch, hipStream_t stream);
+hipError_t launch_evict(const EvictArgs& a, int batch, hipStream_t stream);
 hipError_t launch_clear(uint32_t* p, int n, hipStream_t stream);
 hipError_t launch_probe(const void* src, void* dst, size_t bytes, int mode, int grid,
                         hipStream_t stream);

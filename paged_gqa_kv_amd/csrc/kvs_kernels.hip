@@ -465,7 +465,12 @@ __global__ void __launch_bounds__(kScoreThreads) score_update(ScoreArgs a) {
       stale = true;
     } else {
       const double mh = M > 0.f ? (double)a.mass[r0 + b] / (double)M : 0.0;
-      const double e = a.pol.alpha * mh + (1.0 - a.pol.alpha) * rec->score;
+      // Input 0 on the steps since the last touch: the stored score first
+      // decays over the gap, then takes the one-step update.
+      double prev = rec->score;
+      if (tt != KVS_NEVER_TOUCHED && a.step - tt > 1)
+        prev *= pow(1.0 - a.pol.alpha, (double)(a.step - tt - 1));
+      const double e = a.pol.alpha * mh + (1.0 - a.pol.alpha) * prev;
       rec->score = e;
       rec->touch_count = rec->touch_count + 1u;
       rec->t_touch = a.step;
@@ -479,6 +484,99 @@ __global__ void __launch_bounds__(kScoreThreads) score_update(ScoreArgs a) {
     }
   }
   if (__ballot(stale) != 0ull && (threadIdx.x & 63) == 0) flag(a.status, KVS_DEV_STALE_STEP);
+}
+
+// ---------------------------------------------------------------------------
+// eviction candidates: per sequence, argmin over its records of the
+// order-preserving key K = ln score + t_touch * (-ln(1 - alpha)) (a zero score
+// gives -inf), ties to the lowest logical block.  Pass 1 reduces chunks of
+// kScoreThreads records, pass 2 the chunks; both in a fixed order.
+// ---------------------------------------------------------------------------
+struct KeyIdx {
+  double key;
+  int32_t idx;   // logical block, or -1 for none
+};
+
+__device__ __forceinline__ KeyIdx better(KeyIdx x, KeyIdx y) {
+  if (x.idx < 0) return y;
+  if (y.idx < 0) return x;
+  if (y.key < x.key || (y.key == x.key && y.idx < x.idx)) return y;
+  return x;
+}
+
+__device__ __forceinline__ KeyIdx block_reduce_argmin(KeyIdx v, double* rk, int32_t* ri) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    KeyIdx o;
+    o.key = __shfl_xor(v.key, m, 64);
+    o.idx = __shfl_xor(v.idx, m, 64);
+    v = better(v, o);
+  }
+  const int wv = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    rk[wv] = v.key;
+    ri[wv] = v.idx;
+  }
+  __syncthreads();
+  KeyIdx r{rk[0], ri[0]};
+#pragma unroll
+  for (int k = 1; k < kScoreThreads / 64; ++k) r = better(r, KeyIdx{rk[k], ri[k]});
+  __syncthreads();
+  return r;
+}
+
+__global__ void __launch_bounds__(kScoreThreads) evict_chunks(EvictArgs a) {
+  __shared__ double rk[kScoreThreads / 64];
+  __shared__ int32_t ri[kScoreThreads / 64];
+  const int s = blockIdx.y;
+  const int chunk = blockIdx.x;
+  int r0 = 0;
+  const int nb = seq_records(a.meta_off, s, a.max_nb, a.total_blocks, a.status,
+                             threadIdx.x == 0 && chunk == 0, &r0);
+  if (nb <= 0 || chunk * kScoreThreads >= nb) return;
+  const bool active = a.active == nullptr || a.active[s] != 0;
+  const int b = chunk * kScoreThreads + threadIdx.x;
+  KeyIdx v{0.0, -1};
+  bool future = false;
+  if (active && b < nb) {
+    const kvs_block_meta* rec = a.meta + r0 + b;
+    const uint64_t tt = rec->t_touch;
+    const bool pinned = a.exclude_pinned && rec->tier == 0;
+    future = tt != KVS_NEVER_TOUCHED && tt > a.now;
+    if (!pinned && !future) {
+      const double sc = rec->score;
+      const double t = tt == KVS_NEVER_TOUCHED ? 0.0 : (double)tt;
+      v.key = sc > 0.0 ? log(sc) + t * a.neg_log_keep : -INFINITY;
+      v.idx = b;
+    }
+  }
+  if (__ballot(future) != 0ull && (threadIdx.x & 63) == 0) flag(a.status, KVS_DEV_STALE_STEP);
+  const KeyIdx r = block_reduce_argmin(v, rk, ri);
+  if (threadIdx.x == 0) {
+    a.part_key[(size_t)s * a.max_chunks + chunk] = r.key;
+    a.part_idx[(size_t)s * a.max_chunks + chunk] = r.idx;
+  }
+}
+
+__global__ void __launch_bounds__(kScoreThreads) evict_final(EvictArgs a) {
+  __shared__ double rk[kScoreThreads / 64];
+  __shared__ int32_t ri[kScoreThreads / 64];
+  const int s = blockIdx.x;
+  int r0 = 0;
+  const int nb = seq_records(a.meta_off, s, a.max_nb, a.total_blocks, a.status, false, &r0);
+  const bool active = a.active == nullptr || a.active[s] != 0;
+  KeyIdx v{0.0, -1};
+  if (nb > 0 && active) {
+    const int nch = (nb + kScoreThreads - 1) / kScoreThreads;
+    for (int k = threadIdx.x; k < nch; k += kScoreThreads)
+      v = better(v, KeyIdx{a.part_key[(size_t)s * a.max_chunks + k],
+                           a.part_idx[(size_t)s * a.max_chunks + k]});
+  }
+  const KeyIdx r = block_reduce_argmin(v, rk, ri);
+  if (threadIdx.x == 0) {
+    a.out_block[s] = r.idx;
+    a.out_key[s] = r.idx < 0 ? INFINITY : r.key;
+  }
 }
 
 __global__ void __launch_bounds__(kScoreThreads) classify_records(ScoreArgs a) {
@@ -592,6 +690,12 @@ hipError_t launch_score(const ScoreArgs& a, int batch, hipStream_t stream) {
 hipError_t launch_classify(const ScoreArgs& a, int batch, hipStream_t stream) {
   const dim3 grid(a.max_chunks, batch);
   hipLaunchKernelGGL(classify_records, grid, dim3(kScoreThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_evict(const EvictArgs& a, int batch, hipStream_t stream) {
+  hipLaunchKernelGGL(evict_chunks, dim3(a.max_chunks, batch), dim3(kScoreThreads), 0, stream, a);
+  hipLaunchKernelGGL(evict_final, dim3(batch), dim3(kScoreThreads), 0, stream, a);
   return hipGetLastError();
 }
 

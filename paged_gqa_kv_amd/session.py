@@ -67,12 +67,29 @@ class DecodeSession:
         api.classify(self.meta, m.meta_offsets, m.batch, m.max_blocks, m.total_blocks, pol,
                      tiers_out, stream=self.stream)
 
+    def evict_candidates(self, now: int, alpha: float, active=None, exclude_pinned: int = 0):
+        """(out_block int32 [B], out_key float64 [B]) device tensors."""
+        m = self.m
+        if not hasattr(self, "evict_ws"):
+            self.evict_ws = torch.empty(api.evict_workspace_bytes(m.batch, m.max_blocks),
+                                        dtype=torch.uint8, device=self.out.device)
+            api.workspace_init(self.evict_ws, stream=self.stream)
+        blk = torch.empty(m.batch, dtype=torch.int32, device=self.out.device)
+        key = torch.empty(m.batch, dtype=torch.float64, device=self.out.device)
+        api.evict_candidates(self.meta, m.meta_offsets, active, m.batch, m.max_blocks,
+                             m.total_blocks, now, alpha, exclude_pinned, blk, key, self.evict_ws,
+                             stream=self.stream)
+        return blk, key
+
     def step(self, q, step: int, pol, classify: int = 1):
         self.decode(q)
         self.score(step, pol, classify)
 
     def status(self) -> int:
-        return api.device_status(self.ws, self.stream) | api.device_status(self.score_ws, self.stream)
+        bits = api.device_status(self.ws, self.stream) | api.device_status(self.score_ws, self.stream)
+        if hasattr(self, "evict_ws"):
+            bits |= api.device_status(self.evict_ws, self.stream)
+        return bits
 
     def records(self):
         return api.records(self.meta[: self.m.total_blocks])
