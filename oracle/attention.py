@@ -31,25 +31,38 @@ from __future__ import annotations
 
 import numpy as np
 
+from . import fp8
+
 BLOCK_TOKENS = 16
 GROUP = 8  # query heads per KV head
 
 
-def gather_layer(pool, table_row, n_tokens: int, layer: int, kv_head=None):
+def _values(raw, kv_format: str):
+    """Stored K/V elements to fp64: fp16 values, or E4M3 codes (uint8)."""
+    if kv_format == "fp16":
+        return np.asarray(raw, dtype=np.float64)
+    if kv_format == "e4m3":
+        return fp8.decode_pool(raw)
+    raise ValueError(f"unknown KV format {kv_format}")
+
+
+def gather_layer(pool, table_row, n_tokens: int, layer: int, kv_head=None,
+                 kv_format: str = "fp16"):
     """K and V of one sequence at one layer, fp64.
 
-    pool:      array [P][L][2][H_kv][16][D] (fp16), indexable with numpy ints.
+    pool:      array [P][L][2][H_kv][16][D] of fp16 values or E4M3 codes,
+               indexable with numpy ints.
     table_row: physical block id of each logical block.
     Returns K, V shaped [H_kv][n][D] (or [n][D] when kv_head is given).
     """
     nb = -(-n_tokens // BLOCK_TOKENS)
     pids = np.asarray(table_row[:nb], dtype=np.int64)
     if kv_head is None:
-        blocks = np.asarray(pool[pids, layer], dtype=np.float64)       # [nb][2][H][16][D]
+        blocks = _values(pool[pids, layer], kv_format)                  # [nb][2][H][16][D]
         kv = blocks.transpose(1, 2, 0, 3, 4)                           # [2][H][nb][16][D]
         kv = kv.reshape(2, kv.shape[1], nb * BLOCK_TOKENS, kv.shape[-1])[:, :, :n_tokens]
         return kv[0], kv[1]
-    blocks = np.asarray(pool[pids, layer, :, kv_head], dtype=np.float64)  # [nb][2][16][D]
+    blocks = _values(pool[pids, layer, :, kv_head], kv_format)            # [nb][2][16][D]
     kv = blocks.transpose(1, 0, 2, 3).reshape(2, nb * BLOCK_TOKENS, blocks.shape[-1])
     return kv[0, :n_tokens], kv[1, :n_tokens]
 
@@ -74,12 +87,13 @@ def block_sums(p, n_tokens: int):
     return padded.reshape(nb, BLOCK_TOKENS).sum(axis=1)
 
 
-def decode_layer(q_sl, pool, table_row, n_tokens: int, layer: int, scale: float):
+def decode_layer(q_sl, pool, table_row, n_tokens: int, layer: int, scale: float,
+                 kv_format: str = "fp16"):
     """All 64 query heads of one (sequence, layer).
 
     Returns out [64][D] fp64 and the block mass of this layer [nb] fp64.
     """
-    K, V = gather_layer(pool, table_row, n_tokens, layer)
+    K, V = gather_layer(pool, table_row, n_tokens, layer, kv_format=kv_format)
     n_q = q_sl.shape[0]
     out = np.empty((n_q, K.shape[-1]), dtype=np.float64)
     mass = np.zeros(-(-n_tokens // BLOCK_TOKENS), dtype=np.float64)
@@ -91,11 +105,12 @@ def decode_layer(q_sl, pool, table_row, n_tokens: int, layer: int, scale: float)
 
 
 def decode_step(q, pool, block_table, seq_lens, scale: float,
-                layer_begin: int = 0, layer_end=None):
+                layer_begin: int = 0, layer_end=None, kv_format: str = "fp16"):
     """One decode step for a batch.
 
     q: [B][L][64][D]; pool: [P][L][2][8][16][D]; block_table: [B][max_nb];
-    seq_lens: [B] token counts.
+    seq_lens: [B] token counts; kv_format: "fp16" (pool holds values) or
+    "e4m3" (pool holds E4M3 codes, Fitting a Million Tokens Sec. 02).
     Returns out [B][L][64][D] fp64 (NaN outside [layer_begin, layer_end)) and a
     list with one fp64 array [nb_s] of block mass per sequence, summed over the
     layers in range and all query heads.
@@ -110,7 +125,8 @@ def decode_step(q, pool, block_table, seq_lens, scale: float,
         n = int(seq_lens[s])
         mass = np.zeros(-(-n // BLOCK_TOKENS), dtype=np.float64)
         for layer in range(layer_begin, layer_end):
-            out[s, layer], m = decode_layer(q[s, layer], pool, block_table[s], n, layer, scale)
+            out[s, layer], m = decode_layer(q[s, layer], pool, block_table[s], n, layer, scale,
+                                            kv_format)
             mass += m
         masses.append(mass)
     return out, masses

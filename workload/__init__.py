@@ -12,6 +12,7 @@ from .recipe import (  # noqa: F401
     Workload,
     Materialised,
     WORKLOADS,
+    as_e4m3,
     custom,
     materialise,
     make_query,

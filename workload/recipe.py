@@ -18,8 +18,10 @@ What is drawn (no step of the method is computed here):
   section assumes (Visual Reference Sec. 6).  Rounding to fp16 happens once,
   after the addition.
 * Physical placement is a seeded random permutation of the pool; pool
-  blocks that no table references are filled with fp16 NaN so that a stray
-  read poisons the result.
+  blocks that no table references are filled with NaN (fp16 NaN, or the E4M3
+  NaN code 0x7F) so that a stray read poisons the result.
+* kv_format "e4m3" stores the same drawn values rounded once to FP8 E4M3
+  codes with no scale (Fitting a Million Tokens, Sec. 02).
 * A shared prefix is expressed the paged way: the same physical ids appear
   in several tables and carry a reference count (KV cache offload blog,
   "Top row").  Shared blocks take only the block-0 boost; the recent-tail
@@ -66,6 +68,7 @@ class Workload:
     q_boost: float = 4.0
     k_boost: float = 0.5
     recent_den: int = 10                      # "last 1/recent_den of positions"
+    kv_format: str = "fp16"                   # "fp16" values or "e4m3" codes (uint8)
 
     def lengths(self) -> list:
         if self.seq_lens is not None:
@@ -105,13 +108,18 @@ WORKLOADS = {
 def custom(name: str, num_layers: int, seq_lens: Sequence[int], *, seed: int = 7,
            steps: int = 3, alphas=(0.15,), pool_blocks: Optional[int] = None,
            spare_blocks: int = 4, shared_prefix_tokens: int = 0,
-           q_boost: float = 4.0, k_boost: float = 0.5) -> Workload:
+           q_boost: float = 4.0, k_boost: float = 0.5, kv_format: str = "fp16") -> Workload:
     """A small ad-hoc workload with the same recipe (ragged lengths allowed)."""
     return Workload(name, num_layers=num_layers, batch=len(seq_lens), steps=steps,
                     alphas=tuple(alphas), seed=seed, seq_lens=tuple(int(n) for n in seq_lens),
                     pool_blocks=pool_blocks, spare_blocks=spare_blocks,
                     shared_prefix_tokens=shared_prefix_tokens,
-                    q_boost=q_boost, k_boost=k_boost)
+                    q_boost=q_boost, k_boost=k_boost, kv_format=kv_format)
+
+
+def as_e4m3(wl: Workload) -> Workload:
+    """The same workload with the KV pool stored as E4M3 codes."""
+    return dataclasses.replace(wl, name=wl.name + "-e4m3", kv_format="e4m3")
 
 
 @dataclasses.dataclass
@@ -199,8 +207,11 @@ def materialise(wl: Workload, device="cpu") -> Materialised:
                     dtype=torch.float32)
     u = u / u.norm(dim=-1, keepdim=True)
 
+    if wl.kv_format not in ("fp16", "e4m3"):
+        raise ValueError(f"unknown KV format {wl.kv_format}")
+    fp8 = wl.kv_format == "e4m3"
     pool = torch.empty((pool_n, L, 2, NUM_KV_HEADS, BLOCK_TOKENS, HEAD_DIM),
-                       dtype=torch.float16, device=device)
+                       dtype=torch.uint8 if fp8 else torch.float16, device=device)
     bp, bo = _boost_positions(wl, lens, table, shared_nb)
     bp_t = torch.from_numpy(bp).to(device)
     bo_t = torch.from_numpy(bo).to(device)
@@ -216,12 +227,15 @@ def materialise(wl: Workload, device="cpu") -> Materialised:
                     pid = bp_t[sel] - c0
                     off = bo_t[sel]
                     x[pid, 0, :, off, :] += wl.k_boost * u[layer]
-            pool[c0:c1, layer].copy_(x.to(torch.float16))
+            if fp8:   # one rounding, straight to E4M3 (no scale)
+                pool[c0:c1, layer].copy_(x.to(torch.float8_e4m3fn).view(torch.uint8))
+            else:
+                pool[c0:c1, layer].copy_(x.to(torch.float16))
             del x
     referenced = refcount > 0
     unused = np.nonzero(~referenced)[0]
     if unused.size:
-        pool[torch.from_numpy(unused).to(device)] = float("nan")
+        pool[torch.from_numpy(unused).to(device)] = 0x7F if fp8 else float("nan")
 
     offsets = np.zeros(wl.batch + 1, dtype=np.int32)
     offsets[1:] = np.cumsum(blocks)
