@@ -221,6 +221,27 @@ int kvs_decode_step(const kvs_shape* shape,
                     void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* The same step over a pool of FP8 E4M3 codes: kv_pool is uint8
+ * [pool_blocks][num_layers][2][8][16][128] holding OCP E4M3 codes with no scale
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 encodes
+ * m * 2^-9; 0x7F / 0xFF are NaN), half the bytes of the fp16 pool (Fitting a
+ * Million Tokens, Sec. 02: FP8 E4M3 KV, no calibration).  Every code is
+ * dequantised exactly to fp16 inside the kernel; q, out, the block mass and all
+ * other arguments, sizes and rules are those of kvs_decode_step (the workspace
+ * of kvs_decode_workspace_bytes serves both). */
+int kvs_decode_step_e4m3(const kvs_shape* shape,
+                         const void* q,
+                         const void* kv_pool, int64_t pool_blocks,
+                         const int32_t* block_table, int32_t max_blocks_per_seq,
+                         const int32_t* seq_lens, const int32_t* meta_offsets,
+                         int32_t batch, int64_t total_blocks,
+                         int32_t layer_begin, int32_t layer_end,
+                         float scale,
+                         void* out, float* block_mass, int accumulate,
+                         int32_t split_blocks,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
+
 /* Initialise records [0, total_blocks): key = {seq_ids[s], b}, score 0,
  * t_touch = KVS_NEVER_TOUCHED, touch_count 0, tier = KVS_UNCLASSIFIED,
  * flags = KVS_FLAG_ANCHOR when b < anchor_blocks, priority 0, reserved 0.

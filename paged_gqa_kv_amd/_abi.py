@@ -34,6 +34,7 @@ EXPORTS = (
     "kvs_last_error", "kvs_workspace_init", "kvs_device_status", "kvs_decode_step",
     "kvs_meta_init", "kvs_score_update", "kvs_classify", "kvs_set_decode_events",
     "kvs_stream_probe", "kvs_evict_workspace_bytes", "kvs_evict_candidates",
+    "kvs_decode_step_e4m3",
 )
 
 
@@ -75,6 +76,9 @@ _SIGS = {
     "kvs_workspace_init": (ctypes.c_int, [_vp, _sz, _vp]),
     "kvs_device_status": (ctypes.c_int, [_vp, _vp, ctypes.POINTER(ctypes.c_uint32)]),
     "kvs_decode_step": (ctypes.c_int, [
+        ctypes.POINTER(Shape), _vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _i64, _i32, _i32,
+        ctypes.c_float, _vp, _vp, ctypes.c_int, _i32, _vp, _sz, _vp]),
+    "kvs_decode_step_e4m3": (ctypes.c_int, [
         ctypes.POINTER(Shape), _vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _i64, _i32, _i32,
         ctypes.c_float, _vp, _vp, ctypes.c_int, _i32, _vp, _sz, _vp]),
     "kvs_meta_init": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i64, _i32, _vp]),

@@ -256,12 +256,16 @@ int kvs_device_status(void* workspace, void* stream, uint32_t* bits) {
   return ok();
 }
 
-int kvs_decode_step(const kvs_shape* shape, const void* q, const void* kv_pool, int64_t pool_blocks,
-                    const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
-                    const int32_t* meta_offsets, int32_t batch, int64_t total_blocks,
-                    int32_t layer_begin, int32_t layer_end, float scale, void* out,
-                    float* block_mass, int accumulate, int32_t split_blocks, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int decode_step(bool kv_e4m3, const kvs_shape* shape, const void* q, const void* kv_pool,
+                int64_t pool_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
+                const int32_t* seq_lens, const int32_t* meta_offsets, int32_t batch,
+                int64_t total_blocks, int32_t layer_begin, int32_t layer_end, float scale,
+                void* out, float* block_mass, int accumulate, int32_t split_blocks,
+                void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_shape(shape);
   if (rc) return rc;
   if (!q || !kv_pool || !block_table || !seq_lens || !meta_offsets || !out || !block_mass ||
@@ -319,6 +323,7 @@ int kvs_decode_step(const kvs_shape* shape, const void* q, const void* kv_pool, 
   d.split_blocks = L.split_blocks;
   d.n_splits = L.n_splits;
   d.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  d.kv_e4m3 = kv_e4m3 ? 1 : 0;
   d.ml = reinterpret_cast<float2*>(ws + L.ml);
   d.opart = reinterpret_cast<float*>(ws + L.opart);
   d.pi = reinterpret_cast<float*>(ws + L.pi);
@@ -372,6 +377,33 @@ int kvs_decode_step(const kvs_shape* shape, const void* q, const void* kv_pool, 
     if (e != hipSuccess) return hip_fail(e, "block_mass launch");
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvs_decode_step(const kvs_shape* shape, const void* q, const void* kv_pool, int64_t pool_blocks,
+                    const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                    const int32_t* meta_offsets, int32_t batch, int64_t total_blocks,
+                    int32_t layer_begin, int32_t layer_end, float scale, void* out,
+                    float* block_mass, int accumulate, int32_t split_blocks, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return decode_step(false, shape, q, kv_pool, pool_blocks, block_table, max_blocks_per_seq,
+                     seq_lens, meta_offsets, batch, total_blocks, layer_begin, layer_end, scale,
+                     out, block_mass, accumulate, split_blocks, workspace, workspace_bytes, stream);
+}
+
+int kvs_decode_step_e4m3(const kvs_shape* shape, const void* q, const void* kv_pool,
+                         int64_t pool_blocks, const int32_t* block_table,
+                         int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                         const int32_t* meta_offsets, int32_t batch, int64_t total_blocks,
+                         int32_t layer_begin, int32_t layer_end, float scale, void* out,
+                         float* block_mass, int accumulate, int32_t split_blocks, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return decode_step(true, shape, q, kv_pool, pool_blocks, block_table, max_blocks_per_seq,
+                     seq_lens, meta_offsets, batch, total_blocks, layer_begin, layer_end, scale,
+                     out, block_mass, accumulate, split_blocks, workspace, workspace_bytes, stream);
 }
 
 int kvs_meta_init(kvs_block_meta* meta, const int32_t* meta_offsets, const uint64_t* seq_ids,

@@ -14,7 +14,7 @@ constexpr size_t kMaxDecodeLds = 65536;  // dynamic LDS a decode work-group may 
 
 struct DecodeArgs {
   const uint16_t* q;        // fp16 bits [B][num_layers][64][128]
-  const uint8_t* pool;      // fp16 [P][num_layers][2][8][16][128]
+  const uint8_t* pool;      // [P][num_layers][2][8][16][128] fp16 values or E4M3 codes
   const int32_t* table;     // [B][max_nb]
   const int32_t* seq_lens;  // [B]
   const int32_t* meta_off;  // [B + 1]
@@ -27,6 +27,7 @@ struct DecodeArgs {
   int32_t split_blocks;
   int32_t n_splits;
   float scale_log2;         // softmax scale * log2(e)
+  int32_t kv_e4m3;          // 0: pool holds fp16 values; 1: FP8 E4M3 codes
   float2* ml;               // [B][n_layers][64][n_splits]: (running max, sum), base 2
   float* opart;             // [B][n_layers][64][n_splits][128]
   float* pi;                // [n_layers][64][total_blocks]

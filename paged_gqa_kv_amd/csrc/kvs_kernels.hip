@@ -25,6 +25,7 @@
 
 namespace kvs {
 
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
@@ -34,8 +35,8 @@ typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 constexpr int kHeadDim = 128;
 constexpr int kGroup = 8;                 // query heads per KV head
 constexpr int kQHeads = 64;
-constexpr int kTileBytes = 16 * kHeadDim * 2;          // one (layer, K|V, KV head) tile: 4 KiB
-constexpr int64_t kLayerBytes = 2 * 8 * kTileBytes;    // one block, one layer: 64 KiB
+constexpr int kTileBytes = 16 * kHeadDim * 2;          // fp16 (layer, K|V, KV head) tile: 4 KiB
+constexpr int kVStageBytes = kTileBytes;                // value tile staged as fp16 in LDS
 
 __device__ __forceinline__ float xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 
@@ -88,23 +89,84 @@ __device__ __forceinline__ int seq_blocks(const int32_t* seq_lens, const int32_t
 // gfx950 than non-temporal ones for this access pattern.
 __device__ __forceinline__ u4_t stream_load(const u4_t* p) { return *p; }
 
-struct BlockRegs {
-  u4_t k[4];
-  u4_t v[4];
+// Stored K/V element formats.  A (layer, K|V, KV head) tile is 16 rows of 128
+// elements; a block holds, per layer, 8 key tiles then 8 value tiles.
+struct KvF16 {
+  static constexpr int kElemBytes = 2;
+  static constexpr int kLoads = 4;   // 16-byte loads per lane per tile
+};
+struct KvE4M3 {                      // FP8 E4M3 codes, no scale
+  static constexpr int kElemBytes = 1;
+  static constexpr int kLoads = 2;
 };
 
-// Issues exactly eight 16-byte loads (four of the key tile in the QK operand
-// layout, four of the value tile in plain row order).  Always issuing the same
-// number of loads on every path lets the compiler wait for one ring slot
-// precisely instead of draining every load in flight.
-__device__ __forceinline__ void load_block(BlockRegs& r, const uint8_t* base, int lane, int c,
+template <class F>
+struct BlockRegs {
+  u4_t k[F::kLoads];
+  u4_t v[F::kLoads];
+};
+
+template <class F>
+constexpr int tile_bytes() { return 16 * kHeadDim * F::kElemBytes; }
+
+// Issues exactly 2 * F::kLoads 16-byte loads per lane: the key tile in the QK
+// operand layout (lane (j, c) takes elements [32 j, 32 j + 32) of row c) and
+// the value tile in plain order (load i covers bytes [1024 i, 1024 i + 1024)).
+// Always issuing the same number of loads on every path lets the compiler wait
+// for one ring slot precisely instead of draining every load in flight.
+template <class F>
+__device__ __forceinline__ void load_block(BlockRegs<F>& r, const uint8_t* base, int lane, int c,
                                            int j) {
-  const uint8_t* kp = base + c * 256 + j * 64;
-  const uint8_t* vp = base + 8 * kTileBytes + lane * 16;
+  const uint8_t* kp = base + c * (kHeadDim * F::kElemBytes) + j * (32 * F::kElemBytes);
+  const uint8_t* vp = base + 8 * tile_bytes<F>() + lane * 16;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r.k[i] = stream_load(reinterpret_cast<const u4_t*>(kp + i * 16));
+  for (int i = 0; i < F::kLoads; ++i)
+    r.k[i] = stream_load(reinterpret_cast<const u4_t*>(kp + i * 16));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r.v[i] = stream_load(reinterpret_cast<const u4_t*>(vp + i * 1024));
+  for (int i = 0; i < F::kLoads; ++i)
+    r.v[i] = stream_load(reinterpret_cast<const u4_t*>(vp + i * 1024));
+}
+
+// Four E4M3 codes to four fp16 values (exact: every finite E4M3 value is an
+// fp16 value), with gfx950's packed scaled conversion at scale 1.
+__device__ __forceinline__ u2_t e4m3x4_to_f16(uint32_t w) {
+  const h2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  const h2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+  return u2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
+// Value tile of one ring slot to LDS as row-major fp16 [16][128].
+template <class F>
+__device__ __forceinline__ void stage_values(const BlockRegs<F>& r, u4_t* vstage, int lane) {
+  if constexpr (F::kElemBytes == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vstage[i * 64 + lane] = r.v[i];
+  } else {
+    // load i, lane l: row 8 i + l / 8, elements [16 (l % 8), 16 (l % 8) + 16)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const u2_t a = e4m3x4_to_f16(r.v[i][0]);
+      const u2_t b = e4m3x4_to_f16(r.v[i][1]);
+      const u2_t c2 = e4m3x4_to_f16(r.v[i][2]);
+      const u2_t d = e4m3x4_to_f16(r.v[i][3]);
+      const int base = (8 * i + (lane >> 3)) * 16 + 2 * (lane & 7);
+      vstage[base] = u4_t{a[0], a[1], b[0], b[1]};
+      vstage[base + 1] = u4_t{c2[0], c2[1], d[0], d[1]};
+    }
+  }
+}
+
+// QK operand i of one ring slot: 8 fp16 key elements [32 j + 8 i, 32 j + 8 i + 8).
+template <class F>
+__device__ __forceinline__ h8_t key_operand(const BlockRegs<F>& r, int i) {
+  if constexpr (F::kElemBytes == 2) {
+    return __builtin_bit_cast(h8_t, r.k[i]);
+  } else {
+    const u4_t w = r.k[i >> 1];
+    const u2_t a = e4m3x4_to_f16(w[(i & 1) * 2]);
+    const u2_t b = e4m3x4_to_f16(w[(i & 1) * 2 + 1]);
+    return __builtin_bit_cast(h8_t, u4_t{a[0], a[1], b[0], b[1]});
+  }
 }
 
 // Blocks whose loads are in flight per wave: the ring slot being processed
@@ -116,12 +178,13 @@ constexpr int kWavesPerSimd = 3;
 // reading neighbouring heads of the same blocks measured no faster than 1.
 constexpr int kWpw = 1;
 
+template <class F>
 __global__ void __launch_bounds__(64 * kWpw, kWavesPerSimd) paged_decode_gqa(DecodeArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int SB = a.split_blocks;
   const int wave = threadIdx.x >> 6;
   int32_t* tbl = reinterpret_cast<int32_t*>(smem);                          // [SB] block ids
-  uint8_t* wave_lds = smem + (size_t)4 * SB + (size_t)wave * (32 * SB + kTileBytes);
+  uint8_t* wave_lds = smem + (size_t)4 * SB + (size_t)wave * (32 * SB + kVStageBytes);
   float* pi_lds = reinterpret_cast<float*>(wave_lds);                       // [8][SB]
   u4_t* vstage = reinterpret_cast<u4_t*>(wave_lds + 32 * SB);               // 16 x 16 chunks of 16 B
 
@@ -166,8 +229,9 @@ __global__ void __launch_bounds__(64 * kWpw, kWavesPerSimd) paged_decode_gqa(Dec
     for (int i = 0; i < 4; ++i) qb[i] = h8_t{0, 0, 0, 0, 0, 0, 0, 0};
   }
 
+  constexpr int64_t kLayerBytes = 16 * (int64_t)tile_bytes<F>();   // one block, one layer
   const size_t block_stride = (size_t)a.num_layers * kLayerBytes;
-  const size_t tile_off = (size_t)layer * kLayerBytes + (size_t)g * kTileBytes;
+  const size_t tile_off = (size_t)layer * kLayerBytes + (size_t)g * tile_bytes<F>();
   float m_run = -INFINITY;
   float l_run = 0.f;
   f4_t acc[8];
@@ -185,7 +249,7 @@ __global__ void __launch_bounds__(64 * kWpw, kWavesPerSimd) paged_decode_gqa(Dec
     return a.pool + (size_t)(in_pool ? pid : 0) * block_stride + tile_off;
   };
 
-  BlockRegs ring[kRing];
+  BlockRegs<F> ring[kRing];
   bool ring_ok[kRing];
 #pragma unroll
   for (int k = 0; k < kRing; ++k)
@@ -202,15 +266,14 @@ __global__ void __launch_bounds__(64 * kWpw, kWavesPerSimd) paged_decode_gqa(Dec
       const int valid = cur_ok ? min(16, n - 16 * b) : 0;
 
       // ---- value tile to LDS (the slot's value registers are free after this)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vstage[i * 64 + lane] = ring[k].v[i];
+      stage_values<F>(ring[k], vstage, lane);
 
       // ---- logits of 16 tokens x 16 (8 real) heads
       f4_t sacc = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, ring[k].k[i]),
-                                                      qb[i], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_operand<F>(ring[k], i), qb[i], sacc,
+                                                      0, 0, 0);
 
       // ---- refill this slot with the block kRing ahead
       load_block(ring[k], slot_block(b + kRing, &ring_ok[k]), lane, c, j);
@@ -662,9 +725,15 @@ __global__ void __launch_bounds__(256) stream_copy(const u4_t* __restrict__ src,
 // ---------------------------------------------------------------------------
 hipError_t launch_decode(const DecodeArgs& a, int batch, hipStream_t stream) {
   const uint64_t wgs = (uint64_t)batch * a.n_splits * a.n_layers * (8 / kWpw);
-  const size_t lds = (size_t)4 * a.split_blocks + (size_t)kWpw * (32 * a.split_blocks + kTileBytes);
+  const size_t lds =
+      (size_t)4 * a.split_blocks + (size_t)kWpw * (32 * a.split_blocks + kVStageBytes);
   if (lds > kMaxDecodeLds) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(paged_decode_gqa, dim3((uint32_t)wgs), dim3(64 * kWpw), lds, stream, a);
+  if (a.kv_e4m3)
+    hipLaunchKernelGGL(paged_decode_gqa<KvE4M3>, dim3((uint32_t)wgs), dim3(64 * kWpw), lds,
+                       stream, a);
+  else
+    hipLaunchKernelGGL(paged_decode_gqa<KvF16>, dim3((uint32_t)wgs), dim3(64 * kWpw), lds,
+                       stream, a);
   return hipGetLastError();
 }
 

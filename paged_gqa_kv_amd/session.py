@@ -39,9 +39,14 @@ class DecodeSession:
         self.reset_meta()
 
     @property
+    def kv_elem_bytes(self) -> int:
+        return 1 if self.m.workload.kv_format == "e4m3" else 2
+
+    @property
     def kv_bytes_per_step(self) -> int:
         """Logical KV bytes one decode step reads (keys and values, every token)."""
-        return sum(self.m.lens) * (self.layer_end - self.layer_begin) * 8 * 128 * 2 * 2
+        return (sum(self.m.lens) * (self.layer_end - self.layer_begin) * 8 * 128 * 2
+                * self.kv_elem_bytes)
 
     def reset_meta(self):
         m = self.m
@@ -52,10 +57,11 @@ class DecodeSession:
         m = self.m
         lb = self.layer_begin if layer_begin is None else layer_begin
         le = self.layer_end if layer_end is None else layer_end
-        api.decode_step(self.shape, q, m.pool, m.pool_blocks, m.block_table, m.max_blocks,
-                        m.seq_lens, m.meta_offsets, m.batch, m.total_blocks, lb, le,
-                        api.DEFAULT_SCALE if scale is None else scale, self.out, self.mass,
-                        accumulate, self.split_blocks, self.ws, stream=self.stream)
+        fn = api.decode_step_e4m3 if m.workload.kv_format == "e4m3" else api.decode_step
+        fn(self.shape, q, m.pool, m.pool_blocks, m.block_table, m.max_blocks, m.seq_lens,
+           m.meta_offsets, m.batch, m.total_blocks, lb, le,
+           api.DEFAULT_SCALE if scale is None else scale, self.out, self.mass, accumulate,
+           self.split_blocks, self.ws, stream=self.stream)
 
     def score(self, step: int, pol, classify: int = 1):
         m = self.m

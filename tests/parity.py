@@ -29,12 +29,14 @@ SCALE = 1.0 / math.sqrt(128.0)
 
 def host(m):
     """Host copies of a materialised workload, for the oracle."""
-    return dict(pool=m.pool.cpu().numpy(), table=m.table_host, lens=list(m.lens))
+    return dict(pool=m.pool.cpu().numpy(), table=m.table_host, lens=list(m.lens),
+                kv_format=m.workload.kv_format)
 
 
 def oracle_decode(h, q, layer_begin=0, layer_end=None):
     qn = q.cpu().numpy() if isinstance(q, torch.Tensor) else q
-    return OA.decode_step(qn, h["pool"], h["table"], h["lens"], SCALE, layer_begin, layer_end)
+    return OA.decode_step(qn, h["pool"], h["table"], h["lens"], SCALE, layer_begin, layer_end,
+                          kv_format=h.get("kv_format", "fp16"))
 
 
 def check_out(gpu_out, ref_out, layers, seqs=None):

@@ -19,7 +19,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return set(re.findall(r"\b(kvs_[a-z_]+)\s*\(", src))
+    return set(re.findall(r"\b(kvs_[a-z0-9_]+)\s*\(", src))
 
 
 def test_every_declared_function_is_exported():

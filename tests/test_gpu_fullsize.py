@@ -36,9 +36,12 @@ def _host_layer(m, s, layer):
     return m.pool[pids, layer].cpu().numpy()[:, None]          # [nb][1][2][8][16][128]
 
 
-def _run(name, alpha, steps=2, rows=8, oracle_layers=1, seqs_for_layer_mass=None):
-    print(f"\n[case] full size {name}, alpha {alpha}, {steps} steps", flush=True)
+def _run(name, alpha, steps=2, rows=8, oracle_layers=1, seqs_for_layer_mass=None,
+         kv_format="fp16"):
+    print(f"\n[case] full size {name} ({kv_format} KV), alpha {alpha}, {steps} steps", flush=True)
     wl = W.WORKLOADS[name]
+    if kv_format == "e4m3":
+        wl = W.as_e4m3(wl)
     m = W.materialise(wl, DEV)
     torch.cuda.synchronize()
     L = m.num_layers
@@ -77,7 +80,8 @@ def _run(name, alpha, steps=2, rows=8, oracle_layers=1, seqs_for_layer_mass=None
         layer = int(rng.integers(L))
         h = int(rng.integers(64))
         host = _host_layer(m, s, layer)
-        K, V = OA.gather_layer(host, np.arange(m.blocks[s]), m.lens[s], 0, kv_head=h // 8)
+        K, V = OA.gather_layer(host, np.arange(m.blocks[s]), m.lens[s], 0, kv_head=h // 8,
+                               kv_format=kv_format)
         ref, _ = OA.attend_head(qh[s, layer, h], K, V, scale)
         e = np.abs(out[s, layer, h] - ref).max()
         lim = np.abs(ref).max()
@@ -100,7 +104,8 @@ def _run(name, alpha, steps=2, rows=8, oracle_layers=1, seqs_for_layer_mass=None
     for layer, gm in one_layer.items():
         for s in seqs:
             host = _host_layer(m, s, layer)
-            _, ref = OA.decode_layer(qh[s, layer], host, np.arange(m.blocks[s]), m.lens[s], 0, scale)
+            _, ref = OA.decode_layer(qh[s, layer], host, np.arange(m.blocks[s]), m.lens[s], 0,
+                                     scale, kv_format)
             got = gm[offsets[s]:offsets[s + 1]]
             assert np.all(np.abs(got - ref) <= P.MASS_RTOL * ref + 1e-7 * ref.max()), (layer, s)
         print(f"  layer {layer}: single-layer block mass matches the oracle", flush=True)
@@ -123,3 +128,11 @@ def test_fullsize_shared_prefix_batch():
 
 def test_fullsize_1m_context():
     _run("decode-32L-1M", 0.01, steps=2, rows=6, oracle_layers=1)
+
+
+def test_fullsize_128k_context_e4m3():
+    _run("decode-80L-128K", 0.05, steps=2, rows=8, oracle_layers=1, kv_format="e4m3")
+
+
+def test_fullsize_1m_context_e4m3():
+    _run("decode-32L-1M", 0.15, steps=2, rows=4, oracle_layers=1, kv_format="e4m3")

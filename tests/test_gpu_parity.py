@@ -43,7 +43,7 @@ def _run_pipeline(m, alpha, steps, split_blocks=0, check_decode_steps=None, seqs
         sub = sorted(set(score_seqs) | (set(range(m.batch)) if need_decode else set()))
         # oracle decode of the sequences this step needs
         qh = q.cpu().numpy()
-        h_sub = dict(pool=h["pool"], table=h["table"][sub], lens=[h["lens"][s] for s in sub])
+        h_sub = dict(h, table=h["table"][sub], lens=[h["lens"][s] for s in sub])
         out_ref, mass_ref = P.oracle_decode(h_sub, qh[sub])
         if need_decode:
             worst["out"] = max(worst["out"], P.check_out(sess.out[sub], out_ref,
@@ -231,8 +231,8 @@ def test_device_status_bits():
     assert s.status() & api._abi.KVS_DEV_BAD_BLOCK_ID
     # sequence 0 is untouched by the bad entry of sequence 1
     h = P.host(m)
-    out_ref, mass_ref = P.oracle_decode(dict(pool=h["pool"], table=h["table"][:1],
-                                             lens=h["lens"][:1]), q[:1])
+    out_ref, mass_ref = P.oracle_decode(dict(h, table=h["table"][:1], lens=h["lens"][:1]),
+                                        q[:1])
     P.check_out(s.out[:1], out_ref, [0])
     assert torch.isfinite(s.out).all()
 
