@@ -37,6 +37,8 @@ def _parse():
     ap.add_argument("--steps", type=int, default=16)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="decode-80L-128K")
+    ap.add_argument("--kv-format", choices=("fp16", "e4m3"), default="fp16",
+                    help="stored K/V format (e4m3: FP8 codes, half the bytes)")
     ap.add_argument("--alpha", type=float, default=None)
     ap.add_argument("--split-blocks", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
@@ -146,9 +148,10 @@ def _cpu_baseline(m, alpha, budget_s):
         copy_s += time.perf_counter() - tc
         for s in range(m.batch):
             tbl = np.arange(m.blocks[s])
-            _, ms = OA.decode_layer(q[s, layer], pool_l[s], tbl, m.lens[s], 0, scale)
+            _, ms = OA.decode_layer(q[s, layer], pool_l[s], tbl, m.lens[s], 0, scale,
+                                    m.workload.kv_format)
             masses[s] += ms
-            kv_bytes += m.lens[s] * 8 * 128 * 2 * 2
+            kv_bytes += m.lens[s] * 8 * 128 * 2 * (1 if m.workload.kv_format == "e4m3" else 2)
         layers_done += 1
         if time.perf_counter() - t0 - copy_s >= budget_s:
             break
@@ -190,6 +193,8 @@ def main():
         print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
         sys.exit(1)
     wl = W.WORKLOADS[args.workload]
+    if args.kv_format == "e4m3":
+        wl = W.as_e4m3(wl)
     alpha = args.alpha if args.alpha is not None else wl.alphas[0]
     print(f"[bench] materialising {wl.name} on cuda:0", file=sys.stderr, flush=True)
     t0 = time.time()
@@ -264,7 +269,7 @@ def main():
         raise RuntimeError("a sequence got no eviction candidate")
 
     kv_bytes = sess.kv_bytes_per_step
-    unique_bytes = m.unique_blocks * 16 * m.num_layers * 8 * 128 * 2 * 2
+    unique_bytes = m.unique_blocks * 16 * m.num_layers * 8 * 128 * 2 * sess.kv_elem_bytes
     t_step = total_ms / 1e3 / args.steps
     value = kv_bytes / t_step / 1e9
     dec_avg = sum(decode_ms) / len(decode_ms) / 1e3
@@ -295,12 +300,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp16",
+        "dtype": "fp16" if args.kv_format == "fp16" else "e4m3 KV, fp16 compute",
         "data": "synthetic",
         "config": {
             "workload": wl.name,
             "layers": m.num_layers,
             "batch": m.batch,
+            "kv_format": args.kv_format,
             "context_tokens": int(sum(m.lens)),
             "records": m.total_blocks,
             "alpha": alpha,
@@ -310,6 +316,7 @@ def main():
             "parallelism": "single GPU",
         },
         "blocks_scored_per_s": round(m.total_blocks / t_step, 1),
+        "tokens_attended_per_s": round(sum(m.lens) * m.num_layers / t_step, 1),
         "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
         "decode_kernel_ms": round(dec_avg * 1e3, 4),
         "decode_share_of_step": round(dec_avg / t_step, 4),
