@@ -205,3 +205,29 @@ def eviction_candidates(state: ScoreState, t: int, alpha: float, active=None,
             blocks[s] = int(state.block[best])
             scores[s] = s_now[best]
     return blocks, scores
+
+
+def grow(state: ScoreState, blocks_per_seq, anchor_blocks: int = 1) -> ScoreState:
+    """Records after sequences grew to blocks_per_seq blocks: existing records
+    are kept (their sequence's block count, and so their recency, follows the
+    new length); each new block gets a fresh record (score 0, never touched,
+    unclassified), as a newly allocated block has no history."""
+    old_nb = np.zeros(len(blocks_per_seq), dtype=np.int64)
+    for s in range(len(blocks_per_seq)):
+        old_nb[s] = int((state.seq_index == s).sum())
+    seq_ids = np.zeros(len(blocks_per_seq), dtype=np.uint64)
+    for s in range(len(blocks_per_seq)):
+        rows = np.nonzero(state.seq_index == s)[0]
+        if rows.size:
+            seq_ids[s] = state.seq_id[rows[0]]
+    fresh = init_state(blocks_per_seq, seq_ids, anchor_blocks)
+    out = fresh.copy()
+    for s in range(len(blocks_per_seq)):
+        if blocks_per_seq[s] < old_nb[s]:
+            raise ValueError("sequences only grow")
+        src = np.nonzero(state.seq_index == s)[0]
+        dst = np.nonzero(fresh.seq_index == s)[0][: src.size]
+        for f in ("seq_id", "block", "score", "t_touch", "touch_count", "priority", "tier",
+                  "anchor"):
+            getattr(out, f)[dst] = getattr(state, f)[src]
+    return out

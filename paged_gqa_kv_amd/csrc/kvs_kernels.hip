@@ -94,10 +94,12 @@ __device__ __forceinline__ u4_t stream_load(const u4_t* p) { return *p; }
 struct KvF16 {
   static constexpr int kElemBytes = 2;
   static constexpr int kLoads = 4;   // 16-byte loads per lane per tile
+  static constexpr int kRing = 2;    // ring slots (32 VGPRs each)
 };
 struct KvE4M3 {                      // FP8 E4M3 codes, no scale
   static constexpr int kElemBytes = 1;
   static constexpr int kLoads = 2;
+  static constexpr int kRing = 2;    // 16 VGPRs each; 3 and 4 measured slower
 };
 
 template <class F>
@@ -172,7 +174,6 @@ __device__ __forceinline__ h8_t key_operand(const BlockRegs<F>& r, int i) {
 // Blocks whose loads are in flight per wave: the ring slot being processed
 // plus kRing - 1 ahead (32 VGPRs per slot).  Deeper rings at lower occupancy
 // measured no faster on gfx950.
-constexpr int kRing = 2;
 constexpr int kWavesPerSimd = 3;
 // Waves per work-group (each takes one KV head).  Work-groups of 4 or 8 waves
 // reading neighbouring heads of the same blocks measured no faster than 1.
@@ -249,6 +250,7 @@ __global__ void __launch_bounds__(64 * kWpw, kWavesPerSimd) paged_decode_gqa(Dec
     return a.pool + (size_t)(in_pool ? pid : 0) * block_stride + tile_off;
   };
 
+  constexpr int kRing = F::kRing;
   BlockRegs<F> ring[kRing];
   bool ring_ok[kRing];
 #pragma unroll
