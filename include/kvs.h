@@ -71,6 +71,8 @@ typedef enum {
 #define KVS_DEV_BAD_SEQ_LEN    0x2u  /* seq_len < 0 or > 16 * max_blocks_per_seq: sequence skipped */
 #define KVS_DEV_BAD_OFFSETS    0x4u  /* meta_offsets inconsistent with seq_lens / total_blocks */
 #define KVS_DEV_STALE_STEP     0x8u  /* step <= a record's touch timestamp: record left unchanged */
+#define KVS_DEV_POOL_EXHAUSTED 0x10u /* kvs_append_kv: no free block, table row full or no record
+                                        capacity for a sequence that needed a block: not appended */
 
 /* Model head shape.  The kernels support num_q_heads 64, num_kv_heads 8,
  * head_dim 128, block_tokens 16 and any num_layers >= 1 (Visual Reference
@@ -194,8 +196,11 @@ int kvs_device_status(void* workspace, void* stream, uint32_t* bits);
  *                of each logical block.  Entries past a sequence's end are not read.
  *  seq_lens      int32 [batch], device: tokens per sequence (0 allowed).
  *  meta_offsets  int32 [batch + 1], device: record index of (s, b) is
- *                meta_offsets[s] + b; meta_offsets[s+1] - meta_offsets[s] must be
- *                ceil(seq_lens[s] / 16) and meta_offsets[batch] <= total_blocks.
+ *                meta_offsets[s] + b.  meta_offsets[s+1] - meta_offsets[s] is the
+ *                sequence's record capacity: it must be >= ceil(seq_lens[s] / 16)
+ *                and <= max_blocks_per_seq, and meta_offsets[batch] <= total_blocks.
+ *                (Equal to ceil(seq_lens[s] / 16) for a cache that does not grow;
+ *                larger when kvs_append_kv will grow the sequence.)
  *  total_blocks  host copy of the number of records.
  *  scale         softmax scale (1/sqrt(128) for the pages' model).
  *  out           fp16 [batch][num_layers][64][128], device: rows of layers in
@@ -251,6 +256,11 @@ int kvs_meta_init(kvs_block_meta* meta, const int32_t* meta_offsets,
                   int32_t max_blocks_per_seq, int64_t total_blocks,
                   int32_t anchor_blocks, void* stream);
 
+/* seq_lens (int32 [batch], device) in kvs_score_update, kvs_classify and
+ * kvs_evict_candidates: when non-NULL, only the first ceil(seq_lens[s] / 16)
+ * records of each sequence's capacity are live (and nb below is that count);
+ * when NULL, every record of the capacity is live. */
+
 /* One scoring step over every record of every sequence in the batch:
  * m_hat = block_mass / max over the sequence's blocks (0 if that max is 0),
  * E <- alpha m_hat + (1 - alpha) E_prev in fp64, where E_prev is the stored
@@ -261,7 +271,7 @@ int kvs_meta_init(kvs_block_meta* meta, const int32_t* meta_offsets,
  * t_touch is not KVS_NEVER_TOUCHED and >= step is left unchanged
  * (KVS_DEV_STALE_STEP).  workspace: kvs_score_workspace_bytes() bytes. */
 int kvs_score_update(kvs_block_meta* meta, const float* block_mass,
-                     const int32_t* meta_offsets, int32_t batch,
+                     const int32_t* meta_offsets, const int32_t* seq_lens, int32_t batch,
                      int32_t max_blocks_per_seq, int64_t total_blocks,
                      uint64_t step, const kvs_policy* policy, int classify,
                      void* workspace, size_t workspace_bytes, void* stream);
@@ -271,8 +281,8 @@ int kvs_score_update(kvs_block_meta* meta, const float* block_mass,
  * tier = 0 if P >= t_high, 1 if P >= t_low, else 2, where b is the record's
  * logical block and nb its sequence's record count.  Writes priority and tier
  * into the records and, when tiers_out != NULL, tier into tiers_out[record]. */
-int kvs_classify(kvs_block_meta* meta, const int32_t* meta_offsets, int32_t batch,
-                 int32_t max_blocks_per_seq, int64_t total_blocks,
+int kvs_classify(kvs_block_meta* meta, const int32_t* meta_offsets, const int32_t* seq_lens,
+                 int32_t batch, int32_t max_blocks_per_seq, int64_t total_blocks,
                  const kvs_policy* policy, uint8_t* tiers_out, void* stream);
 
 /* Workspace bytes kvs_evict_candidates needs (status header + per-chunk partials). */
@@ -294,10 +304,45 @@ size_t kvs_evict_workspace_bytes(int32_t batch, int32_t max_blocks_per_seq);
  * workspace: kvs_evict_workspace_bytes() bytes, 256-B aligned, header zeroed
  * once by kvs_workspace_init(). */
 int kvs_evict_candidates(const kvs_block_meta* meta, const int32_t* meta_offsets,
-                         const uint8_t* active, int32_t batch, int32_t max_blocks_per_seq,
+                         const int32_t* seq_lens, const uint8_t* active, int32_t batch,
+                         int32_t max_blocks_per_seq,
                          int64_t total_blocks, uint64_t now, double alpha, int exclude_pinned,
                          int32_t* out_block, double* out_key, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* Workspace bytes kvs_append_kv needs (status header + two words per sequence). */
+size_t kvs_append_workspace_bytes(int32_t batch);
+
+/* Append one token per sequence to the paged cache (the write that precedes
+ * each decode step: generation adds one key and one value per layer per KV head,
+ * Fitting a Million Tokens, Sec. 01; fixed-size blocks from a block manager's
+ * pool, KV cache offload post, "Top row").  For every sequence s in batch order:
+ * the token goes to position t = seq_lens[s], logical block t / 16, slot t % 16.
+ * When t % 16 == 0 a block is taken from the top of the free stack -- the k-th
+ * sequence (in batch order) that needs one takes free_stack[*free_top - 1 - k] --
+ * block_table[s][t / 16] is set and the block's record at meta_offsets[s] + t / 16
+ * is created fresh (as kvs_meta_init).  K and V of the token are written to the
+ * slot for every layer and KV head; nothing else in the pool changes.  Then
+ * seq_lens[s] += 1 and finally *free_top decreases by the blocks taken.
+ *  kv_elem_bytes  2: the pool holds fp16 values, 1: E4M3 codes.  k_new and v_new
+ *                 are [batch][num_layers][8][128] elements of that format (no
+ *                 rounding happens here), device, 16-byte aligned.
+ *  free_stack     int32 [free_capacity], device; entries [0, *free_top) are free.
+ *  free_top       int32, device, in / out; a value outside [0, free_capacity] is
+ *                 clamped into it (KVS_DEV_BAD_OFFSETS).
+ *  seq_lens       int32 [batch], device, in / out.
+ * A sequence that needs a block when none is left, whose table row or record
+ * capacity is full, is left unchanged (KVS_DEV_POOL_EXHAUSTED).
+ * workspace: kvs_append_workspace_bytes() bytes. */
+int kvs_append_kv(const kvs_shape* shape, int kv_elem_bytes,
+                  const void* k_new, const void* v_new,
+                  void* kv_pool, int64_t pool_blocks,
+                  int32_t* block_table, int32_t max_blocks_per_seq,
+                  int32_t* seq_lens,
+                  const int32_t* free_stack, int32_t free_capacity, int32_t* free_top,
+                  kvs_block_meta* meta, const int32_t* meta_offsets, const uint64_t* seq_ids,
+                  int32_t anchor_blocks, int32_t batch, int64_t total_blocks,
+                  void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -22,6 +22,7 @@ KVS_DEV_BAD_BLOCK_ID = 0x1
 KVS_DEV_BAD_SEQ_LEN = 0x2
 KVS_DEV_BAD_OFFSETS = 0x4
 KVS_DEV_STALE_STEP = 0x8
+KVS_DEV_POOL_EXHAUSTED = 0x10
 
 KVS_NEVER_TOUCHED = 0xFFFF_FFFF_FFFF_FFFF
 KVS_UNCLASSIFIED = 0xFF
@@ -34,7 +35,7 @@ EXPORTS = (
     "kvs_last_error", "kvs_workspace_init", "kvs_device_status", "kvs_decode_step",
     "kvs_meta_init", "kvs_score_update", "kvs_classify", "kvs_set_decode_events",
     "kvs_stream_probe", "kvs_evict_workspace_bytes", "kvs_evict_candidates",
-    "kvs_decode_step_e4m3",
+    "kvs_decode_step_e4m3", "kvs_append_workspace_bytes", "kvs_append_kv",
 )
 
 
@@ -82,13 +83,18 @@ _SIGS = {
         ctypes.POINTER(Shape), _vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _i64, _i32, _i32,
         ctypes.c_float, _vp, _vp, ctypes.c_int, _i32, _vp, _sz, _vp]),
     "kvs_meta_init": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i64, _i32, _vp]),
-    "kvs_score_update": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i64, ctypes.c_uint64,
+    "kvs_score_update": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i64, ctypes.c_uint64,
                                         ctypes.POINTER(Policy), ctypes.c_int, _vp, _sz, _vp]),
-    "kvs_classify": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i64, ctypes.POINTER(Policy), _vp, _vp]),
+    "kvs_classify": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i64, ctypes.POINTER(Policy),
+                                    _vp, _vp]),
     "kvs_set_decode_events": (ctypes.c_int, [_vp, _vp]),
     "kvs_stream_probe": (ctypes.c_int, [_vp, _vp, _sz, ctypes.c_int, _i32, _vp]),
+    "kvs_append_workspace_bytes": (_sz, [_i32]),
+    "kvs_append_kv": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.c_int, _vp, _vp, _vp, _i64,
+                                     _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32,
+                                     _i64, _vp, _sz, _vp]),
     "kvs_evict_workspace_bytes": (_sz, [_i32, _i32]),
-    "kvs_evict_candidates": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i64, ctypes.c_uint64,
+    "kvs_evict_candidates": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i64, ctypes.c_uint64,
                                             ctypes.c_double, ctypes.c_int, _vp, _vp, _vp, _sz,
                                             _vp]),
 }

@@ -141,30 +141,47 @@ def meta_init(meta, meta_offsets, seq_ids, batch: int, max_blocks: int, total_bl
                               total_blocks, anchor_blocks, _s(stream)))
 
 
-def score_update(meta, block_mass, meta_offsets, batch: int, max_blocks: int,
+def score_update(meta, block_mass, meta_offsets, seq_lens, batch: int, max_blocks: int,
                  total_blocks: int, step: int, pol: Policy, classify: int, workspace,
                  workspace_bytes=None, stream=None) -> None:
     ws_bytes = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
-    check(lib().kvs_score_update(_p(meta), _p(block_mass), _p(meta_offsets), batch, max_blocks,
-                                 total_blocks, step, ctypes.byref(pol), classify, _p(workspace),
-                                 ws_bytes, _s(stream)))
+    check(lib().kvs_score_update(_p(meta), _p(block_mass), _p(meta_offsets), _p(seq_lens), batch,
+                                 max_blocks, total_blocks, step, ctypes.byref(pol), classify,
+                                 _p(workspace), ws_bytes, _s(stream)))
 
 
-def classify(meta, meta_offsets, batch: int, max_blocks: int, total_blocks: int, pol: Policy,
-             tiers_out=None, stream=None) -> None:
-    check(lib().kvs_classify(_p(meta), _p(meta_offsets), batch, max_blocks, total_blocks,
-                             ctypes.byref(pol), _p(tiers_out), _s(stream)))
+def classify(meta, meta_offsets, seq_lens, batch: int, max_blocks: int, total_blocks: int,
+             pol: Policy, tiers_out=None, stream=None) -> None:
+    check(lib().kvs_classify(_p(meta), _p(meta_offsets), _p(seq_lens), batch, max_blocks,
+                             total_blocks, ctypes.byref(pol), _p(tiers_out), _s(stream)))
+
+
+def append_workspace_bytes(batch: int) -> int:
+    return lib().kvs_append_workspace_bytes(batch)
+
+
+def append_kv(shp: Shape, kv_elem_bytes: int, k_new, v_new, kv_pool, pool_blocks: int,
+              block_table, max_blocks: int, seq_lens, free_stack, free_capacity: int, free_top,
+              meta, meta_offsets, seq_ids, anchor_blocks: int, batch: int, total_blocks: int,
+              workspace, workspace_bytes=None, stream=None) -> None:
+    ws_bytes = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    check(lib().kvs_append_kv(ctypes.byref(shp), kv_elem_bytes, _p(k_new), _p(v_new),
+                              _p(kv_pool), pool_blocks, _p(block_table), max_blocks,
+                              _p(seq_lens), _p(free_stack), free_capacity, _p(free_top), _p(meta),
+                              _p(meta_offsets), _p(seq_ids), anchor_blocks, batch, total_blocks,
+                              _p(workspace), ws_bytes, _s(stream)))
 
 
 def evict_workspace_bytes(batch: int, max_blocks: int) -> int:
     return lib().kvs_evict_workspace_bytes(batch, max_blocks)
 
 
-def evict_candidates(meta, meta_offsets, active, batch: int, max_blocks: int, total_blocks: int,
-                     now: int, alpha: float, exclude_pinned: int, out_block, out_key, workspace,
-                     workspace_bytes=None, stream=None) -> None:
+def evict_candidates(meta, meta_offsets, seq_lens, active, batch: int, max_blocks: int,
+                     total_blocks: int, now: int, alpha: float, exclude_pinned: int, out_block,
+                     out_key, workspace, workspace_bytes=None, stream=None) -> None:
     ws_bytes = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
-    check(lib().kvs_evict_candidates(_p(meta), _p(meta_offsets), _p(active), batch, max_blocks,
+    check(lib().kvs_evict_candidates(_p(meta), _p(meta_offsets), _p(seq_lens), _p(active),
+                                     batch, max_blocks,
                                      total_blocks, now, alpha, exclude_pinned, _p(out_block),
                                      _p(out_key), _p(workspace), ws_bytes, _s(stream)))
 

@@ -418,6 +418,7 @@ int kvs_meta_init(kvs_block_meta* meta, const int32_t* meta_offsets, const uint6
   kvs::MetaInitArgs a{};
   a.meta = meta;
   a.meta_off = meta_offsets;
+  a.seq_lens = nullptr;
   a.seq_ids = seq_ids;
   a.total_blocks = total_blocks;
   a.max_nb = max_blocks_per_seq;
@@ -430,9 +431,9 @@ int kvs_meta_init(kvs_block_meta* meta, const int32_t* meta_offsets, const uint6
 }
 
 int kvs_score_update(kvs_block_meta* meta, const float* block_mass, const int32_t* meta_offsets,
-                     int32_t batch, int32_t max_blocks_per_seq, int64_t total_blocks, uint64_t step,
-                     const kvs_policy* policy, int classify, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+                     const int32_t* seq_lens, int32_t batch, int32_t max_blocks_per_seq,
+                     int64_t total_blocks, uint64_t step, const kvs_policy* policy, int classify,
+                     void* workspace, size_t workspace_bytes, void* stream) {
   if (!meta || !block_mass || !meta_offsets || !workspace)
     return fail(KVS_E_NULL, "a required pointer is NULL");
   int rc = check_policy(policy);
@@ -452,6 +453,7 @@ int kvs_score_update(kvs_block_meta* meta, const float* block_mass, const int32_
   a.meta = meta;
   a.mass = block_mass;
   a.meta_off = meta_offsets;
+  a.seq_lens = seq_lens;
   a.chunk_max = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kHeader);
   a.tiers_out = nullptr;
   a.total_blocks = total_blocks;
@@ -475,7 +477,8 @@ size_t kvs_evict_workspace_bytes(int32_t batch, int32_t max_blocks_per_seq) {
 }
 
 int kvs_evict_candidates(const kvs_block_meta* meta, const int32_t* meta_offsets,
-                         const uint8_t* active, int32_t batch, int32_t max_blocks_per_seq,
+                         const int32_t* seq_lens, const uint8_t* active, int32_t batch,
+                         int32_t max_blocks_per_seq,
                          int64_t total_blocks, uint64_t now, double alpha, int exclude_pinned,
                          int32_t* out_block, double* out_key, void* workspace,
                          size_t workspace_bytes, void* stream) {
@@ -501,6 +504,7 @@ int kvs_evict_candidates(const kvs_block_meta* meta, const int32_t* meta_offsets
   kvs::EvictArgs a{};
   a.meta = meta;
   a.meta_off = meta_offsets;
+  a.seq_lens = seq_lens;
   a.active = active;
   a.part_key = reinterpret_cast<double*>(ws + kHeader);
   a.part_idx = reinterpret_cast<int32_t*>(ws + align_up(kHeader + (size_t)batch * chunks * 8u));
@@ -518,9 +522,68 @@ int kvs_evict_candidates(const kvs_block_meta* meta, const int32_t* meta_offsets
   return ok();
 }
 
-int kvs_classify(kvs_block_meta* meta, const int32_t* meta_offsets, int32_t batch,
-                 int32_t max_blocks_per_seq, int64_t total_blocks, const kvs_policy* policy,
-                 uint8_t* tiers_out, void* stream) {
+size_t kvs_append_workspace_bytes(int32_t batch) {
+  if (batch < 1 || batch > kMaxBatch) return 0;
+  return align_up(kHeader + (uint64_t)batch * 8u);
+}
+
+int kvs_append_kv(const kvs_shape* shape, int kv_elem_bytes, const void* k_new, const void* v_new,
+                  void* kv_pool, int64_t pool_blocks, int32_t* block_table,
+                  int32_t max_blocks_per_seq, int32_t* seq_lens, const int32_t* free_stack,
+                  int32_t free_capacity, int32_t* free_top, kvs_block_meta* meta,
+                  const int32_t* meta_offsets,
+                  const uint64_t* seq_ids, int32_t anchor_blocks, int32_t batch,
+                  int64_t total_blocks, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!k_new || !v_new || !kv_pool || !block_table || !seq_lens || !free_stack || !free_top ||
+      !meta || !meta_offsets || !seq_ids || !workspace)
+    return fail(KVS_E_NULL, "a required pointer is NULL");
+  if (kv_elem_bytes != 1 && kv_elem_bytes != 2)
+    return fail(KVS_E_RANGE, "kv_elem_bytes must be 1 (E4M3) or 2 (fp16)");
+  rc = check_counts(batch, max_blocks_per_seq);
+  if (rc) return rc;
+  if (pool_blocks < 1 || pool_blocks > INT32_MAX) return fail(KVS_E_RANGE, "pool_blocks out of range");
+  if (total_blocks < 0 || total_blocks > INT32_MAX) return fail(KVS_E_RANGE, "total_blocks out of range");
+  if (anchor_blocks < 0) return fail(KVS_E_RANGE, "anchor_blocks < 0");
+  if (free_capacity < 0) return fail(KVS_E_RANGE, "free_capacity < 0");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(kv_pool, 16) || !aligned(meta, 16))
+    return fail(KVS_E_ALIGN, "k_new, v_new, kv_pool and meta must be 16-byte aligned");
+  if (!aligned(workspace, kAlign)) return fail(KVS_E_ALIGN, "workspace must be 256-byte aligned");
+  const size_t need = kvs_append_workspace_bytes(batch);
+  if (workspace_bytes < need)
+    return fail(KVS_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  if ((uint64_t)shape->num_layers > 65535) return fail(KVS_E_RANGE, "num_layers > 65535");
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  kvs::AppendArgs a{};
+  a.k_new = static_cast<const uint8_t*>(k_new);
+  a.v_new = static_cast<const uint8_t*>(v_new);
+  a.pool = static_cast<uint8_t*>(kv_pool);
+  a.pool_blocks = pool_blocks;
+  a.table = block_table;
+  a.max_nb = max_blocks_per_seq;
+  a.seq_lens = seq_lens;
+  a.free_stack = free_stack;
+  a.free_capacity = free_capacity;
+  a.free_top = free_top;
+  a.meta = meta;
+  a.meta_off = meta_offsets;
+  a.seq_ids = seq_ids;
+  a.anchor_blocks = anchor_blocks;
+  a.total_blocks = total_blocks;
+  a.num_layers = shape->num_layers;
+  a.elem_bytes = kv_elem_bytes;
+  a.slot_pid = reinterpret_cast<int32_t*>(ws + kHeader);
+  a.slot_idx = reinterpret_cast<int32_t*>(ws + kHeader + (size_t)batch * 4u);
+  a.status = reinterpret_cast<uint32_t*>(ws);
+  hipError_t e = kvs::launch_append(a, batch, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return ok();
+}
+
+int kvs_classify(kvs_block_meta* meta, const int32_t* meta_offsets, const int32_t* seq_lens,
+                 int32_t batch, int32_t max_blocks_per_seq, int64_t total_blocks,
+                 const kvs_policy* policy, uint8_t* tiers_out, void* stream) {
   if (!meta || !meta_offsets) return fail(KVS_E_NULL, "a required pointer is NULL");
   int rc = check_policy(policy);
   if (rc) return rc;
@@ -532,6 +595,7 @@ int kvs_classify(kvs_block_meta* meta, const int32_t* meta_offsets, int32_t batc
   kvs::ScoreArgs a{};
   a.meta = meta;
   a.meta_off = meta_offsets;
+  a.seq_lens = seq_lens;
   a.tiers_out = tiers_out;
   a.total_blocks = total_blocks;
   a.pol = to_score_policy(policy);

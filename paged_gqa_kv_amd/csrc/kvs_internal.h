@@ -74,6 +74,7 @@ struct ScoreArgs {
   kvs_block_meta* meta;
   const float* mass;
   const int32_t* meta_off;
+  const int32_t* seq_lens;  // nullable: every record of the capacity is live
   float* chunk_max;         // [B][max_chunks]
   uint8_t* tiers_out;
   int64_t total_blocks;
@@ -88,6 +89,7 @@ struct ScoreArgs {
 struct EvictArgs {
   const kvs_block_meta* meta;
   const int32_t* meta_off;
+  const int32_t* seq_lens;  // nullable
   const uint8_t* active;    // nullable
   double* part_key;         // [B][max_chunks]
   int32_t* part_idx;        // [B][max_chunks]
@@ -102,9 +104,33 @@ struct EvictArgs {
   uint32_t* status;
 };
 
+struct AppendArgs {
+  const uint8_t* k_new;     // [B][num_layers][8][128] elements (pool's format)
+  const uint8_t* v_new;
+  uint8_t* pool;
+  int64_t pool_blocks;
+  int32_t* table;           // [B][max_nb]
+  int32_t max_nb;
+  int32_t* seq_lens;        // in / out
+  const int32_t* free_stack;
+  int32_t free_capacity;    // entries in free_stack
+  int32_t* free_top;        // in / out
+  kvs_block_meta* meta;
+  const int32_t* meta_off;
+  const uint64_t* seq_ids;
+  int32_t anchor_blocks;
+  int64_t total_blocks;
+  int32_t num_layers;
+  int32_t elem_bytes;       // 2: fp16, 1: E4M3
+  int32_t* slot_pid;        // [B] workspace: block written, -1 none
+  int32_t* slot_idx;        // [B] workspace: slot written
+  uint32_t* status;
+};
+
 struct MetaInitArgs {
   kvs_block_meta* meta;
   const int32_t* meta_off;
+  const int32_t* seq_lens;  // always null: initialise the whole capacity
   const uint64_t* seq_ids;
   int64_t total_blocks;
   int32_t max_nb;
@@ -120,6 +146,7 @@ hipError_t launch_score(const ScoreArgs& a, int batch, hipStream_t stream);
 hipError_t launch_classify(const ScoreArgs& a, int batch, hipStream_t stream);
 hipError_t launch_meta_init(const MetaInitArgs& a, int batch, hipStream_t stream);
 hipError_t launch_evict(const EvictArgs& a, int batch, hipStream_t stream);
+hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t stream);
 hipError_t launch_clear(uint32_t* p, int n, hipStream_t stream);
 hipError_t launch_probe(const void* src, void* dst, size_t bytes, int mode, int grid,
                         hipStream_t stream);

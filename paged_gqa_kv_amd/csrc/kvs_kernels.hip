@@ -58,7 +58,7 @@ __device__ __forceinline__ int seq_blocks(const int32_t* seq_lens, const int32_t
     return -1;
   }
   const int nb = (n + 15) >> 4;
-  if (r0 < 0 || r1 - r0 != nb || (int64_t)r1 > total_blocks) {
+  if (r0 < 0 || r1 - r0 < nb || (int64_t)r1 > total_blocks) {
     if (report) flag(status, KVS_DEV_BAD_OFFSETS);
     return -1;
   }
@@ -459,17 +459,29 @@ __global__ void __launch_bounds__(kMassThreads) block_mass(MassArgs a) {
 // ---------------------------------------------------------------------------
 // Scoring kernels.  Grid (chunk of kScoreThreads records, sequence).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int seq_records(const int32_t* off, int s, int max_nb,
-                                           int64_t total_blocks, uint32_t* status, bool report,
-                                           int* r0_out) {
+// Live records of sequence s: [r0, r0 + nb).  Records [r0, r1) are the
+// sequence's capacity; with seq_lens, nb = ceil(seq_lens[s] / 16) <= r1 - r0,
+// otherwise every record of the capacity is live.
+__device__ __forceinline__ int seq_records(const int32_t* off, const int32_t* seq_lens, int s,
+                                           int max_nb, int64_t total_blocks, uint32_t* status,
+                                           bool report, int* r0_out) {
   const int r0 = off[s];
   const int r1 = off[s + 1];
   if (r0 < 0 || r1 < r0 || r1 - r0 > max_nb || (int64_t)r1 > total_blocks) {
     if (report) flag(status, KVS_DEV_BAD_OFFSETS);
     return -1;
   }
+  int nb = r1 - r0;
+  if (seq_lens) {
+    const int n = seq_lens[s];
+    if (n < 0 || ((n + 15) >> 4) > nb) {
+      if (report) flag(status, KVS_DEV_BAD_SEQ_LEN);
+      return -1;
+    }
+    nb = (n + 15) >> 4;
+  }
   *r0_out = r0;
-  return r1 - r0;
+  return nb;
 }
 
 __device__ __forceinline__ float block_reduce_max(float v, float* red) {
@@ -490,7 +502,7 @@ __global__ void __launch_bounds__(kScoreThreads) seq_chunk_max(ScoreArgs a) {
   const int s = blockIdx.y;
   const int chunk = blockIdx.x;
   int r0 = 0;
-  const int nb = seq_records(a.meta_off, s, a.max_nb, a.total_blocks, a.status,
+  const int nb = seq_records(a.meta_off, a.seq_lens, s, a.max_nb, a.total_blocks, a.status,
                              threadIdx.x == 0 && chunk == 0, &r0);
   if (nb <= 0 || chunk * kScoreThreads >= nb) return;
   const int b = chunk * kScoreThreads + threadIdx.x;
@@ -513,7 +525,7 @@ __global__ void __launch_bounds__(kScoreThreads) score_update(ScoreArgs a) {
   const int s = blockIdx.y;
   const int chunk = blockIdx.x;
   int r0 = 0;
-  const int nb = seq_records(a.meta_off, s, a.max_nb, a.total_blocks, a.status, false, &r0);
+  const int nb = seq_records(a.meta_off, a.seq_lens, s, a.max_nb, a.total_blocks, a.status, false, &r0);
   if (nb <= 0 || chunk * kScoreThreads >= nb) return;
   const int nch = (nb + kScoreThreads - 1) / kScoreThreads;
   float M = 0.f;
@@ -596,7 +608,7 @@ __global__ void __launch_bounds__(kScoreThreads) evict_chunks(EvictArgs a) {
   const int s = blockIdx.y;
   const int chunk = blockIdx.x;
   int r0 = 0;
-  const int nb = seq_records(a.meta_off, s, a.max_nb, a.total_blocks, a.status,
+  const int nb = seq_records(a.meta_off, a.seq_lens, s, a.max_nb, a.total_blocks, a.status,
                              threadIdx.x == 0 && chunk == 0, &r0);
   if (nb <= 0 || chunk * kScoreThreads >= nb) return;
   const bool active = a.active == nullptr || a.active[s] != 0;
@@ -628,7 +640,7 @@ __global__ void __launch_bounds__(kScoreThreads) evict_final(EvictArgs a) {
   __shared__ int32_t ri[kScoreThreads / 64];
   const int s = blockIdx.x;
   int r0 = 0;
-  const int nb = seq_records(a.meta_off, s, a.max_nb, a.total_blocks, a.status, false, &r0);
+  const int nb = seq_records(a.meta_off, a.seq_lens, s, a.max_nb, a.total_blocks, a.status, false, &r0);
   const bool active = a.active == nullptr || a.active[s] != 0;
   KeyIdx v{0.0, -1};
   if (nb > 0 && active) {
@@ -647,7 +659,7 @@ __global__ void __launch_bounds__(kScoreThreads) evict_final(EvictArgs a) {
 __global__ void __launch_bounds__(kScoreThreads) classify_records(ScoreArgs a) {
   const int s = blockIdx.y;
   int r0 = 0;
-  const int nb = seq_records(a.meta_off, s, a.max_nb, a.total_blocks, a.status, false, &r0);
+  const int nb = seq_records(a.meta_off, a.seq_lens, s, a.max_nb, a.total_blocks, a.status, false, &r0);
   const int b = blockIdx.x * kScoreThreads + threadIdx.x;
   if (nb <= 0 || b >= nb) return;
   kvs_block_meta* rec = a.meta + r0 + b;
@@ -662,7 +674,7 @@ __global__ void __launch_bounds__(kScoreThreads) classify_records(ScoreArgs a) {
 __global__ void __launch_bounds__(kScoreThreads) meta_init(MetaInitArgs a) {
   const int s = blockIdx.y;
   int r0 = 0;
-  const int nb = seq_records(a.meta_off, s, a.max_nb, a.total_blocks, a.status, false, &r0);
+  const int nb = seq_records(a.meta_off, a.seq_lens, s, a.max_nb, a.total_blocks, a.status, false, &r0);
   const int b = blockIdx.x * kScoreThreads + threadIdx.x;
   if (nb <= 0 || b >= nb) return;
   kvs_block_meta rec;
@@ -678,6 +690,118 @@ __global__ void __launch_bounds__(kScoreThreads) meta_init(MetaInitArgs a) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) rec.reserved1[i] = 0u;
   a.meta[r0 + b] = rec;
+}
+
+// ---------------------------------------------------------------------------
+// KV append.  append_alloc (one work-group) walks the batch in order, hands
+// each sequence whose new token opens a block the next id from the top of the
+// free stack (an exclusive prefix count over the sequences that need one),
+// sets the table entry, creates the block's record and advances seq_lens.
+// append_scatter writes the token's K and V rows into their slot.
+// ---------------------------------------------------------------------------
+constexpr int kAllocThreads = 1024;
+
+__device__ __forceinline__ kvs_block_meta fresh_record(uint64_t seq_id, int b, int anchor_blocks) {
+  kvs_block_meta rec;
+  rec.key[0] = seq_id;
+  rec.key[1] = (uint64_t)b;
+  rec.score = 0.0;
+  rec.t_touch = KVS_NEVER_TOUCHED;
+  rec.touch_count = 0u;
+  rec.tier = KVS_UNCLASSIFIED;
+  rec.flags = b < anchor_blocks ? KVS_FLAG_ANCHOR : 0u;
+  rec.reserved0 = 0u;
+  rec.priority = 0.0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) rec.reserved1[i] = 0u;
+  return rec;
+}
+
+__global__ void __launch_bounds__(kAllocThreads) append_alloc(AppendArgs a, int batch) {
+  __shared__ int scan[kAllocThreads];
+  const int tid = threadIdx.x;
+  int top0 = *a.free_top;
+  if (top0 < 0 || top0 > a.free_capacity) {
+    if (tid == 0) flag(a.status, KVS_DEV_BAD_OFFSETS);
+    top0 = top0 < 0 ? 0 : a.free_capacity;
+  }
+  int carry = 0;
+  for (int base = 0; base < batch; base += kAllocThreads) {
+    const int s = base + tid;
+    int need = 0, t = 0, b = 0, slot = 0, r0 = 0, cap = 0;
+    bool valid = false;
+    if (s < batch) {
+      t = a.seq_lens[s];
+      r0 = a.meta_off[s];
+      cap = a.meta_off[s + 1] - r0;
+      valid = t >= 0 && r0 >= 0 && cap >= 0 && cap <= a.max_nb &&
+              (int64_t)r0 + cap <= a.total_blocks && ((t + 15) >> 4) <= cap;
+      b = t >> 4;
+      slot = t & 15;
+      need = (valid && slot == 0 && b < cap) ? 1 : 0;
+    }
+    scan[tid] = need;
+    __syncthreads();
+    for (int off = 1; off < kAllocThreads; off <<= 1) {
+      const int v = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    const int prefix = carry + scan[tid] - need;
+    if (s < batch) {
+      int pid = -1;
+      if (!valid) {
+        flag(a.status, KVS_DEV_BAD_SEQ_LEN);
+      } else if (slot == 0) {
+        if (need && prefix < top0) {
+          const int cand = a.free_stack[top0 - 1 - prefix];
+          if (cand >= 0 && (int64_t)cand < a.pool_blocks) {
+            pid = cand;
+            a.table[(size_t)s * a.max_nb + b] = pid;
+            a.meta[r0 + b] = fresh_record(a.seq_ids[s], b, a.anchor_blocks);
+          } else {
+            flag(a.status, KVS_DEV_BAD_BLOCK_ID);
+          }
+        } else {
+          flag(a.status, KVS_DEV_POOL_EXHAUSTED);
+        }
+      } else {
+        const int cur = a.table[(size_t)s * a.max_nb + b];
+        if (cur >= 0 && (int64_t)cur < a.pool_blocks) pid = cur;
+        else flag(a.status, KVS_DEV_BAD_BLOCK_ID);
+      }
+      if (pid >= 0) a.seq_lens[s] = t + 1;
+      a.slot_pid[s] = pid;
+      a.slot_idx[s] = slot;
+    }
+    carry += scan[kAllocThreads - 1];
+    __syncthreads();
+  }
+  if (tid == 0) *a.free_top = top0 - min(carry, top0);
+}
+
+__global__ void __launch_bounds__(256) append_scatter(AppendArgs a) {
+  const int s = blockIdx.x;
+  const int layer = blockIdx.y;
+  const int pid = a.slot_pid[s];
+  if (pid < 0) return;
+  const int slot = a.slot_idx[s];
+  const int row_bytes = kHeadDim * a.elem_bytes;          // one token, one head
+  const int row16 = row_bytes / 16;
+  const size_t tile = (size_t)16 * row_bytes;
+  const size_t blk = (size_t)a.num_layers * 16 * tile;    // 16 tiles (K, V x 8 heads) per layer
+  uint8_t* dst_layer = a.pool + (size_t)pid * blk + (size_t)layer * 16 * tile;
+  const size_t src_off = ((size_t)s * a.num_layers + layer) * 8 * row_bytes;
+  for (int idx = threadIdx.x; idx < 16 * row16; idx += 256) {
+    const int row = idx / row16;          // kv * 8 + head
+    const int part = idx - row * row16;
+    const int kv = row >> 3;
+    const int g = row & 7;
+    const uint8_t* src = (kv == 0 ? a.k_new : a.v_new) + src_off + (size_t)g * row_bytes + part * 16;
+    uint8_t* dst = dst_layer + (size_t)row * tile + (size_t)slot * row_bytes + part * 16;
+    *reinterpret_cast<u4_t*>(dst) = *reinterpret_cast<const u4_t*>(src);
+  }
 }
 
 __global__ void __launch_bounds__(64) clear_words(uint32_t* p, int n) {
@@ -773,6 +897,12 @@ hipError_t launch_evict(const EvictArgs& a, int batch, hipStream_t stream) {
 hipError_t launch_meta_init(const MetaInitArgs& a, int batch, hipStream_t stream) {
   const dim3 grid(a.max_chunks, batch);
   hipLaunchKernelGGL(meta_init, grid, dim3(kScoreThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t stream) {
+  hipLaunchKernelGGL(append_alloc, dim3(1), dim3(kAllocThreads), 0, stream, a, batch);
+  hipLaunchKernelGGL(append_scatter, dim3(batch, a.num_layers), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -5,6 +5,7 @@ decode + scoring step needs, and calls the library.  No arithmetic here.
 """
 from __future__ import annotations
 
+import numpy as np
 import torch
 
 from . import api
@@ -44,7 +45,8 @@ class DecodeSession:
 
     @property
     def kv_bytes_per_step(self) -> int:
-        """Logical KV bytes one decode step reads (keys and values, every token)."""
+        """Logical KV bytes one decode step reads (keys and values, every token of
+        the lengths materialised; appends grow this by one token per sequence)."""
         return (sum(self.m.lens) * (self.layer_end - self.layer_begin) * 8 * 128 * 2
                 * self.kv_elem_bytes)
 
@@ -65,13 +67,31 @@ class DecodeSession:
 
     def score(self, step: int, pol, classify: int = 1):
         m = self.m
-        api.score_update(self.meta, self.mass, m.meta_offsets, m.batch, m.max_blocks,
-                         m.total_blocks, step, pol, classify, self.score_ws, stream=self.stream)
+        api.score_update(self.meta, self.mass, m.meta_offsets, m.seq_lens, m.batch,
+                         m.max_blocks, m.total_blocks, step, pol, classify, self.score_ws,
+                         stream=self.stream)
 
     def classify(self, pol, tiers_out=None):
         m = self.m
-        api.classify(self.meta, m.meta_offsets, m.batch, m.max_blocks, m.total_blocks, pol,
-                     tiers_out, stream=self.stream)
+        api.classify(self.meta, m.meta_offsets, m.seq_lens, m.batch, m.max_blocks,
+                     m.total_blocks, pol, tiers_out, stream=self.stream)
+
+    def append(self, k_new, v_new):
+        """Append one token per sequence (updates the pool, table, seq_lens and
+        records in place; the host copies of lengths are not touched)."""
+        m = self.m
+        if not hasattr(self, "free_stack"):
+            dev = self.out.device
+            self.free_stack = torch.from_numpy(m.free_stack.astype(np.int32)).to(dev)
+            self.free_top = torch.tensor([int(m.free_stack.size)], dtype=torch.int32, device=dev)
+            self.append_ws = torch.empty(api.append_workspace_bytes(m.batch), dtype=torch.uint8,
+                                         device=dev)
+            api.workspace_init(self.append_ws, stream=self.stream)
+        eb = 1 if m.workload.kv_format == "e4m3" else 2
+        api.append_kv(self.shape, eb, k_new, v_new, m.pool, m.pool_blocks, m.block_table,
+                      m.max_blocks, m.seq_lens, self.free_stack, int(self.free_stack.numel()),
+                      self.free_top, self.meta, m.meta_offsets, m.seq_ids, self.anchor_blocks,
+                      m.batch, m.total_blocks, self.append_ws, stream=self.stream)
 
     def evict_candidates(self, now: int, alpha: float, active=None, exclude_pinned: int = 0):
         """(out_block int32 [B], out_key float64 [B]) device tensors."""
@@ -82,7 +102,7 @@ class DecodeSession:
             api.workspace_init(self.evict_ws, stream=self.stream)
         blk = torch.empty(m.batch, dtype=torch.int32, device=self.out.device)
         key = torch.empty(m.batch, dtype=torch.float64, device=self.out.device)
-        api.evict_candidates(self.meta, m.meta_offsets, active, m.batch, m.max_blocks,
+        api.evict_candidates(self.meta, m.meta_offsets, m.seq_lens, active, m.batch, m.max_blocks,
                              m.total_blocks, now, alpha, exclude_pinned, blk, key, self.evict_ws,
                              stream=self.stream)
         return blk, key
@@ -95,6 +115,8 @@ class DecodeSession:
         bits = api.device_status(self.ws, self.stream) | api.device_status(self.score_ws, self.stream)
         if hasattr(self, "evict_ws"):
             bits |= api.device_status(self.evict_ws, self.stream)
+        if hasattr(self, "append_ws"):
+            bits |= api.device_status(self.append_ws, self.stream)
         return bits
 
     def records(self):

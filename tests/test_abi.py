@@ -112,7 +112,7 @@ def test_decode_rejects_before_launch(over, code):
 def test_score_and_classify_validation():
     pol = api.policy(0.15)
     ok_ws = api.score_workspace_bytes(2, 4)
-    args = (0x1000, 0x2000, 0x3000, 2, 4, 8)
+    args = (0x1000, 0x2000, 0x3000, 0x3800, 2, 4, 8)
     with pytest.raises(KvsError) as e:
         api.score_update(*args, 0, api.policy(0.0), 1, 0x10000, ok_ws, stream=0)
     assert e.value.code == KVS_E_POLICY
@@ -130,10 +130,10 @@ def test_score_and_classify_validation():
         api.score_update(*args, 2**64 - 1, pol, 1, 0x10000, ok_ws, stream=0)
     assert e.value.code == KVS_E_RANGE
     with pytest.raises(KvsError) as e:
-        api.score_update(0, 0x2000, 0x3000, 2, 4, 8, 0, pol, 1, 0x10000, ok_ws, stream=0)
+        api.score_update(0, 0x2000, 0x3000, 0x3800, 2, 4, 8, 0, pol, 1, 0x10000, ok_ws, stream=0)
     assert e.value.code == KVS_E_NULL
     with pytest.raises(KvsError) as e:
-        api.classify(0x1000, 0x3000, 0, 4, 8, pol, stream=0)
+        api.classify(0x1000, 0x3000, None, 0, 4, 8, pol, stream=0)
     assert e.value.code == KVS_E_RANGE
     with pytest.raises(KvsError) as e:
         api.meta_init(0x1000, 0x3000, 0x5000, 2, 4, 8, anchor_blocks=-1, stream=0)
@@ -157,3 +157,44 @@ def test_binding_requires_the_library(monkeypatch):
     monkeypatch.setattr(_abi, "LIB_PATH", "/nonexistent/libkvs.so")
     with pytest.raises(ImportError):
         _abi.lib()
+
+
+def test_append_validation():
+    shp = api.shape(2)
+    ws = api.append_workspace_bytes(3)
+    assert ws >= 256 + 3 * 8
+    base = dict(kv_elem_bytes=2, k_new=0x1000, v_new=0x2000, kv_pool=0x3000, pool_blocks=10,
+                block_table=0x4000, max_blocks=4, seq_lens=0x5000, free_stack=0x6000,
+                free_capacity=5, free_top=0x7000, meta=0x8000, meta_offsets=0x9000,
+                seq_ids=0xA000, anchor_blocks=1, batch=3, total_blocks=12, workspace=0x10000,
+                workspace_bytes=ws)
+
+    def call(**over):
+        a = dict(base, **over)
+        api.append_kv(shp, a["kv_elem_bytes"], a["k_new"], a["v_new"], a["kv_pool"],
+                      a["pool_blocks"], a["block_table"], a["max_blocks"], a["seq_lens"],
+                      a["free_stack"], a["free_capacity"], a["free_top"], a["meta"],
+                      a["meta_offsets"], a["seq_ids"], a["anchor_blocks"], a["batch"],
+                      a["total_blocks"], a["workspace"], a["workspace_bytes"], stream=0)
+
+    for over, code in [(dict(k_new=0), KVS_E_NULL), (dict(free_top=0), KVS_E_NULL),
+                       (dict(kv_elem_bytes=4), KVS_E_RANGE), (dict(batch=0), KVS_E_RANGE),
+                       (dict(free_capacity=-1), KVS_E_RANGE), (dict(anchor_blocks=-1), KVS_E_RANGE),
+                       (dict(kv_pool=0x3008), KVS_E_ALIGN), (dict(workspace_bytes=ws - 1),
+                                                             KVS_E_WORKSPACE)]:
+        with pytest.raises(KvsError) as e:
+            call(**over)
+        assert e.value.code == code, over
+
+
+def test_capacity_layout_host_side():
+    import workload as W
+    m = W.materialise(W.custom("cap", 1, [17, 40], seed=1, spare_blocks=5), "cpu",
+                      extra_blocks=3)
+    assert m.capacity == [2 + 3, 3 + 3]
+    assert m.meta_offsets.tolist() == [0, 5, 11]
+    assert m.total_blocks == 11 and m.max_blocks == 6
+    assert m.block_table.shape == (2, 6)
+    used = set(m.table_host[m.table_host >= 0].tolist())
+    assert used.isdisjoint(set(m.free_stack.tolist()))
+    assert len(used) + m.free_stack.size == m.pool_blocks

@@ -16,5 +16,6 @@ from .recipe import (  # noqa: F401
     custom,
     materialise,
     make_query,
+    new_token_kv,
     query_seed,
 )

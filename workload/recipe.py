@@ -139,6 +139,8 @@ class Materialised:
     table_host: np.ndarray        # int32 [B][max_blocks]
     refcount: np.ndarray          # int32 [P]: sequences referencing each physical block
     unique_blocks: int
+    free_stack: np.ndarray = None  # int32: pool blocks no table references (top = last)
+    capacity: list = None          # records (and table entries) per sequence
 
     @property
     def num_layers(self) -> int:
@@ -153,7 +155,7 @@ def query_seed(seed: int, step: int) -> int:
     return (seed * 1_000_003 + 7_919 * (step + 1)) & 0x7FFF_FFFF_FFFF
 
 
-def _layout(wl: Workload):
+def _layout(wl: Workload, extra_blocks: int = 0):
     lens = wl.lengths()
     if any(n <= 0 for n in lens):
         raise ValueError("every sequence needs at least one token")
@@ -168,7 +170,7 @@ def _layout(wl: Workload):
     perm = rng.permutation(pool).astype(np.int64)
     shared = perm[:used_shared]
     cursor = used_shared
-    max_nb = max(blocks)
+    max_nb = max(blocks) + extra_blocks
     table = np.full((wl.batch, max_nb), -1, dtype=np.int32)
     refcount = np.zeros(pool, dtype=np.int32)
     for s, nb in enumerate(blocks):
@@ -177,7 +179,8 @@ def _layout(wl: Workload):
         table[s, k:nb] = perm[cursor:cursor + nb - k]
         cursor += nb - k
         np.add.at(refcount, table[s, :nb], 1)
-    return lens, blocks, shared_nb, pool, table, refcount, unique
+    free = perm[cursor:].astype(np.int32)
+    return lens, blocks, shared_nb, pool, table, refcount, unique, free
 
 
 def _boost_positions(wl: Workload, lens, table, shared_nb):
@@ -196,9 +199,12 @@ def _boost_positions(wl: Workload, lens, table, shared_nb):
     return arr[:, 0], arr[:, 1]
 
 
-def materialise(wl: Workload, device="cpu") -> Materialised:
+def materialise(wl: Workload, device="cpu", extra_blocks: int = 0) -> Materialised:
+    """extra_blocks: table entries and records reserved per sequence beyond its
+    current blocks, for appends; pool blocks no table references form the free
+    stack."""
     device = torch.device(device)
-    lens, blocks, shared_nb, pool_n, table, refcount, unique = _layout(wl)
+    lens, blocks, shared_nb, pool_n, table, refcount, unique, free = _layout(wl, extra_blocks)
     L = wl.num_layers
 
     gen = torch.Generator(device=device)
@@ -237,8 +243,9 @@ def materialise(wl: Workload, device="cpu") -> Materialised:
     if unused.size:
         pool[torch.from_numpy(unused).to(device)] = 0x7F if fp8 else float("nan")
 
+    capacity = [nb + extra_blocks for nb in blocks]
     offsets = np.zeros(wl.batch + 1, dtype=np.int32)
-    offsets[1:] = np.cumsum(blocks)
+    offsets[1:] = np.cumsum(capacity)
     return Materialised(
         workload=wl,
         pool=pool,
@@ -249,12 +256,14 @@ def materialise(wl: Workload, device="cpu") -> Materialised:
         u=u,
         lens=lens,
         blocks=blocks,
-        max_blocks=max(blocks),
+        max_blocks=max(capacity),
         total_blocks=int(offsets[-1]),
         pool_blocks=pool_n,
         table_host=table,
         refcount=refcount,
         unique_blocks=unique,
+        free_stack=free,
+        capacity=capacity,
     )
 
 
@@ -268,3 +277,21 @@ def make_query(m: Materialised, step: int) -> torch.Tensor:
                     generator=gen, device=device, dtype=torch.float32)
     q += wl.q_boost * m.u[None, :, :, None, :]
     return q.reshape(wl.batch, wl.num_layers, NUM_Q_HEADS, HEAD_DIM).to(torch.float16)
+
+
+def new_token_kv(m: Materialised, step: int):
+    """K and V of the token appended before decode step `step`: [B][L][8][128]
+    in the pool's format.  Values N(0, 1); keys get the recent-tail boost
+    +k_boost*u (the new token is the most recent position)."""
+    wl = m.workload
+    device = m.u.device
+    gen = torch.Generator(device=device)
+    gen.manual_seed(query_seed(wl.seed, step) ^ 0x5A5A5A5A)
+    shape = (wl.batch, wl.num_layers, NUM_KV_HEADS, HEAD_DIM)
+    k = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    v = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    k += wl.k_boost * m.u[None]
+    if wl.kv_format == "e4m3":
+        return (k.to(torch.float8_e4m3fn).view(torch.uint8).contiguous(),
+                v.to(torch.float8_e4m3fn).view(torch.uint8).contiguous())
+    return k.to(torch.float16).contiguous(), v.to(torch.float16).contiguous()
