@@ -41,6 +41,8 @@ def _parse():
                     help="stored K/V format (e4m3: FP8 codes, half the bytes)")
     ap.add_argument("--alpha", type=float, default=None)
     ap.add_argument("--split-blocks", type=int, default=0)
+    ap.add_argument("--append", action="store_true",
+                    help="each step first appends one token per sequence (kvs_append_kv)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="approximate CPU time budget of the oracle baseline (0 = skip)")
     ap.add_argument("--copy-probe-gib", type=float, default=4.0,
@@ -196,9 +198,15 @@ def main():
     if args.kv_format == "e4m3":
         wl = W.as_e4m3(wl)
     alpha = args.alpha if args.alpha is not None else wl.alphas[0]
+    extra = 0
+    if args.append:
+        # room for the appended tokens: table entries, records and free pool blocks
+        extra = (args.warmup + args.steps) // 16 + 2
+        import dataclasses
+        wl = dataclasses.replace(wl, spare_blocks=max(wl.spare_blocks, extra * wl.batch + 8))
     print(f"[bench] materialising {wl.name} on cuda:0", file=sys.stderr, flush=True)
     t0 = time.time()
-    m = W.materialise(wl, "cuda")
+    m = W.materialise(wl, "cuda", extra_blocks=extra)
     torch.cuda.synchronize()
     print(f"[bench] inputs ready in {time.time() - t0:.1f} s; pool {m.pool.numel() * 2 / 2**30:.2f} GiB",
           file=sys.stderr, flush=True)
@@ -206,6 +214,12 @@ def main():
     pol = api.policy(alpha)
     n_q = args.warmup + args.steps
     queries = [W.make_query(m, k) for k in range(n_q)]
+    new_kv = [W.new_token_kv(m, k) for k in range(n_q)] if args.append else None
+
+    def run_step(k, idx):
+        if new_kv is not None:
+            sess.append(*new_kv[idx])
+        sess.step(queries[idx], k, pol)
     torch.cuda.synchronize()
 
     ev = HipEvents()
@@ -214,7 +228,7 @@ def main():
     # warm-up on the same buffers; records are re-initialised afterwards so the
     # timed steps start from fresh records with steps 0..K-1
     for k in range(args.warmup):
-        sess.step(queries[k], k, pol)
+        run_step(k, k)
     torch.cuda.synchronize()
     sess.reset_meta()
     torch.cuda.synchronize()
@@ -224,10 +238,11 @@ def main():
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
+    lens_at_start = m.seq_lens.cpu().numpy().copy()
     start.record(stream)
     for k in range(args.steps):
         api.set_decode_events(*pairs[k])
-        sess.step(queries[args.warmup + k], k, pol)
+        run_step(k, args.warmup + k)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -245,13 +260,22 @@ def main():
     # mass sums to layers x 64
     mass = sess.mass.cpu().numpy().astype(np.float64)
     offs = m.meta_offsets.cpu().numpy()
+    lens_end = m.seq_lens.cpu().numpy()
+    nb_end = (lens_end + 15) // 16
+    nb_start = (lens_at_start + 15) // 16
     for s in range(m.batch):
-        tot = mass[offs[s]:offs[s + 1]].sum()
+        tot = mass[offs[s]:offs[s] + nb_end[s]].sum()
         if not math.isclose(tot, m.num_layers * 64, rel_tol=1e-4):
             raise RuntimeError(f"block mass of sequence {s} sums to {tot}")
     rec = sess.records()
-    if not (rec["touch_count"] == args.steps).all() or not (rec["t_touch"] == args.steps - 1).all():
+    rows = np.concatenate([offs[s] + np.arange(nb_start[s]) for s in range(m.batch)])
+    if (not (rec["touch_count"][rows] == args.steps).all()
+            or not (rec["t_touch"][rows] == args.steps - 1).all()):
         raise RuntimeError("touch counts / timestamps do not match the steps run")
+    if args.append and not np.array_equal(lens_end, lens_at_start + args.steps):
+        raise RuntimeError("appends did not advance every sequence by one token per step")
+    live = np.concatenate([offs[s] + np.arange(nb_end[s]) for s in range(m.batch)])
+    rec = rec[live]
 
     # eviction candidates over the same records (the step after classification;
     # timed on its own, outside the step)
@@ -269,6 +293,9 @@ def main():
         raise RuntimeError("a sequence got no eviction candidate")
 
     kv_bytes = sess.kv_bytes_per_step
+    if args.append:   # the average step reads the lengths in the middle of the run
+        mean_tokens = float(lens_at_start.sum()) + m.batch * (args.steps + 1) / 2.0
+        kv_bytes = int(mean_tokens * m.num_layers * 8 * 128 * 2 * sess.kv_elem_bytes)
     unique_bytes = m.unique_blocks * 16 * m.num_layers * 8 * 128 * 2 * sess.kv_elem_bytes
     t_step = total_ms / 1e3 / args.steps
     value = kv_bytes / t_step / 1e9
@@ -307,6 +334,7 @@ def main():
             "layers": m.num_layers,
             "batch": m.batch,
             "kv_format": args.kv_format,
+            "append": bool(args.append),
             "context_tokens": int(sum(m.lens)),
             "records": m.total_blocks,
             "alpha": alpha,
