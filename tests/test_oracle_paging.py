@@ -85,3 +85,58 @@ def test_grow_keeps_history_and_adds_fresh_records():
     assert g.nblocks.tolist() == [3, 3, 3, 1]
     with pytest.raises(ValueError):
         OS.grow(st, [1, 1])
+
+
+def test_append_rebuilds_a_cache_made_at_the_longer_length():
+    """Take a cache made with lengths n+1, cut every sequence back to n (the last
+    token's block returns to the free stack when it held only that token), and
+    append the cut token: pool, table and decode are those of the original."""
+    lens1 = [17, 32, 1, 48, 100]
+    wl = W.custom("cut", 2, lens1, seed=21, spare_blocks=4)
+    m = W.materialise(wl, "cpu")
+    pool = m.pool.numpy().copy()
+    table = m.table_host.astype(np.int64).copy()
+    B, L = len(lens1), 2
+    k = np.empty((B, L, 8, 128), np.float16)
+    v = np.empty((B, L, 8, 128), np.float16)
+    freed = []
+    for s, n1 in enumerate(lens1):
+        b, slot = divmod(n1 - 1, 16)
+        pid = int(table[s, b])
+        k[s] = pool[pid, :, 0, :, slot, :]
+        v[s] = pool[pid, :, 1, :, slot, :]
+        pool[pid, :, :, :, slot, :] = np.nan               # the cut slot forgets its token
+        if slot == 0:
+            freed.append(pid)
+            table[s, b] = -1
+    free = np.array(freed[::-1], dtype=np.int64)            # first needing sequence takes freed[0]
+    lens = np.array([n - 1 for n in lens1], dtype=np.int64)
+    top, allocs, rejected = PG.append_step(pool, table, lens, free, free.size, k, v)
+    assert rejected == [] and top == 0
+    assert lens.tolist() == lens1
+    assert np.array_equal(table, m.table_host)
+    live = np.unique(table[table >= 0])
+    assert np.array_equal(pool[live].view(np.uint16), m.pool.numpy()[live].view(np.uint16))
+    q = np.random.default_rng(5).standard_normal((B, L, 64, 128)).astype(np.float16)
+    scale = 1.0 / np.sqrt(128.0)
+    out_a, mass_a = OA.decode_step(q, pool, table, lens1, scale)
+    out_b, mass_b = OA.decode_step(q, m.pool.numpy(), m.table_host, lens1, scale)
+    assert np.array_equal(out_a, out_b)
+    assert all(np.array_equal(x, y) for x, y in zip(mass_a, mass_b))
+
+
+def test_sixteen_appends_fill_one_block_then_open_the_next():
+    m, pool, table, lens, free = _setup([16, 3], spare=4)
+    rng = np.random.default_rng(9)
+    top = free.size
+    opened = []
+    for step in range(17):
+        k, v = _new_kv(rng, 2, 2)
+        top, allocs, rejected = PG.append_step(pool, table, lens, free, top, k, v)
+        assert rejected == []
+        opened += [(step, s, b) for s, b, _ in allocs]
+    # sequence 0 opens block 1 at its first append and block 2 after 16 more;
+    # sequence 1 (3 tokens) opens block 1 when it reaches 16 tokens (13th append)
+    assert opened == [(0, 0, 1), (13, 1, 1), (16, 0, 2)]
+    assert lens.tolist() == [33, 20]
+    assert top == free.size - 3
