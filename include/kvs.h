@@ -133,18 +133,21 @@ size_t kvs_block_bytes(const kvs_shape* shape);
  * priority, reserved1. */
 size_t kvs_meta_layout(size_t* offsets, int n);
 
-/* Blocks per split used by kvs_decode_step for this problem when
- * split_blocks == 0 is passed (a power of two in [16, 512]); otherwise
- * split_blocks itself if valid, or 0 if invalid. */
-int32_t kvs_decode_split_blocks(const kvs_shape* shape, int32_t batch,
+/* Blocks per split used for this problem when split_blocks == 0 is passed (a
+ * power of two in [16, 1024], chosen from the sizes and the stored element
+ * size: kv_elem_bytes 2 for kvs_decode_step's fp16 pool, 1 for
+ * kvs_decode_step_e4m3's pool); otherwise split_blocks itself if valid.  0 if
+ * any argument is invalid. */
+int32_t kvs_decode_split_blocks(const kvs_shape* shape, int32_t kv_elem_bytes, int32_t batch,
                                 int32_t max_blocks_per_seq, int32_t layer_begin,
                                 int32_t layer_end, int32_t split_blocks);
 
-/* Workspace bytes kvs_decode_step needs for these sizes (0 on invalid input).
- * The workspace holds a 256-byte status header, the per-split softmax
- * statistics and partial outputs, and the per-(layer, head, block) mass
- * partials: about 4 x 64 x (layer_end - layer_begin) x total_blocks bytes. */
-size_t kvs_decode_workspace_bytes(const kvs_shape* shape, int32_t batch,
+/* Workspace bytes the decode entry point of this element size (2: fp16, 1:
+ * E4M3) needs for these sizes (0 on invalid input).  The workspace holds a
+ * 256-byte status header, the per-split softmax statistics and partial outputs,
+ * and the per-(layer, head, block) mass partials: about
+ * 4 x 64 x (layer_end - layer_begin) x total_blocks bytes. */
+size_t kvs_decode_workspace_bytes(const kvs_shape* shape, int32_t kv_elem_bytes, int32_t batch,
                                   int32_t max_blocks_per_seq, int64_t total_blocks,
                                   int32_t layer_begin, int32_t layer_end,
                                   int32_t split_blocks);

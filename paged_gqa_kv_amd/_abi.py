@@ -69,8 +69,9 @@ _SIGS = {
     "kvs_bytes_per_token": (_sz, [ctypes.POINTER(Shape)]),
     "kvs_block_bytes": (_sz, [ctypes.POINTER(Shape)]),
     "kvs_meta_layout": (_sz, [ctypes.POINTER(ctypes.c_size_t), ctypes.c_int]),
-    "kvs_decode_split_blocks": (_i32, [ctypes.POINTER(Shape), _i32, _i32, _i32, _i32, _i32]),
-    "kvs_decode_workspace_bytes": (_sz, [ctypes.POINTER(Shape), _i32, _i32, _i64, _i32, _i32, _i32]),
+    "kvs_decode_split_blocks": (_i32, [ctypes.POINTER(Shape), _i32, _i32, _i32, _i32, _i32, _i32]),
+    "kvs_decode_workspace_bytes": (_sz, [ctypes.POINTER(Shape), _i32, _i32, _i32, _i64, _i32, _i32,
+                                         _i32]),
     "kvs_score_workspace_bytes": (_sz, [_i32, _i32]),
     "kvs_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kvs_last_error": (ctypes.c_char_p, []),

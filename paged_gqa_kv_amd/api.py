@@ -66,15 +66,16 @@ def meta_layout():
 
 
 def decode_split_blocks(shp: Shape, batch: int, max_blocks: int, layer_begin: int,
-                        layer_end: int, split_blocks: int = 0) -> int:
-    return lib().kvs_decode_split_blocks(ctypes.byref(shp), batch, max_blocks, layer_begin,
-                                         layer_end, split_blocks)
+                        layer_end: int, split_blocks: int = 0, kv_elem_bytes: int = 2) -> int:
+    return lib().kvs_decode_split_blocks(ctypes.byref(shp), kv_elem_bytes, batch, max_blocks,
+                                         layer_begin, layer_end, split_blocks)
 
 
 def decode_workspace_bytes(shp: Shape, batch: int, max_blocks: int, total_blocks: int,
-                           layer_begin: int, layer_end: int, split_blocks: int = 0) -> int:
-    return lib().kvs_decode_workspace_bytes(ctypes.byref(shp), batch, max_blocks, total_blocks,
-                                            layer_begin, layer_end, split_blocks)
+                           layer_begin: int, layer_end: int, split_blocks: int = 0,
+                           kv_elem_bytes: int = 2) -> int:
+    return lib().kvs_decode_workspace_bytes(ctypes.byref(shp), kv_elem_bytes, batch, max_blocks,
+                                            total_blocks, layer_begin, layer_end, split_blocks)
 
 
 def score_workspace_bytes(batch: int, max_blocks: int) -> int:

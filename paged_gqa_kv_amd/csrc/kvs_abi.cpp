@@ -43,10 +43,14 @@ int ok() {
 
 constexpr size_t kHeader = 256;
 constexpr size_t kAlign = 256;
-// Split-K sizing: the largest split (fewest partial results, longest streams)
-// that still gives at least this many decode waves, about three rounds of the
-// chip at the decode kernel's 12 resident waves per CU.
-constexpr uint64_t kTargetWaves = 8192;
+// Split-K sizing.  Each decode wave keeps two blocks of its (layer, KV head)
+// in flight: 16 KiB for fp16, 8 KiB for E4M3.  The chip needs about 16 MiB of
+// reads in flight to stay at HBM bandwidth, and on gfx950 about 56 KiB per
+// compute unit; within those, the longest splits measured fastest (fewer
+// partial results, longer streams per wave, fewer resident streams).
+constexpr uint64_t kChipInflightBytes = 16ull << 20;
+constexpr uint64_t kCuInflightBytes = 56ull << 10;
+constexpr int32_t kMaxAutoSplit = 1024;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -93,11 +97,18 @@ int check_counts(int32_t batch, int32_t max_blocks) {
   return KVS_OK;
 }
 
-int32_t choose_split(int32_t batch, int32_t max_nb, int32_t n_layers) {
-  const uint64_t items = (uint64_t)batch * (uint64_t)n_layers * 8u;
-  for (int32_t cand = 512; cand >= 16; cand >>= 1) {
-    const uint64_t waves = items * (uint64_t)((max_nb + cand - 1) / cand);
-    if (waves >= kTargetWaves) return cand;
+// The largest power-of-two split in [16, 1024] whose launch keeps enough
+// bytes in flight on the whole chip (wave count) and per compute unit (waves
+// that fit the LDS a split needs, at most kDecodeWavesPerSimd per SIMD).
+int32_t choose_split(int32_t batch, int32_t max_nb, int32_t n_layers, int32_t kv_elem_bytes) {
+  const uint64_t streams = (uint64_t)batch * (uint64_t)n_layers * 8u;
+  const uint64_t wave_inflight = 2ull * 2ull * 16ull * 128ull * (uint64_t)kv_elem_bytes;
+  for (int32_t cand = kMaxAutoSplit; cand >= 16; cand >>= 1) {
+    const uint64_t waves = streams * (uint64_t)((max_nb + cand - 1) / cand);
+    uint64_t per_cu = kvs::kLdsPerCu / kvs::decode_lds_bytes(cand);
+    if (per_cu > 4u * kvs::kDecodeWavesPerSimd) per_cu = 4u * kvs::kDecodeWavesPerSimd;
+    if (waves * wave_inflight >= kChipInflightBytes && per_cu * wave_inflight >= kCuInflightBytes)
+      return cand;
   }
   return 16;
 }
@@ -112,13 +123,16 @@ struct DecodeLayout {
 };
 
 // Returns false on invalid sizes (no message).
-bool decode_layout(const kvs_shape* shape, int32_t batch, int32_t max_nb, int64_t total_blocks,
-                   int32_t lb, int32_t le, int32_t split_blocks, DecodeLayout* L) {
-  if (!shape || batch < 1 || batch > kMaxBatch || max_nb < 1 || max_nb > kMaxBlocksPerSeq ||
-      total_blocks < 0 || total_blocks > INT32_MAX || lb < 0 || le <= lb || le > shape->num_layers)
+bool decode_layout(const kvs_shape* shape, int32_t kv_elem_bytes, int32_t batch, int32_t max_nb,
+                   int64_t total_blocks, int32_t lb, int32_t le, int32_t split_blocks,
+                   DecodeLayout* L) {
+  if (!shape || (kv_elem_bytes != 1 && kv_elem_bytes != 2) || batch < 1 || batch > kMaxBatch ||
+      max_nb < 1 || max_nb > kMaxBlocksPerSeq || total_blocks < 0 || total_blocks > INT32_MAX ||
+      lb < 0 || le <= lb || le > shape->num_layers)
     return false;
   const int32_t nl = le - lb;
-  const int32_t sb = split_blocks == 0 ? choose_split(batch, max_nb, nl) : split_blocks;
+  const int32_t sb =
+      split_blocks == 0 ? choose_split(batch, max_nb, nl, kv_elem_bytes) : split_blocks;
   if (!split_valid(sb)) return false;
   const uint64_t nsplit = (uint64_t)(max_nb + sb - 1) / sb;
   const uint64_t stats = (uint64_t)batch * nl * 64u * nsplit;
@@ -186,20 +200,22 @@ size_t kvs_meta_layout(size_t* offsets, int n) {
   return sizeof(kvs_block_meta);
 }
 
-int32_t kvs_decode_split_blocks(const kvs_shape* shape, int32_t batch, int32_t max_blocks_per_seq,
-                                int32_t layer_begin, int32_t layer_end, int32_t split_blocks) {
+int32_t kvs_decode_split_blocks(const kvs_shape* shape, int32_t kv_elem_bytes, int32_t batch,
+                                int32_t max_blocks_per_seq, int32_t layer_begin, int32_t layer_end,
+                                int32_t split_blocks) {
   DecodeLayout L;
-  if (!decode_layout(shape, batch, max_blocks_per_seq, 0, layer_begin, layer_end, split_blocks, &L))
+  if (!decode_layout(shape, kv_elem_bytes, batch, max_blocks_per_seq, 0, layer_begin, layer_end,
+                     split_blocks, &L))
     return 0;
   return L.split_blocks;
 }
 
-size_t kvs_decode_workspace_bytes(const kvs_shape* shape, int32_t batch, int32_t max_blocks_per_seq,
-                                  int64_t total_blocks, int32_t layer_begin, int32_t layer_end,
-                                  int32_t split_blocks) {
+size_t kvs_decode_workspace_bytes(const kvs_shape* shape, int32_t kv_elem_bytes, int32_t batch,
+                                  int32_t max_blocks_per_seq, int64_t total_blocks,
+                                  int32_t layer_begin, int32_t layer_end, int32_t split_blocks) {
   DecodeLayout L;
-  if (!decode_layout(shape, batch, max_blocks_per_seq, total_blocks, layer_begin, layer_end,
-                     split_blocks, &L))
+  if (!decode_layout(shape, kv_elem_bytes, batch, max_blocks_per_seq, total_blocks, layer_begin,
+                     layer_end, split_blocks, &L))
     return 0;
   return L.total;
 }
@@ -291,8 +307,8 @@ int decode_step(bool kv_e4m3, const kvs_shape* shape, const void* q, const void*
     return fail(KVS_E_ALIGN, "int32 / fp32 arrays must be 4-byte aligned");
   if (!aligned(workspace, kAlign)) return fail(KVS_E_ALIGN, "workspace must be 256-byte aligned");
   DecodeLayout L;
-  if (!decode_layout(shape, batch, max_blocks_per_seq, total_blocks, layer_begin, layer_end,
-                     split_blocks, &L))
+  if (!decode_layout(shape, kv_e4m3 ? 1 : 2, batch, max_blocks_per_seq, total_blocks, layer_begin,
+                     layer_end, split_blocks, &L))
     return fail(KVS_E_RANGE, "inconsistent sizes");
   if (workspace_bytes < L.total)
     return fail(KVS_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);

@@ -11,6 +11,14 @@ namespace kvs {
 constexpr int kMassThreads = 1024;   // 16 waves share one 64-block column
 constexpr int kScoreThreads = 256;   // records per scoring work-group
 constexpr size_t kMaxDecodeLds = 65536;  // dynamic LDS a decode work-group may request
+constexpr size_t kLdsPerCu = 163840;     // gfx950: 160 KiB of LDS per compute unit
+constexpr int kDecodeWavesPerSimd = 3;   // decode kernel launch bound (VGPR budget)
+
+// LDS of one decode work-group (one wave): the split's block ids (4 B each),
+// per-block mass partials of the 8 heads (32 B each) and the 4 KiB value stage.
+constexpr size_t decode_lds_bytes(int32_t split_blocks) {
+  return (size_t)36 * (size_t)split_blocks + 4096;
+}
 
 struct DecodeArgs {
   const uint16_t* q;        // fp16 bits [B][num_layers][64][128]

@@ -36,7 +36,8 @@ constexpr int kHeadDim = 128;
 constexpr int kGroup = 8;                 // query heads per KV head
 constexpr int kQHeads = 64;
 constexpr int kTileBytes = 16 * kHeadDim * 2;          // fp16 (layer, K|V, KV head) tile: 4 KiB
-constexpr int kVStageBytes = kTileBytes;                // value tile staged as fp16 in LDS
+static_assert(decode_lds_bytes(1024) <= kMaxDecodeLds, "largest split must fit the LDS bound");
+static_assert(decode_lds_bytes(0) == kTileBytes, "value stage holds one fp16 tile");
 
 __device__ __forceinline__ float xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 
@@ -85,9 +86,13 @@ __device__ __forceinline__ int seq_blocks(const int32_t* seq_lens, const int32_t
 //  maximum per head; the per-block mass of head c is kept in LDS relative to
 //  the current maximum and rescaled whenever that maximum grows.
 // ---------------------------------------------------------------------------
-// K/V tiles are read exactly once per step; plain loads measured faster on
-// gfx950 than non-temporal ones for this access pattern.
-__device__ __forceinline__ u4_t stream_load(const u4_t* p) { return *p; }
+// K/V tiles are read exactly once per step.  Value loads are non-temporal:
+// each instruction reads 1 KiB contiguous, and on gfx950 that measured ~10 %
+// faster than plain loads.  Key loads stay plain: an instruction covers 16 rows
+// x 64 bytes, half of each 128-byte line, and non-temporal loads of partial
+// lines measured slower (the line is fetched again by the second half).
+__device__ __forceinline__ u4_t stream_load(const u4_t* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ u4_t plain_load(const u4_t* p) { return *p; }
 
 // Stored K/V element formats.  A (layer, K|V, KV head) tile is 16 rows of 128
 // elements; a block holds, per layer, 8 key tiles then 8 value tiles.
@@ -111,19 +116,29 @@ struct BlockRegs {
 template <class F>
 constexpr int tile_bytes() { return 16 * kHeadDim * F::kElemBytes; }
 
+// First of the 8 elements of a 128-element row that lane group j feeds to QK
+// step i (key and query alike, so the 128-term dot product is covered once).
+// Key load i of lane (j, c) reads bytes [64 i + 16 j, 64 i + 16 j + 16) of row
+// c: each load instruction reads whole 64-byte row segments.
+template <class F>
+__device__ __forceinline__ int qk_elem(int i, int j) {
+  if constexpr (F::kElemBytes == 2) return 32 * i + 8 * j;          // load i
+  else return 64 * (i >> 1) + 16 * j + 8 * (i & 1);                 // half i & 1 of load i >> 1
+}
+
 // Issues exactly 2 * F::kLoads 16-byte loads per lane: the key tile in the QK
-// operand layout (lane (j, c) takes elements [32 j, 32 j + 32) of row c) and
-// the value tile in plain order (load i covers bytes [1024 i, 1024 i + 1024)).
-// Always issuing the same number of loads on every path lets the compiler wait
-// for one ring slot precisely instead of draining every load in flight.
+// operand layout above and the value tile in plain order (load i covers bytes
+// [1024 i, 1024 i + 1024)).  Always issuing the same number of loads on every
+// path lets the compiler wait for one ring slot precisely instead of draining
+// every load in flight.
 template <class F>
 __device__ __forceinline__ void load_block(BlockRegs<F>& r, const uint8_t* base, int lane, int c,
                                            int j) {
-  const uint8_t* kp = base + c * (kHeadDim * F::kElemBytes) + j * (32 * F::kElemBytes);
+  const uint8_t* kp = base + c * (kHeadDim * F::kElemBytes) + j * 16;
   const uint8_t* vp = base + 8 * tile_bytes<F>() + lane * 16;
 #pragma unroll
   for (int i = 0; i < F::kLoads; ++i)
-    r.k[i] = stream_load(reinterpret_cast<const u4_t*>(kp + i * 16));
+    r.k[i] = plain_load(reinterpret_cast<const u4_t*>(kp + i * 64));
 #pragma unroll
   for (int i = 0; i < F::kLoads; ++i)
     r.v[i] = stream_load(reinterpret_cast<const u4_t*>(vp + i * 1024));
@@ -158,7 +173,7 @@ __device__ __forceinline__ void stage_values(const BlockRegs<F>& r, u4_t* vstage
   }
 }
 
-// QK operand i of one ring slot: 8 fp16 key elements [32 j + 8 i, 32 j + 8 i + 8).
+// QK operand i of one ring slot: 8 fp16 key elements from qk_elem(i, j) on.
 template <class F>
 __device__ __forceinline__ h8_t key_operand(const BlockRegs<F>& r, int i) {
   if constexpr (F::kElemBytes == 2) {
@@ -173,34 +188,29 @@ __device__ __forceinline__ h8_t key_operand(const BlockRegs<F>& r, int i) {
 
 // Blocks whose loads are in flight per wave: the ring slot being processed
 // plus kRing - 1 ahead (32 VGPRs per slot).  Deeper rings at lower occupancy
-// measured no faster on gfx950.
-constexpr int kWavesPerSimd = 3;
-// Waves per work-group (each takes one KV head).  Work-groups of 4 or 8 waves
-// reading neighbouring heads of the same blocks measured no faster than 1.
-constexpr int kWpw = 1;
-
+// measured no faster on gfx950.  One wave per work-group, one KV head each:
+// work-groups of 4 or 8 waves reading neighbouring heads measured no faster.
 template <class F>
-__global__ void __launch_bounds__(64 * kWpw, kWavesPerSimd) paged_decode_gqa(DecodeArgs a) {
+__global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_gqa(DecodeArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int SB = a.split_blocks;
-  const int wave = threadIdx.x >> 6;
+  // LDS layout (decode_lds_bytes): block ids, mass partials, value stage.
   int32_t* tbl = reinterpret_cast<int32_t*>(smem);                          // [SB] block ids
-  uint8_t* wave_lds = smem + (size_t)4 * SB + (size_t)wave * (32 * SB + kVStageBytes);
-  float* pi_lds = reinterpret_cast<float*>(wave_lds);                       // [8][SB]
-  u4_t* vstage = reinterpret_cast<u4_t*>(wave_lds + 32 * SB);               // 16 x 16 chunks of 16 B
+  float* pi_lds = reinterpret_cast<float*>(smem + (size_t)4 * SB);          // [8][SB]
+  u4_t* vstage = reinterpret_cast<u4_t*>(smem + (size_t)36 * SB);           // 16 x 16 chunks of 16 B
 
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;
   const int j = lane >> 4;
 
   uint32_t w = blockIdx.x;
-  const uint32_t lgg_count = (uint32_t)a.n_layers * (8u / kWpw);
+  const uint32_t lgg_count = (uint32_t)a.n_layers * 8u;
   const int lgg = (int)(w % lgg_count);
   w /= lgg_count;
   const int split = (int)(w % (uint32_t)a.n_splits);
   const int s = (int)(w / (uint32_t)a.n_splits);
-  const int lr = lgg / (8 / kWpw);
-  const int g = (lgg % (8 / kWpw)) * kWpw + wave;
+  const int lr = lgg >> 3;
+  const int g = lgg & 7;
   const int layer = a.layer_begin + lr;
 
   int r0 = 0;
@@ -214,17 +224,17 @@ __global__ void __launch_bounds__(64 * kWpw, kWavesPerSimd) paged_decode_gqa(Dec
 
   // The split's block ids go to LDS once, so that no later block-id read waits
   // on the vector-memory counter behind the in-flight K/V loads.
-  for (int i = threadIdx.x; i < b1 - b0; i += 64 * kWpw)
+  for (int i = threadIdx.x; i < b1 - b0; i += 64)
     tbl[i] = a.table[(size_t)s * a.max_nb + b0 + i];
   __syncthreads();
 
   // B operand of QK: queries of the group, rows 8..15 zero.
   h8_t qb[4];
   if (c < kGroup) {
-    const h8_t* qp = reinterpret_cast<const h8_t*>(
-        a.q + ((((size_t)s * a.num_layers + layer) * kQHeads + kGroup * g + c) * kHeadDim) + 32 * j);
+    const uint16_t* qp =
+        a.q + ((((size_t)s * a.num_layers + layer) * kQHeads + kGroup * g + c) * kHeadDim);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) qb[i] = qp[i];
+    for (int i = 0; i < 4; ++i) qb[i] = *reinterpret_cast<const h8_t*>(qp + qk_elem<F>(i, j));
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) qb[i] = h8_t{0, 0, 0, 0, 0, 0, 0, 0};
@@ -850,16 +860,13 @@ __global__ void __launch_bounds__(256) stream_copy(const u4_t* __restrict__ src,
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_decode(const DecodeArgs& a, int batch, hipStream_t stream) {
-  const uint64_t wgs = (uint64_t)batch * a.n_splits * a.n_layers * (8 / kWpw);
-  const size_t lds =
-      (size_t)4 * a.split_blocks + (size_t)kWpw * (32 * a.split_blocks + kVStageBytes);
+  const uint64_t wgs = (uint64_t)batch * a.n_splits * a.n_layers * 8u;
+  const size_t lds = decode_lds_bytes(a.split_blocks);
   if (lds > kMaxDecodeLds) return hipErrorInvalidValue;
   if (a.kv_e4m3)
-    hipLaunchKernelGGL(paged_decode_gqa<KvE4M3>, dim3((uint32_t)wgs), dim3(64 * kWpw), lds,
-                       stream, a);
+    hipLaunchKernelGGL(paged_decode_gqa<KvE4M3>, dim3((uint32_t)wgs), dim3(64), lds, stream, a);
   else
-    hipLaunchKernelGGL(paged_decode_gqa<KvF16>, dim3((uint32_t)wgs), dim3(64 * kWpw), lds,
-                       stream, a);
+    hipLaunchKernelGGL(paged_decode_gqa<KvF16>, dim3((uint32_t)wgs), dim3(64), lds, stream, a);
   return hipGetLastError();
 }
 

@@ -22,14 +22,15 @@ class DecodeSession:
         self.shape = api.shape(L)
         dev = m.pool.device
         B = m.batch
+        eb = 1 if m.workload.kv_format == "e4m3" else 2
         self.split_blocks = api.decode_split_blocks(self.shape, B, m.max_blocks, self.layer_begin,
-                                                    self.layer_end, split_blocks)
+                                                    self.layer_end, split_blocks, eb)
         if self.split_blocks == 0:
             raise ValueError(f"invalid split_blocks {split_blocks}")
         self.out = torch.zeros((B, L, 64, 128), dtype=torch.float16, device=dev)
         self.mass = torch.zeros(max(m.total_blocks, 1), dtype=torch.float32, device=dev)
         ws_bytes = api.decode_workspace_bytes(self.shape, B, m.max_blocks, m.total_blocks,
-                                              self.layer_begin, self.layer_end, self.split_blocks)
+                                              self.layer_begin, self.layer_end, self.split_blocks, eb)
         self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         api.workspace_init(self.ws, stream=stream)
         self.meta = torch.empty((max(m.total_blocks, 1), 64), dtype=torch.uint8, device=dev)
