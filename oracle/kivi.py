@@ -197,11 +197,13 @@ def _gather16(pool, table_row, n: int, layer: int):
 #   value tile: entry (j, c) holds channel group c of each 16-channel tile;
 #               set S holds tiles k = 2 S and 2 S + 1; code m = 4 (k % 2) + r
 #               is token 4 j + r of channel 16 k + c.
-# Bytes [512, 768): group parameters as (scale, zero) fp16 pairs.
+# Bytes [512, 768): group parameters, fp16, 128 bytes of scales then 128
+# bytes of zero points.
 #   key tile:   64 channels: channels 0..63 in the even block of a 32-token
-#               pair, 64..127 in the odd block; pair for channel d at
-#               512 + 4 (d % 64).
-#   value tile: token t, channel group g at 512 + 16 t + 4 g.
+#               pair, 64..127 in the odd block; channel d's scale at
+#               512 + 2 (d % 64), its zero point at 640 + 2 (d % 64).
+#   value tile: token t, channel group g: scale at 512 + 2 (16 g + t), zero
+#               point at 640 + 2 (16 g + t).
 # ---------------------------------------------------------------------------
 
 def _set_base(S):
@@ -257,17 +259,16 @@ def pack_k_tile(codes16, scale, zero, odd: bool) -> bytes:
     t, d = k_entry_layout()
     raw = pack_codes(np.asarray(codes16)[t, d])
     half = slice(64, 128) if odd else slice(0, 64)
-    meta = np.stack([np.asarray(scale, np.float16)[half], np.asarray(zero, np.float16)[half]],
-                    axis=1)
-    return raw + meta.astype("<f2").tobytes()
+    return (raw + np.asarray(scale, np.float16)[half].astype("<f2").tobytes()
+            + np.asarray(zero, np.float16)[half].astype("<f2").tobytes())
 
 
 def pack_v_tile(codes16, scale, zero) -> bytes:
     """codes16: uint8 [16][128]; scale, zero: fp16 [16][4] (token, channel group)."""
     t, d = v_entry_layout()
     raw = pack_codes(np.asarray(codes16)[t, d])
-    meta = np.stack([np.asarray(scale, np.float16), np.asarray(zero, np.float16)], axis=2)
-    return raw + meta.astype("<f2").tobytes()
+    planes = [np.asarray(a, np.float16).T.astype("<f2").tobytes() for a in (scale, zero)]
+    return raw + planes[0] + planes[1]
 
 
 def unpack_k_tile(raw):
@@ -276,8 +277,8 @@ def unpack_k_tile(raw):
     t, d = k_entry_layout()
     codes = np.zeros((16, 128), dtype=np.uint8)
     codes[t, d] = unpack_codes(raw[:512])
-    meta = np.frombuffer(raw[512:768], dtype="<f2").reshape(64, 2)
-    return codes, meta[:, 0].astype(np.float16), meta[:, 1].astype(np.float16)
+    meta = np.frombuffer(raw[512:768], dtype="<f2").reshape(2, 64)
+    return codes, meta[0].astype(np.float16), meta[1].astype(np.float16)
 
 
 def unpack_v_tile(raw):
@@ -286,8 +287,8 @@ def unpack_v_tile(raw):
     t, d = v_entry_layout()
     codes = np.zeros((16, 128), dtype=np.uint8)
     codes[t, d] = unpack_codes(raw[:512])
-    meta = np.frombuffer(raw[512:768], dtype="<f2").reshape(16, 4, 2)
-    return codes, meta[..., 0].astype(np.float16), meta[..., 1].astype(np.float16)
+    meta = np.frombuffer(raw[512:768], dtype="<f2").reshape(2, 4, 16)
+    return codes, meta[0].T.astype(np.float16), meta[1].T.astype(np.float16)
 
 
 def pack_pair(K32, V32):

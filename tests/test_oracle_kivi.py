@@ -148,15 +148,20 @@ def test_packed_format_hand_placed_bits():
     raw = KV.pack_v_tile(codes, np.zeros((16, 4), np.float16), np.zeros((16, 4), np.float16))
     b = np.frombuffer(raw[:512], np.uint8)
     assert b[8 * 38 + 4] == 0x20 and b.sum() == 0x20
-    # parameters: key channel 70 of an odd block at 512 + 4 * 6; value (9, 2) at 512 + 16*9 + 8
+    # parameters: key channel 70 of an odd block: scale at 512 + 2 * 6, zero at
+    # 640 + 2 * 6; value token 9, group 2: scale at 512 + 2 * 41, zero at 640 + 82
     s = np.zeros(128, np.float16)
-    s[70] = 1.5
-    raw = KV.pack_k_tile(np.zeros((16, 128), np.uint8), s, np.zeros(128, np.float16), True)
-    assert np.frombuffer(raw[512 + 24:512 + 26], "<f2")[0] == 1.5
+    z = np.zeros(128, np.float16)
+    s[70], z[70] = 1.5, -0.25
+    raw = KV.pack_k_tile(np.zeros((16, 128), np.uint8), s, z, True)
+    meta = np.frombuffer(raw[512:], "<f2")
+    assert meta[6] == 1.5 and meta[64 + 6] == -0.25 and np.count_nonzero(meta) == 2
     vs = np.zeros((16, 4), np.float16)
-    vs[9, 2] = -2.0
-    raw = KV.pack_v_tile(np.zeros((16, 128), np.uint8), vs, np.zeros((16, 4), np.float16))
-    assert np.frombuffer(raw[512 + 152:512 + 154], "<f2")[0] == -2.0
+    vz = np.zeros((16, 4), np.float16)
+    vs[9, 2], vz[9, 2] = -2.0, 3.0
+    raw = KV.pack_v_tile(np.zeros((16, 128), np.uint8), vs, vz)
+    meta = np.frombuffer(raw[512:], "<f2")
+    assert meta[41] == -2.0 and meta[64 + 41] == 3.0 and np.count_nonzero(meta) == 2
 
 
 def test_pack_unpack_round_trip_and_layout_is_a_bijection():
