@@ -37,7 +37,7 @@ def _parse():
     ap.add_argument("--steps", type=int, default=16)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="decode-80L-128K")
-    ap.add_argument("--kv-format", choices=("fp16", "e4m3"), default="fp16",
+    ap.add_argument("--kv-format", choices=("fp16", "e4m3", "kivi2"), default="fp16",
                     help="stored K/V format (e4m3: FP8 codes, half the bytes)")
     ap.add_argument("--alpha", type=float, default=None)
     ap.add_argument("--split-blocks", type=int, default=0)
@@ -129,6 +129,7 @@ def _cpu_baseline(m, alpha, budget_s):
 
     import workload as W
     from oracle import attention as OA
+    from oracle import kivi as KV
     from oracle import scoring as OS
 
     q = W.make_query(m, 0).cpu().numpy()
@@ -150,10 +151,15 @@ def _cpu_baseline(m, alpha, budget_s):
         copy_s += time.perf_counter() - tc
         for s in range(m.batch):
             tbl = np.arange(m.blocks[s])
-            _, ms = OA.decode_layer(q[s, layer], pool_l[s], tbl, m.lens[s], 0, scale,
-                                    m.workload.kv_format)
+            fmt = m.workload.kv_format
+            if fmt == "kivi2":
+                _, ms = KV.decode_layer(q[s, layer], pool_l[s], tbl, m.lens[s], 0, scale)
+                nq = KV.quant_boundary(m.lens[s])
+                kv_bytes += 8 * (nq // 16 * 2 * KV.TILE_BYTES + (m.lens[s] - nq) * 128 * 2 * 2)
+            else:
+                _, ms = OA.decode_layer(q[s, layer], pool_l[s], tbl, m.lens[s], 0, scale, fmt)
+                kv_bytes += m.lens[s] * 8 * 128 * 2 * (1 if fmt == "e4m3" else 2)
             masses[s] += ms
-            kv_bytes += m.lens[s] * 8 * 128 * 2 * (1 if m.workload.kv_format == "e4m3" else 2)
         layers_done += 1
         if time.perf_counter() - t0 - copy_s >= budget_s:
             break
@@ -197,6 +203,11 @@ def main():
     wl = W.WORKLOADS[args.workload]
     if args.kv_format == "e4m3":
         wl = W.as_e4m3(wl)
+    elif args.kv_format == "kivi2":
+        if args.append:
+            print("bench.py --append does not support --kv-format kivi2", file=sys.stderr)
+            sys.exit(2)
+        wl = W.as_kivi2(wl)
     alpha = args.alpha if args.alpha is not None else wl.alphas[0]
     extra = 0
     if args.append:
@@ -297,6 +308,10 @@ def main():
         mean_tokens = float(lens_at_start.sum()) + m.batch * (args.steps + 1) / 2.0
         kv_bytes = int(mean_tokens * m.num_layers * 8 * 128 * 2 * sess.kv_elem_bytes)
     unique_bytes = m.unique_blocks * 16 * m.num_layers * 8 * 128 * 2 * sess.kv_elem_bytes
+    fp16_bytes = sum(m.lens) * m.num_layers * 8 * 128 * 2 * 2
+    if args.kv_format == "kivi2":
+        resid = sum(m.lens) - int(sess.quant_lens_host.sum())
+        unique_bytes = (sess.kivi_blocks * 2 * 768 + resid * 128 * 2 * 2) * m.num_layers * 8
     t_step = total_ms / 1e3 / args.steps
     value = kv_bytes / t_step / 1e9
     dec_avg = sum(decode_ms) / len(decode_ms) / 1e3
@@ -327,7 +342,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp16" if args.kv_format == "fp16" else "e4m3 KV, fp16 compute",
+        "dtype": {"fp16": "fp16", "e4m3": "e4m3 KV, fp16 compute",
+                  "kivi2": "2-bit KIVI KV + fp16 residual, fp16/fp32 compute"}[args.kv_format],
         "data": "synthetic",
         "config": {
             "workload": wl.name,
@@ -345,6 +361,7 @@ def main():
         },
         "blocks_scored_per_s": round(m.total_blocks / t_step, 1),
         "tokens_attended_per_s": round(sum(m.lens) * m.num_layers / t_step, 1),
+        "fp16_equivalent_kv_gbps": round(fp16_bytes / t_step / 1e9, 2),
         "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
         "decode_kernel_ms": round(dec_avg * 1e3, 4),
         "decode_share_of_step": round(dec_avg / t_step, 4),
@@ -355,7 +372,7 @@ def main():
         "frac_of_copy_probe": round(value / probe["gbps"], 4) if probe else None,
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_decode_gqa",
+            "kernel": "paged_decode_kivi" if args.kv_format == "kivi2" else "paged_decode_gqa",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

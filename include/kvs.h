@@ -133,24 +133,32 @@ size_t kvs_block_bytes(const kvs_shape* shape);
  * priority, reserved1. */
 size_t kvs_meta_layout(size_t* offsets, int n);
 
+/* Stored K/V formats, one per decode entry point. */
+#define KVS_KV_FP16 0   /* kvs_decode_step: fp16 values */
+#define KVS_KV_E4M3 1   /* kvs_decode_step_e4m3: FP8 E4M3 codes */
+#define KVS_KV_KIVI2 2  /* kvs_decode_step_kivi: 2-bit KIVI blocks + fp16 residual */
+
 /* Blocks per split used for this problem when split_blocks == 0 is passed (a
- * power of two in [16, 1024], chosen from the sizes and the stored element
- * size: kv_elem_bytes 2 for kvs_decode_step's fp16 pool, 1 for
- * kvs_decode_step_e4m3's pool); otherwise split_blocks itself if valid.  0 if
- * any argument is invalid. */
-int32_t kvs_decode_split_blocks(const kvs_shape* shape, int32_t kv_elem_bytes, int32_t batch,
+ * power of two in [16, 1024], chosen from the sizes and the stored format
+ * kv_format, one of KVS_KV_*); otherwise split_blocks itself if valid (for
+ * KVS_KV_KIVI2 it must also be even).  0 if any argument is invalid. */
+int32_t kvs_decode_split_blocks(const kvs_shape* shape, int32_t kv_format, int32_t batch,
                                 int32_t max_blocks_per_seq, int32_t layer_begin,
                                 int32_t layer_end, int32_t split_blocks);
 
-/* Workspace bytes the decode entry point of this element size (2: fp16, 1:
- * E4M3) needs for these sizes (0 on invalid input).  The workspace holds a
- * 256-byte status header, the per-split softmax statistics and partial outputs,
- * and the per-(layer, head, block) mass partials: about
+/* Workspace bytes the decode entry point of format kv_format needs for these
+ * sizes (0 on invalid input).  The workspace holds a 256-byte status header,
+ * the per-split softmax statistics and partial outputs, and the
+ * per-(layer, head, block) mass partials: about
  * 4 x 64 x (layer_end - layer_begin) x total_blocks bytes. */
-size_t kvs_decode_workspace_bytes(const kvs_shape* shape, int32_t kv_elem_bytes, int32_t batch,
+size_t kvs_decode_workspace_bytes(const kvs_shape* shape, int32_t kv_format, int32_t batch,
                                   int32_t max_blocks_per_seq, int64_t total_blocks,
                                   int32_t layer_begin, int32_t layer_end,
                                   int32_t split_blocks);
+
+/* Bytes of one quantised (KIVI 2-bit) block: num_layers x 2 x 8 x 768, 3/16
+ * of an fp16 block.  0 if shape is NULL. */
+size_t kvs_kivi_block_bytes(const kvs_shape* shape);
 
 /* Workspace bytes kvs_score_update needs (status header + per-chunk maxima). */
 size_t kvs_score_workspace_bytes(int32_t batch, int32_t max_blocks_per_seq);
@@ -242,6 +250,74 @@ int kvs_decode_step_e4m3(const kvs_shape* shape,
                          const void* kv_pool, int64_t pool_blocks,
                          const int32_t* block_table, int32_t max_blocks_per_seq,
                          const int32_t* seq_lens, const int32_t* meta_offsets,
+                         int32_t batch, int64_t total_blocks,
+                         int32_t layer_begin, int32_t layer_end,
+                         float scale,
+                         void* out, float* block_mass, int accumulate,
+                         int32_t split_blocks,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* ---- KIVI-style 2-bit KV (Fitting a Million Tokens, Sec. 02) --------------
+ * Asymmetric 2-bit quantisation in groups of 32 elements: zero point z = the
+ * group minimum, scale s = fp16(fp32(fp32(max - min) / 3)), code =
+ * clamp(rint(fp32(fp32(x - z) / s)), 0, 3) (code 0 when s == 0), read back as
+ * z + code * s.  Keys are grouped per channel over 32 consecutive tokens (two
+ * 16-token blocks), values per token over 32 consecutive channels.  The newest
+ * tokens stay fp16: tokens [0, quant_len) of a sequence are quantised, with
+ * quant_len a multiple of 32 (the pages' residual window of ~128 tokens gives
+ * quant_len = max(0, floor((n - 128) / 32) * 32); the caller chooses).
+ *
+ * Quantised block format, uint8 [kivi_blocks][num_layers][2][8][768]: per
+ * layer 8 key tiles then 8 value tiles of 768 bytes, one per KV head.  Bytes
+ * [0, 512) of a tile hold the block's 16 x 128 codes as 64 little-endian
+ * 8-byte entries; entry l = 16 j + c is two 32-bit words holding four sets
+ * S = 0..3 of 8 codes, set S in word S / 2, code m of the set at bits
+ * 4 m + 2 (S % 2).
+ *   key tile:   entry (j, c) is token c; set S, code m is channel 32 S + 8 j + m.
+ *   value tile: set S, code m is token 4 j + (m % 4) of channel
+ *               16 (2 S + m / 4) + c.
+ * Bytes [512, 768): 64 fp16 scales then 64 fp16 zero points.
+ *   key tile:   the 32-token group of an even/odd block pair; channels 0..63
+ *               in the even block, 64..127 in the odd one, at index d % 64.
+ *   value tile: token t, channel group g at index 16 g + t.
+ * A 32-token pair is two blocks with logical indices 2 p and 2 p + 1; the
+ * two may be any physical blocks of the quantised pool. */
+
+/* Quantise 32-token pairs of fp16 blocks into quantised blocks.
+ *  kv_pool     fp16 pool as for kvs_decode_step (read only).
+ *  kivi_pool   quantised pool, uint8 [kivi_blocks][num_layers][2][8][768].
+ *  pairs       int32 [n_pairs][4], device: {fp16 block of tokens 0..15, fp16
+ *              block of tokens 16..31, destination block for tokens 0..15,
+ *              destination block for tokens 16..31}.  Pairs whose ids fall
+ *              outside the pools are skipped and raise KVS_DEV_BAD_BLOCK_ID.
+ *              Destination blocks of different pairs must differ.
+ *  workspace   >= 256 bytes with a status header zeroed by kvs_workspace_init.
+ * Every layer and KV head of each pair is quantised.  Inputs must be finite. */
+int kvs_kivi_quantize(const kvs_shape* shape,
+                      const void* kv_pool, int64_t pool_blocks,
+                      void* kivi_pool, int64_t kivi_blocks,
+                      const int32_t* pairs, int32_t n_pairs,
+                      void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* The decode step of kvs_decode_step over a KIVI cache: for sequence s, block
+ * table entries b < quant_lens[s] / 16 are ids in kivi_pool (quantised blocks,
+ * pairs 2p, 2p + 1 holding one 32-token key group), and entries from
+ * quant_lens[s] / 16 on are ids in kv_pool (fp16 residual blocks).
+ * quant_lens: int32 [batch], device; each a multiple of 32 in [0, seq_lens[s]],
+ * else the sequence is skipped and KVS_DEV_BAD_SEQ_LEN raised.  The result is
+ * attention over the read-back values z + code * s of the quantised tokens and
+ * the fp16 values of the rest.  split_blocks must be 0 or even.  Workspace:
+ * kvs_decode_workspace_bytes(..., KVS_KV_KIVI2, ...).  Other arguments, outputs
+ * and rules as kvs_decode_step. */
+int kvs_decode_step_kivi(const kvs_shape* shape,
+                         const void* q,
+                         const void* kv_pool, int64_t pool_blocks,
+                         const void* kivi_pool, int64_t kivi_blocks,
+                         const int32_t* block_table, int32_t max_blocks_per_seq,
+                         const int32_t* seq_lens, const int32_t* quant_lens,
+                         const int32_t* meta_offsets,
                          int32_t batch, int64_t total_blocks,
                          int32_t layer_begin, int32_t layer_end,
                          float scale,

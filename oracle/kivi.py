@@ -145,6 +145,22 @@ def kivi_kv(K, V, n: int):
     return Kh, Vh
 
 
+def decode_layer(q_sl, pool, table_row, n: int, layer: int, scale: float):
+    """All 64 query heads of one (sequence, layer) over its KIVI cache.
+
+    Returns out [64][D] fp64 and the block mass of this layer [nb] fp64.
+    """
+    K16, V16 = _gather16(pool, table_row, n, layer)
+    out = np.empty((q_sl.shape[0], HEAD_DIM), dtype=np.float64)
+    mass = np.zeros(-(-n // BLOCK_TOKENS), dtype=np.float64)
+    for g in range(8):
+        Kh, Vh = kivi_kv(K16[g], V16[g], n)
+        for h in range(8 * g, 8 * g + 8):
+            out[h], p = OA.attend_head(q_sl[h], Kh, Vh, scale)
+            mass += OA.block_sums(p, n)
+    return out, mass
+
+
 def decode_step(q, pool, block_table, seq_lens, scale: float, layer_begin: int = 0,
                 layer_end=None):
     """One decode step over KIVI caches built from an fp16 pool.
@@ -164,12 +180,8 @@ def decode_step(q, pool, block_table, seq_lens, scale: float, layer_begin: int =
         nb = -(-n // BLOCK_TOKENS)
         mass = np.zeros(nb, dtype=np.float64)
         for layer in range(layer_begin, layer_end):
-            K16, V16 = _gather16(pool, block_table[s], n, layer)
-            for g in range(8):
-                Kh, Vh = kivi_kv(K16[g], V16[g], n)
-                for h in range(8 * g, 8 * g + 8):
-                    out[s, layer, h], p = OA.attend_head(q[s, layer, h], Kh, Vh, scale)
-                    mass += OA.block_sums(p, n)
+            out[s, layer], ms = decode_layer(q[s, layer], pool, block_table[s], n, layer, scale)
+            mass += ms
         masses.append(mass)
     return out, masses
 

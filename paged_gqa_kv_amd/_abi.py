@@ -24,6 +24,11 @@ KVS_DEV_BAD_OFFSETS = 0x4
 KVS_DEV_STALE_STEP = 0x8
 KVS_DEV_POOL_EXHAUSTED = 0x10
 
+KVS_KV_FP16 = 0
+KVS_KV_E4M3 = 1
+KVS_KV_KIVI2 = 2
+KV_FORMATS = {"fp16": KVS_KV_FP16, "e4m3": KVS_KV_E4M3, "kivi2": KVS_KV_KIVI2}
+
 KVS_NEVER_TOUCHED = 0xFFFF_FFFF_FFFF_FFFF
 KVS_UNCLASSIFIED = 0xFF
 KVS_FLAG_ANCHOR = 0x1
@@ -36,6 +41,7 @@ EXPORTS = (
     "kvs_meta_init", "kvs_score_update", "kvs_classify", "kvs_set_decode_events",
     "kvs_stream_probe", "kvs_evict_workspace_bytes", "kvs_evict_candidates",
     "kvs_decode_step_e4m3", "kvs_append_workspace_bytes", "kvs_append_kv",
+    "kvs_kivi_block_bytes", "kvs_kivi_quantize", "kvs_decode_step_kivi",
 )
 
 
@@ -83,6 +89,12 @@ _SIGS = {
     "kvs_decode_step_e4m3": (ctypes.c_int, [
         ctypes.POINTER(Shape), _vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _i64, _i32, _i32,
         ctypes.c_float, _vp, _vp, ctypes.c_int, _i32, _vp, _sz, _vp]),
+    "kvs_decode_step_kivi": (ctypes.c_int, [
+        ctypes.POINTER(Shape), _vp, _vp, _i64, _vp, _i64, _vp, _i32, _vp, _vp, _vp, _i32, _i64,
+        _i32, _i32, ctypes.c_float, _vp, _vp, ctypes.c_int, _i32, _vp, _sz, _vp]),
+    "kvs_kivi_block_bytes": (_sz, [ctypes.POINTER(Shape)]),
+    "kvs_kivi_quantize": (ctypes.c_int, [ctypes.POINTER(Shape), _vp, _i64, _vp, _i64, _vp, _i32,
+                                         _vp, _sz, _vp]),
     "kvs_meta_init": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i64, _i32, _vp]),
     "kvs_score_update": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i64, ctypes.c_uint64,
                                         ctypes.POINTER(Policy), ctypes.c_int, _vp, _sz, _vp]),

@@ -65,17 +65,26 @@ def meta_layout():
     return size, list(offs)
 
 
+def _fmt(kv_format) -> int:
+    return _abi.KV_FORMATS[kv_format] if isinstance(kv_format, str) else int(kv_format)
+
+
 def decode_split_blocks(shp: Shape, batch: int, max_blocks: int, layer_begin: int,
-                        layer_end: int, split_blocks: int = 0, kv_elem_bytes: int = 2) -> int:
-    return lib().kvs_decode_split_blocks(ctypes.byref(shp), kv_elem_bytes, batch, max_blocks,
+                        layer_end: int, split_blocks: int = 0, kv_format="fp16") -> int:
+    return lib().kvs_decode_split_blocks(ctypes.byref(shp), _fmt(kv_format), batch, max_blocks,
                                          layer_begin, layer_end, split_blocks)
 
 
 def decode_workspace_bytes(shp: Shape, batch: int, max_blocks: int, total_blocks: int,
                            layer_begin: int, layer_end: int, split_blocks: int = 0,
-                           kv_elem_bytes: int = 2) -> int:
-    return lib().kvs_decode_workspace_bytes(ctypes.byref(shp), kv_elem_bytes, batch, max_blocks,
-                                            total_blocks, layer_begin, layer_end, split_blocks)
+                           kv_format="fp16") -> int:
+    return lib().kvs_decode_workspace_bytes(ctypes.byref(shp), _fmt(kv_format), batch,
+                                            max_blocks, total_blocks, layer_begin, layer_end,
+                                            split_blocks)
+
+
+def kivi_block_bytes(shp: Shape) -> int:
+    return lib().kvs_kivi_block_bytes(ctypes.byref(shp))
 
 
 def score_workspace_bytes(batch: int, max_blocks: int) -> int:
@@ -134,6 +143,28 @@ def decode_step_e4m3(shp: Shape, q, kv_pool, pool_blocks: int, block_table, max_
                                      batch, total_blocks, layer_begin, layer_end, scale, _p(out),
                                      _p(block_mass), accumulate, split_blocks, _p(workspace),
                                      ws_bytes, _s(stream)))
+
+
+def decode_step_kivi(shp: Shape, q, kv_pool, pool_blocks: int, kivi_pool, kivi_blocks: int,
+                     block_table, max_blocks: int, seq_lens, quant_lens, meta_offsets, batch: int,
+                     total_blocks: int, layer_begin: int, layer_end: int, scale: float, out,
+                     block_mass, accumulate: int, split_blocks: int, workspace,
+                     workspace_bytes=None, stream=None) -> None:
+    ws_bytes = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    check(lib().kvs_decode_step_kivi(ctypes.byref(shp), _p(q), _p(kv_pool), pool_blocks,
+                                     _p(kivi_pool), kivi_blocks, _p(block_table), max_blocks,
+                                     _p(seq_lens), _p(quant_lens), _p(meta_offsets), batch,
+                                     total_blocks, layer_begin, layer_end, scale, _p(out),
+                                     _p(block_mass), accumulate, split_blocks, _p(workspace),
+                                     ws_bytes, _s(stream)))
+
+
+def kivi_quantize(shp: Shape, kv_pool, pool_blocks: int, kivi_pool, kivi_blocks: int, pairs,
+                  n_pairs: int, workspace, workspace_bytes=None, stream=None) -> None:
+    ws_bytes = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    check(lib().kvs_kivi_quantize(ctypes.byref(shp), _p(kv_pool), pool_blocks, _p(kivi_pool),
+                                  kivi_blocks, _p(pairs), n_pairs, _p(workspace), ws_bytes,
+                                  _s(stream)))
 
 
 def meta_init(meta, meta_offsets, seq_ids, batch: int, max_blocks: int, total_blocks: int,

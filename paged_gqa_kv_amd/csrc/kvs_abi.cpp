@@ -100,9 +100,21 @@ int check_counts(int32_t batch, int32_t max_blocks) {
 // The largest power-of-two split in [16, 1024] whose launch keeps enough
 // bytes in flight on the whole chip (wave count) and per compute unit (waves
 // that fit the LDS a split needs, at most kDecodeWavesPerSimd per SIMD).
-int32_t choose_split(int32_t batch, int32_t max_nb, int32_t n_layers, int32_t kv_elem_bytes) {
+// Reads one decode wave keeps in flight: two fp16 or E4M3 blocks (K and V tiles
+// of its KV head), or two 32-token quantised pairs (4 tiles of 768 bytes each).
+uint64_t wave_inflight_bytes(int32_t kv_format) {
+  switch (kv_format) {
+    case KVS_KV_FP16: return 2ull * 2ull * 4096ull;
+    case KVS_KV_E4M3: return 2ull * 2ull * 2048ull;
+    default: return 2ull * 4ull * (uint64_t)kvs::kKiviTileBytes;
+  }
+}
+
+bool format_valid(int32_t f) { return f == KVS_KV_FP16 || f == KVS_KV_E4M3 || f == KVS_KV_KIVI2; }
+
+int32_t choose_split(int32_t batch, int32_t max_nb, int32_t n_layers, int32_t kv_format) {
   const uint64_t streams = (uint64_t)batch * (uint64_t)n_layers * 8u;
-  const uint64_t wave_inflight = 2ull * 2ull * 16ull * 128ull * (uint64_t)kv_elem_bytes;
+  const uint64_t wave_inflight = wave_inflight_bytes(kv_format);
   for (int32_t cand = kMaxAutoSplit; cand >= 16; cand >>= 1) {
     const uint64_t waves = streams * (uint64_t)((max_nb + cand - 1) / cand);
     uint64_t per_cu = kvs::kLdsPerCu / kvs::decode_lds_bytes(cand);
@@ -123,17 +135,18 @@ struct DecodeLayout {
 };
 
 // Returns false on invalid sizes (no message).
-bool decode_layout(const kvs_shape* shape, int32_t kv_elem_bytes, int32_t batch, int32_t max_nb,
+bool decode_layout(const kvs_shape* shape, int32_t kv_format, int32_t batch, int32_t max_nb,
                    int64_t total_blocks, int32_t lb, int32_t le, int32_t split_blocks,
                    DecodeLayout* L) {
-  if (!shape || (kv_elem_bytes != 1 && kv_elem_bytes != 2) || batch < 1 || batch > kMaxBatch ||
-      max_nb < 1 || max_nb > kMaxBlocksPerSeq || total_blocks < 0 || total_blocks > INT32_MAX ||
-      lb < 0 || le <= lb || le > shape->num_layers)
+  if (!shape || !format_valid(kv_format) || batch < 1 || batch > kMaxBatch || max_nb < 1 ||
+      max_nb > kMaxBlocksPerSeq || total_blocks < 0 || total_blocks > INT32_MAX || lb < 0 ||
+      le <= lb || le > shape->num_layers)
     return false;
   const int32_t nl = le - lb;
   const int32_t sb =
-      split_blocks == 0 ? choose_split(batch, max_nb, nl, kv_elem_bytes) : split_blocks;
+      split_blocks == 0 ? choose_split(batch, max_nb, nl, kv_format) : split_blocks;
   if (!split_valid(sb)) return false;
+  if (kv_format == KVS_KV_KIVI2 && (sb & 1)) return false;
   const uint64_t nsplit = (uint64_t)(max_nb + sb - 1) / sb;
   const uint64_t stats = (uint64_t)batch * nl * 64u * nsplit;
   size_t off = kHeader;
@@ -200,21 +213,21 @@ size_t kvs_meta_layout(size_t* offsets, int n) {
   return sizeof(kvs_block_meta);
 }
 
-int32_t kvs_decode_split_blocks(const kvs_shape* shape, int32_t kv_elem_bytes, int32_t batch,
+int32_t kvs_decode_split_blocks(const kvs_shape* shape, int32_t kv_format, int32_t batch,
                                 int32_t max_blocks_per_seq, int32_t layer_begin, int32_t layer_end,
                                 int32_t split_blocks) {
   DecodeLayout L;
-  if (!decode_layout(shape, kv_elem_bytes, batch, max_blocks_per_seq, 0, layer_begin, layer_end,
+  if (!decode_layout(shape, kv_format, batch, max_blocks_per_seq, 0, layer_begin, layer_end,
                      split_blocks, &L))
     return 0;
   return L.split_blocks;
 }
 
-size_t kvs_decode_workspace_bytes(const kvs_shape* shape, int32_t kv_elem_bytes, int32_t batch,
+size_t kvs_decode_workspace_bytes(const kvs_shape* shape, int32_t kv_format, int32_t batch,
                                   int32_t max_blocks_per_seq, int64_t total_blocks,
                                   int32_t layer_begin, int32_t layer_end, int32_t split_blocks) {
   DecodeLayout L;
-  if (!decode_layout(shape, kv_elem_bytes, batch, max_blocks_per_seq, total_blocks, layer_begin,
+  if (!decode_layout(shape, kv_format, batch, max_blocks_per_seq, total_blocks, layer_begin,
                      layer_end, split_blocks, &L))
     return 0;
   return L.total;
@@ -276,9 +289,11 @@ int kvs_device_status(void* workspace, void* stream, uint32_t* bits) {
 
 namespace {
 
-int decode_step(bool kv_e4m3, const kvs_shape* shape, const void* q, const void* kv_pool,
-                int64_t pool_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
-                const int32_t* seq_lens, const int32_t* meta_offsets, int32_t batch,
+int decode_step(int32_t kv_format, const kvs_shape* shape, const void* q, const void* kv_pool,
+                int64_t pool_blocks, const void* kivi_pool, int64_t kivi_blocks,
+                const int32_t* block_table, int32_t max_blocks_per_seq,
+                const int32_t* seq_lens, const int32_t* quant_lens,
+                const int32_t* meta_offsets, int32_t batch,
                 int64_t total_blocks, int32_t layer_begin, int32_t layer_end, float scale,
                 void* out, float* block_mass, int accumulate, int32_t split_blocks,
                 void* workspace, size_t workspace_bytes, void* stream) {
@@ -300,6 +315,15 @@ int decode_step(bool kv_e4m3, const kvs_shape* shape, const void* q, const void*
   if (accumulate != 0 && accumulate != 1) return fail(KVS_E_RANGE, "accumulate must be 0 or 1");
   if (split_blocks != 0 && !split_valid(split_blocks))
     return fail(KVS_E_RANGE, "split_blocks %d not in [4, 1024]", split_blocks);
+  const bool kivi = kv_format == KVS_KV_KIVI2;
+  if (kivi) {
+    if (!kivi_pool || !quant_lens) return fail(KVS_E_NULL, "kivi_pool and quant_lens are required");
+    if (kivi_blocks < 1 || kivi_blocks > INT32_MAX)
+      return fail(KVS_E_RANGE, "kivi_blocks %lld out of range", (long long)kivi_blocks);
+    if (split_blocks & 1) return fail(KVS_E_RANGE, "split_blocks must be even for KIVI pairs");
+    if (!aligned(kivi_pool, 16) || !aligned(quant_lens, 4))
+      return fail(KVS_E_ALIGN, "kivi_pool must be 16-byte and quant_lens 4-byte aligned");
+  }
   if (!aligned(q, 16) || !aligned(kv_pool, 16) || !aligned(out, 16))
     return fail(KVS_E_ALIGN, "q, kv_pool and out must be 16-byte aligned");
   if (!aligned(block_mass, 4) || !aligned(block_table, 4) || !aligned(seq_lens, 4) ||
@@ -307,7 +331,7 @@ int decode_step(bool kv_e4m3, const kvs_shape* shape, const void* q, const void*
     return fail(KVS_E_ALIGN, "int32 / fp32 arrays must be 4-byte aligned");
   if (!aligned(workspace, kAlign)) return fail(KVS_E_ALIGN, "workspace must be 256-byte aligned");
   DecodeLayout L;
-  if (!decode_layout(shape, kv_e4m3 ? 1 : 2, batch, max_blocks_per_seq, total_blocks, layer_begin,
+  if (!decode_layout(shape, kv_format, batch, max_blocks_per_seq, total_blocks, layer_begin,
                      layer_end, split_blocks, &L))
     return fail(KVS_E_RANGE, "inconsistent sizes");
   if (workspace_bytes < L.total)
@@ -339,7 +363,10 @@ int decode_step(bool kv_e4m3, const kvs_shape* shape, const void* q, const void*
   d.split_blocks = L.split_blocks;
   d.n_splits = L.n_splits;
   d.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  d.kv_e4m3 = kv_e4m3 ? 1 : 0;
+  d.kv_format = kv_format;
+  d.kivi = static_cast<const uint8_t*>(kivi_pool);
+  d.kivi_blocks = kivi ? kivi_blocks : 0;
+  d.quant_lens = kivi ? quant_lens : nullptr;
   d.ml = reinterpret_cast<float2*>(ws + L.ml);
   d.opart = reinterpret_cast<float*>(ws + L.opart);
   d.pi = reinterpret_cast<float*>(ws + L.pi);
@@ -405,8 +432,8 @@ int kvs_decode_step(const kvs_shape* shape, const void* q, const void* kv_pool, 
                     int32_t layer_begin, int32_t layer_end, float scale, void* out,
                     float* block_mass, int accumulate, int32_t split_blocks, void* workspace,
                     size_t workspace_bytes, void* stream) {
-  return decode_step(false, shape, q, kv_pool, pool_blocks, block_table, max_blocks_per_seq,
-                     seq_lens, meta_offsets, batch, total_blocks, layer_begin, layer_end, scale,
+  return decode_step(KVS_KV_FP16, shape, q, kv_pool, pool_blocks, nullptr, 0, block_table,
+                     max_blocks_per_seq, seq_lens, nullptr, meta_offsets, batch, total_blocks, layer_begin, layer_end, scale,
                      out, block_mass, accumulate, split_blocks, workspace, workspace_bytes, stream);
 }
 
@@ -417,9 +444,59 @@ int kvs_decode_step_e4m3(const kvs_shape* shape, const void* q, const void* kv_p
                          int32_t layer_begin, int32_t layer_end, float scale, void* out,
                          float* block_mass, int accumulate, int32_t split_blocks, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  return decode_step(true, shape, q, kv_pool, pool_blocks, block_table, max_blocks_per_seq,
-                     seq_lens, meta_offsets, batch, total_blocks, layer_begin, layer_end, scale,
-                     out, block_mass, accumulate, split_blocks, workspace, workspace_bytes, stream);
+  return decode_step(KVS_KV_E4M3, shape, q, kv_pool, pool_blocks, nullptr, 0, block_table,
+                     max_blocks_per_seq, seq_lens, nullptr, meta_offsets, batch, total_blocks,
+                     layer_begin, layer_end, scale, out, block_mass, accumulate, split_blocks,
+                     workspace, workspace_bytes, stream);
+}
+
+int kvs_decode_step_kivi(const kvs_shape* shape, const void* q, const void* kv_pool,
+                         int64_t pool_blocks, const void* kivi_pool, int64_t kivi_blocks,
+                         const int32_t* block_table, int32_t max_blocks_per_seq,
+                         const int32_t* seq_lens, const int32_t* quant_lens,
+                         const int32_t* meta_offsets, int32_t batch, int64_t total_blocks,
+                         int32_t layer_begin, int32_t layer_end, float scale, void* out,
+                         float* block_mass, int accumulate, int32_t split_blocks, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return decode_step(KVS_KV_KIVI2, shape, q, kv_pool, pool_blocks, kivi_pool, kivi_blocks,
+                     block_table, max_blocks_per_seq, seq_lens, quant_lens, meta_offsets, batch,
+                     total_blocks, layer_begin, layer_end, scale, out, block_mass, accumulate,
+                     split_blocks, workspace, workspace_bytes, stream);
+}
+
+size_t kvs_kivi_block_bytes(const kvs_shape* shape) {
+  if (!shape) return 0;
+  return (size_t)shape->num_layers * 2u * 8u * (size_t)kvs::kKiviTileBytes;
+}
+
+int kvs_kivi_quantize(const kvs_shape* shape, const void* kv_pool, int64_t pool_blocks,
+                      void* kivi_pool, int64_t kivi_blocks, const int32_t* pairs, int32_t n_pairs,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!kv_pool || !kivi_pool || !pairs || !workspace)
+    return fail(KVS_E_NULL, "kv_pool, kivi_pool, pairs and workspace must be non-NULL");
+  if (n_pairs < 0) return fail(KVS_E_RANGE, "n_pairs %d < 0", n_pairs);
+  if (pool_blocks < 1 || pool_blocks > INT32_MAX || kivi_blocks < 1 || kivi_blocks > INT32_MAX)
+    return fail(KVS_E_RANGE, "pool sizes out of range");
+  if (!aligned(kv_pool, 16) || !aligned(kivi_pool, 16) || !aligned(pairs, 4))
+    return fail(KVS_E_ALIGN, "pools must be 16-byte aligned, pairs 4-byte aligned");
+  if (!aligned(workspace, kAlign)) return fail(KVS_E_ALIGN, "workspace must be 256-byte aligned");
+  if (workspace_bytes < kHeader)
+    return fail(KVS_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, kHeader);
+  if (n_pairs == 0) return ok();
+  kvs::KiviQuantArgs a{};
+  a.pool = static_cast<const uint8_t*>(kv_pool);
+  a.kivi = static_cast<uint8_t*>(kivi_pool);
+  a.pairs = pairs;
+  a.pool_blocks = pool_blocks;
+  a.kivi_blocks = kivi_blocks;
+  a.num_layers = shape->num_layers;
+  a.n_pairs = n_pairs;
+  a.status = static_cast<uint32_t*>(workspace);
+  hipError_t e = kvs::launch_kivi_quantize(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "kivi_quantize launch");
+  return ok();
 }
 
 int kvs_meta_init(kvs_block_meta* meta, const int32_t* meta_offsets, const uint64_t* seq_ids,

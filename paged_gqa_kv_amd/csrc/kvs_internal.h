@@ -35,7 +35,10 @@ struct DecodeArgs {
   int32_t split_blocks;
   int32_t n_splits;
   float scale_log2;         // softmax scale * log2(e)
-  int32_t kv_e4m3;          // 0: pool holds fp16 values; 1: FP8 E4M3 codes
+  int32_t kv_format;        // KVS_KV_FP16, KVS_KV_E4M3 or KVS_KV_KIVI2
+  const uint8_t* kivi;      // KVS_KV_KIVI2: quantised pool [kivi_blocks][num_layers][2][8][768]
+  int64_t kivi_blocks;
+  const int32_t* quant_lens;  // KVS_KV_KIVI2: [B] quantised tokens per sequence
   float2* ml;               // [B][n_layers][64][n_splits]: (running max, sum), base 2
   float* opart;             // [B][n_layers][64][n_splits][128]
   float* pi;                // [n_layers][64][total_blocks]
@@ -147,7 +150,21 @@ struct MetaInitArgs {
   uint32_t* status;         // may be a scratch word; init reports nothing
 };
 
+constexpr int kKiviTileBytes = 768;     // (layer, K|V, KV head) tile of a quantised block
+
+struct KiviQuantArgs {
+  const uint8_t* pool;      // fp16 [P][num_layers][2][8][16][128]
+  uint8_t* kivi;            // [kivi_blocks][num_layers][2][8][768]
+  const int32_t* pairs;     // [n_pairs][4]
+  int64_t pool_blocks;
+  int64_t kivi_blocks;
+  int32_t num_layers;
+  int32_t n_pairs;
+  uint32_t* status;
+};
+
 hipError_t launch_decode(const DecodeArgs& a, int batch, hipStream_t stream);
+hipError_t launch_kivi_quantize(const KiviQuantArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int batch, hipStream_t stream);
 hipError_t launch_mass(const MassArgs& a, int batch, hipStream_t stream);
 hipError_t launch_score(const ScoreArgs& a, int batch, hipStream_t stream);

@@ -1,14 +1,25 @@
 """Device-memory plumbing around the C ABI for one materialised workload.
 
 Allocates (with torch) the output, block-mass, record and workspace buffers a
-decode + scoring step needs, and calls the library.  No arithmetic here.
+decode + scoring step needs, and calls the library.  No arithmetic here; for
+a KIVI cache it also decides which tokens are quantised (the residual-window
+rule) and which quantised blocks hold them.
 """
 from __future__ import annotations
 
 import numpy as np
 import torch
 
+import workload as W
+
 from . import api
+
+
+def kivi_quant_len(n: int) -> int:
+    """Quantised tokens of an n-token sequence under a KIVI cache: the newest
+    ~128 tokens stay fp16 and the boundary is snapped down to a whole 32-token
+    group (Fitting a Million Tokens, Sec. 02)."""
+    return max(0, (int(n) - 128) // 32 * 32)
 
 
 class DecodeSession:
@@ -22,15 +33,17 @@ class DecodeSession:
         self.shape = api.shape(L)
         dev = m.pool.device
         B = m.batch
-        eb = 1 if m.workload.kv_format == "e4m3" else 2
+        fmt = m.workload.kv_format
+        self.kv_format = fmt
         self.split_blocks = api.decode_split_blocks(self.shape, B, m.max_blocks, self.layer_begin,
-                                                    self.layer_end, split_blocks, eb)
+                                                    self.layer_end, split_blocks, fmt)
         if self.split_blocks == 0:
             raise ValueError(f"invalid split_blocks {split_blocks}")
         self.out = torch.zeros((B, L, 64, 128), dtype=torch.float16, device=dev)
         self.mass = torch.zeros(max(m.total_blocks, 1), dtype=torch.float32, device=dev)
         ws_bytes = api.decode_workspace_bytes(self.shape, B, m.max_blocks, m.total_blocks,
-                                              self.layer_begin, self.layer_end, self.split_blocks, eb)
+                                              self.layer_begin, self.layer_end, self.split_blocks,
+                                              fmt)
         self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         api.workspace_init(self.ws, stream=stream)
         self.meta = torch.empty((max(m.total_blocks, 1), 64), dtype=torch.uint8, device=dev)
@@ -39,6 +52,47 @@ class DecodeSession:
         api.workspace_init(self.score_ws, stream=stream)
         self.anchor_blocks = anchor_blocks
         self.reset_meta()
+        if fmt == "kivi2":
+            self._build_kivi()
+
+    def _build_kivi(self):
+        """Quantise every sequence's tokens below its KIVI boundary with the
+        library's quantiser into a separate pool of quantised blocks, and point
+        those table entries at it.  Pairs of fp16 blocks shared between
+        sequences are quantised once."""
+        m = self.m
+        dev = m.pool.device
+        table = m.table_host
+        self.quant_lens_host = np.array([kivi_quant_len(n) for n in m.lens], dtype=np.int32)
+        pairs, where = [], {}
+        kivi_table = table.astype(np.int32).copy()
+        for s_ in range(m.batch):
+            for p in range(int(self.quant_lens_host[s_]) // 32):
+                src = (int(table[s_, 2 * p]), int(table[s_, 2 * p + 1]))
+                if src not in where:
+                    where[src] = len(pairs)
+                    pairs.append(src)
+                k = where[src]
+                kivi_table[s_, 2 * p:2 * p + 2] = (2 * k, 2 * k + 1)
+        n_blocks = max(2, 2 * len(pairs))
+        place = W.kivi_placement(m.workload, n_blocks)       # pair k -> blocks place[2k], place[2k+1]
+        for s_ in range(m.batch):
+            nqb = int(self.quant_lens_host[s_]) // 16
+            kivi_table[s_, :nqb] = place[kivi_table[s_, :nqb]]
+        spec = np.zeros((max(1, len(pairs)), 4), dtype=np.int32)
+        for k, (e, o) in enumerate(pairs):
+            spec[k] = (e, o, place[2 * k], place[2 * k + 1])
+        self.kivi_blocks = n_blocks
+        self.kivi_pool = torch.empty((n_blocks, api.kivi_block_bytes(self.shape)),
+                                     dtype=torch.uint8, device=dev)
+        self.kivi_table = torch.from_numpy(kivi_table).to(dev)
+        self.kivi_table_host = kivi_table
+        self.quant_lens = torch.from_numpy(self.quant_lens_host).to(dev)
+        self.kivi_pairs = torch.from_numpy(spec).to(dev)
+        self.kivi_ws = torch.empty(256, dtype=torch.uint8, device=dev)
+        api.workspace_init(self.kivi_ws, stream=self.stream)
+        api.kivi_quantize(self.shape, m.pool, m.pool_blocks, self.kivi_pool, n_blocks,
+                          self.kivi_pairs, len(pairs), self.kivi_ws, stream=self.stream)
 
     @property
     def kv_elem_bytes(self) -> int:
@@ -46,10 +100,14 @@ class DecodeSession:
 
     @property
     def kv_bytes_per_step(self) -> int:
-        """Logical KV bytes one decode step reads (keys and values, every token of
-        the lengths materialised; appends grow this by one token per sequence)."""
-        return (sum(self.m.lens) * (self.layer_end - self.layer_begin) * 8 * 128 * 2
-                * self.kv_elem_bytes)
+        """Stored KV bytes one decode step reads (keys and values, every token of
+        the lengths materialised; appends grow this by one token per sequence).
+        Under KIVI: 768-byte tiles for quantised blocks, fp16 for the rest."""
+        layers = self.layer_end - self.layer_begin
+        if self.kv_format == "kivi2":
+            nq = int(self.quant_lens_host.sum())
+            return (nq // 16 * 2 * 768 + (sum(self.m.lens) - nq) * 128 * 2 * 2) * layers * 8
+        return sum(self.m.lens) * layers * 8 * 128 * 2 * self.kv_elem_bytes
 
     def reset_meta(self):
         m = self.m
@@ -60,10 +118,17 @@ class DecodeSession:
         m = self.m
         lb = self.layer_begin if layer_begin is None else layer_begin
         le = self.layer_end if layer_end is None else layer_end
-        fn = api.decode_step_e4m3 if m.workload.kv_format == "e4m3" else api.decode_step
+        sc = api.DEFAULT_SCALE if scale is None else scale
+        if self.kv_format == "kivi2":
+            api.decode_step_kivi(self.shape, q, m.pool, m.pool_blocks, self.kivi_pool,
+                                 self.kivi_blocks, self.kivi_table, m.max_blocks, m.seq_lens,
+                                 self.quant_lens, m.meta_offsets, m.batch, m.total_blocks, lb, le,
+                                 sc, self.out, self.mass, accumulate, self.split_blocks, self.ws,
+                                 stream=self.stream)
+            return
+        fn = api.decode_step_e4m3 if self.kv_format == "e4m3" else api.decode_step
         fn(self.shape, q, m.pool, m.pool_blocks, m.block_table, m.max_blocks, m.seq_lens,
-           m.meta_offsets, m.batch, m.total_blocks, lb, le,
-           api.DEFAULT_SCALE if scale is None else scale, self.out, self.mass, accumulate,
+           m.meta_offsets, m.batch, m.total_blocks, lb, le, sc, self.out, self.mass, accumulate,
            self.split_blocks, self.ws, stream=self.stream)
 
     def score(self, step: int, pol, classify: int = 1):
@@ -81,6 +146,8 @@ class DecodeSession:
         """Append one token per sequence (updates the pool, table, seq_lens and
         records in place; the host copies of lengths are not touched)."""
         m = self.m
+        if self.kv_format == "kivi2":
+            raise NotImplementedError("append into a KIVI cache is not supported")
         if not hasattr(self, "free_stack"):
             dev = self.out.device
             self.free_stack = torch.from_numpy(m.free_stack.astype(np.int32)).to(dev)
@@ -118,6 +185,8 @@ class DecodeSession:
             bits |= api.device_status(self.evict_ws, self.stream)
         if hasattr(self, "append_ws"):
             bits |= api.device_status(self.append_ws, self.stream)
+        if hasattr(self, "kivi_ws"):
+            bits |= api.device_status(self.kivi_ws, self.stream)
         return bits
 
     def records(self):

@@ -57,21 +57,25 @@ def test_workspace_sizing():
     assert api.decode_workspace_bytes(shp, 1, 8192, 8192, 0, 81, 0) == 0
     assert api.decode_split_blocks(shp, 1, 8192, 0, 80, 3) == 0
     assert api.decode_split_blocks(shp, 1, 8192, 0, 80, 64) == 64
-    assert api.decode_split_blocks(shp, 1, 8192, 0, 80, 0, 3) == 0       # element size 1 or 2
-    assert api.decode_workspace_bytes(shp, 1, 8192, 8192, 0, 80, 0, 0) == 0
+    assert api.decode_split_blocks(shp, 1, 8192, 0, 80, 0, 3) == 0       # unknown format
+    assert api.decode_workspace_bytes(shp, 1, 8192, 8192, 0, 80, 0, -1) == 0
+    assert api.decode_split_blocks(shp, 1, 8192, 0, 80, 62, "kivi2") == 62
+    assert api.decode_split_blocks(shp, 1, 8192, 0, 80, 63, "kivi2") == 0   # pairs need even splits
+    assert api.decode_split_blocks(shp, 1, 8192, 0, 80, 63, "fp16") == 63
 
 
 def test_split_policy():
     """The library's split choice keeps about 16 MiB of reads in flight on the
     chip and 56 KiB per compute unit, preferring the longest split."""
-    def sb(batch, max_nb, layers, eb):
-        return api.decode_split_blocks(api.shape(layers), batch, max_nb, 0, layers, 0, eb)
-    assert sb(1, 8192, 80, 2) == 1024       # 128K context, fp16: 4 waves per CU suffice
-    assert sb(1, 8192, 80, 1) == 512        # E4M3 halves the bytes per wave: 7 waves per CU
-    assert sb(1, 65536, 32, 2) == 1024
-    assert sb(8, 512, 4, 2) == 128          # 1,024 waves x 16 KiB in flight
-    assert sb(8, 512, 4, 1) == 64           # 2,048 waves x 8 KiB
-    assert sb(1, 64, 1, 2) == 16            # too small to fill the chip: shortest split
+    def sb(batch, max_nb, layers, fmt):
+        return api.decode_split_blocks(api.shape(layers), batch, max_nb, 0, layers, 0, fmt)
+    assert sb(1, 8192, 80, "fp16") == 1024  # 128K context, fp16: 4 waves per CU suffice
+    assert sb(1, 8192, 80, "e4m3") == 512   # E4M3 halves the bytes per wave: 7 waves per CU
+    assert sb(1, 65536, 32, "fp16") == 1024
+    assert sb(8, 512, 4, "fp16") == 128     # 1,024 waves x 16 KiB in flight
+    assert sb(8, 512, 4, "e4m3") == 64      # 2,048 waves x 8 KiB
+    assert sb(1, 64, 1, "fp16") == 16       # too small to fill the chip: shortest split
+    assert sb(1, 8192, 80, "kivi2") == 256  # 6 KiB per wave: 12 waves per CU needed
     assert api.score_workspace_bytes(1, 65536) >= 256 + 4 * 256
     assert api.score_workspace_bytes(0, 10) == 0
 

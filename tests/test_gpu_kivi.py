@@ -1,0 +1,142 @@
+"""GPU parity of the KIVI 2-bit KV path (kvs_kivi_quantize, kvs_decode_step_kivi)
+against the oracle's quantisation, packed format and decode (oracle/kivi.py)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workload as W
+from oracle import kivi as KV
+from oracle import scoring as OS
+from paged_gqa_kv_amd import api
+from paged_gqa_kv_amd.session import DecodeSession, kivi_quant_len
+
+from . import parity as P
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+SCALE = 1.0 / math.sqrt(128.0)
+
+
+def _case(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def _kivi_session(lens, layers=2, split_blocks=0, seed=21, shared=0):
+    wl = W.as_kivi2(W.custom("kivi", layers, lens, seed=seed, spare_blocks=7,
+                             shared_prefix_tokens=shared))
+    m = W.materialise(wl, DEV)
+    sess = DecodeSession(m, split_blocks=split_blocks)
+    torch.cuda.synchronize()
+    assert [kivi_quant_len(n) for n in m.lens] == [KV.quant_boundary(n) for n in m.lens]
+    return m, sess
+
+
+def _check_quantised_bytes(m, sess, layers_to_check=None):
+    pool = m.pool.cpu().numpy()
+    kivi = sess.kivi_pool.cpu().numpy().reshape(sess.kivi_blocks, m.num_layers, 2, 8, KV.TILE_BYTES)
+    ktab = sess.kivi_table_host
+    layers = range(m.num_layers) if layers_to_check is None else layers_to_check
+    checked = 0
+    for s in range(m.batch):
+        for p in range(int(sess.quant_lens_host[s]) // 32):
+            e, o = m.table_host[s, 2 * p], m.table_host[s, 2 * p + 1]
+            de, do = ktab[s, 2 * p], ktab[s, 2 * p + 1]
+            for layer in layers:
+                for g in range(8):
+                    K32 = np.concatenate([pool[e, layer, 0, g], pool[o, layer, 0, g]])
+                    V32 = np.concatenate([pool[e, layer, 1, g], pool[o, layer, 1, g]])
+                    ke, ko, ve, vo = KV.pack_pair(K32, V32)
+                    assert kivi[de, layer, 0, g].tobytes() == ke, (s, p, layer, g, "K even")
+                    assert kivi[do, layer, 0, g].tobytes() == ko, (s, p, layer, g, "K odd")
+                    assert kivi[de, layer, 1, g].tobytes() == ve, (s, p, layer, g, "V even")
+                    assert kivi[do, layer, 1, g].tobytes() == vo, (s, p, layer, g, "V odd")
+                    checked += 1
+    return checked
+
+
+def test_quantiser_writes_the_oracles_bytes():
+    _case("kvs_kivi_quantize vs the oracle's packed tiles, 2 layers, lengths 200/33/500/1000")
+    m, sess = _kivi_session([200, 33, 500, 1000])
+    n = _check_quantised_bytes(m, sess)
+    assert n == 2 * 8 * sum(KV.quant_boundary(x) // 32 for x in m.lens)
+    assert sess.status() == 0
+
+
+def test_quantiser_edge_values():
+    _case("quantiser on degenerate and outlier groups: constant channels, one huge channel")
+    wl = W.as_kivi2(W.custom("kedge", 1, [288], seed=5, spare_blocks=3))
+    m = W.materialise(wl, DEV)
+    # constant key channel 3, huge key channel 77, constant value group of token 10
+    pids = torch.as_tensor(m.table_host[0, :18].astype(np.int64), device=DEV)
+    blk = m.pool[pids]                                    # [18][L][2][8][16][128]
+    blk[:, :, 0, :, :, 3] = 0.75
+    blk[:, :, 0, :, :, 77] *= 500.0
+    blk[0, :, 1, :, 10, 32:64] = -1.5
+    m.pool[pids] = blk
+    sess = DecodeSession(m)
+    torch.cuda.synchronize()
+    assert _check_quantised_bytes(m, sess) > 0
+
+
+@pytest.mark.parametrize("split_blocks", [0, 4, 16, 64])
+def test_kivi_decode_parity(split_blocks):
+    _case(f"KIVI decode vs oracle, 2 layers, ragged lengths, split_blocks={split_blocks}")
+    m, sess = _kivi_session([1, 17, 159, 160, 161, 200, 333, 1000, 2049], split_blocks=split_blocks)
+    pool = m.pool.cpu().numpy()
+    for step in range(2):
+        q = W.make_query(m, step)
+        sess.decode(q)
+        torch.cuda.synchronize()
+        out_ref, mass_ref = KV.decode_step(q.cpu().numpy(), pool, m.table_host, m.lens, SCALE)
+        w_out = P.check_out(sess.out, out_ref, range(m.num_layers))
+        w_mass = P.check_mass(sess.mass, mass_ref, m.meta_offsets.cpu().numpy())
+        print(f"  step {step}: worst output {w_out:.2e}, worst mass {w_mass:.2e}", flush=True)
+    assert sess.status() == 0
+
+
+def test_kivi_decode_shared_prefix_and_scoring():
+    _case("KIVI decode + scoring, shared 256-token prefix quantised once, 3 layers, 4 steps")
+    m, sess = _kivi_session([300, 640, 256, 1200], layers=3, shared=256, seed=4)
+    shared_pairs = sum(KV.quant_boundary(n) // 32 for n in m.lens)
+    assert int(sess.kivi_pairs.shape[0]) < shared_pairs          # shared pairs quantised once
+    _check_quantised_bytes(m, sess, layers_to_check=[1])
+    pool = m.pool.cpu().numpy()
+    pol = OS.Policy(alpha=0.15)
+    gpol = api.policy(0.15)
+    state = OS.init_state(m.blocks, m.seq_ids.cpu().numpy())
+    for step in range(4):
+        q = W.make_query(m, step)
+        sess.step(q, step, gpol)
+        torch.cuda.synchronize()
+        out_ref, mass_ref = KV.decode_step(q.cpu().numpy(), pool, m.table_host, m.lens, SCALE)
+        P.check_out(sess.out, out_ref, range(m.num_layers))
+        P.check_mass(sess.mass, mass_ref, m.meta_offsets.cpu().numpy())
+        state, stale = OS.score_update(state, mass_ref, step, pol)
+        assert not stale.any()
+        P.check_records(sess.records(), state, pol)
+    assert sess.status() == 0
+
+
+def test_kivi_bad_quant_len_skips_the_sequence():
+    _case("quant_lens not a multiple of 32 / beyond the length: status bit, zero output")
+    m, sess = _kivi_session([500, 400])
+    q = W.make_query(m, 0)
+    good = sess.quant_lens.clone()
+    for bad in (good[0] - 16, torch.tensor(512, dtype=torch.int32, device=DEV)):
+        sess.quant_lens[0] = bad
+        sess.decode(q)
+        torch.cuda.synchronize()
+        assert sess.status() & api._abi.KVS_DEV_BAD_SEQ_LEN
+        assert torch.count_nonzero(sess.out[0]) == 0
+        offs = m.meta_offsets.cpu().numpy()
+        assert torch.count_nonzero(sess.mass[offs[0]:offs[1]]) == 0
+        out_ref, mass_ref = KV.decode_step(q[1:].cpu().numpy(), m.pool.cpu().numpy(),
+                                           m.table_host[1:], m.lens[1:], SCALE)
+        P.check_out(sess.out[1:], out_ref, range(m.num_layers))
+    sess.quant_lens.copy_(good)
+    sess.decode(q)
+    torch.cuda.synchronize()
+    assert sess.status() == 0

@@ -13,6 +13,8 @@ from .recipe import (  # noqa: F401
     Materialised,
     WORKLOADS,
     as_e4m3,
+    as_kivi2,
+    kivi_placement,
     custom,
     materialise,
     make_query,

@@ -22,6 +22,10 @@ What is drawn (no step of the method is computed here):
   NaN code 0x7F) so that a stray read poisons the result.
 * kv_format "e4m3" stores the same drawn values rounded once to FP8 E4M3
   codes with no scale (Fitting a Million Tokens, Sec. 02).
+* kv_format "kivi2" keeps the fp16 values in the pool; the 2-bit KIVI cache
+  of the same section is built from them by the consumer (the library's
+  quantiser, or the oracle on the test side).  KIVI pool placement is a
+  seeded permutation (kivi_placement).
 * A shared prefix is expressed the paged way: the same physical ids appear
   in several tables and carry a reference count (KV cache offload blog,
   "Top row").  Shared blocks take only the block-0 boost; the recent-tail
@@ -122,6 +126,16 @@ def as_e4m3(wl: Workload) -> Workload:
     return dataclasses.replace(wl, name=wl.name + "-e4m3", kv_format="e4m3")
 
 
+def as_kivi2(wl: Workload) -> Workload:
+    """The same workload decoded through a KIVI 2-bit cache (fp16 pool as source)."""
+    return dataclasses.replace(wl, name=wl.name + "-kivi2", kv_format="kivi2")
+
+
+def kivi_placement(wl: Workload, n_blocks: int) -> np.ndarray:
+    """Seeded random physical ids 0..n_blocks-1 for quantised blocks."""
+    return np.random.default_rng([wl.seed, 2]).permutation(n_blocks).astype(np.int32)
+
+
 @dataclasses.dataclass
 class Materialised:
     workload: Workload
@@ -213,7 +227,7 @@ def materialise(wl: Workload, device="cpu", extra_blocks: int = 0) -> Materialis
                     dtype=torch.float32)
     u = u / u.norm(dim=-1, keepdim=True)
 
-    if wl.kv_format not in ("fp16", "e4m3"):
+    if wl.kv_format not in ("fp16", "e4m3", "kivi2"):
         raise ValueError(f"unknown KV format {wl.kv_format}")
     fp8 = wl.kv_format == "e4m3"
     pool = torch.empty((pool_n, L, 2, NUM_KV_HEADS, BLOCK_TOKENS, HEAD_DIM),
