@@ -514,6 +514,32 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
     m_run = m_new;
   };
 
+  // The same for a block whose 16 logits are all finite (m_new is finite, so
+  // no masked-out head needs guarding).
+  auto softmax_full = [&](const float (&sv)[4], int b, float (&pv)[4]) {
+    float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    bm = fmaxf(bm, xor_f(bm, 16));
+    bm = fmaxf(bm, xor_f(bm, 32));
+    const float m_new = fmaxf(m_run, bm);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_new);
+    const float ps = (pv[0] + pv[1]) + (pv[2] + pv[3]);
+    l_run = l_run * alpha + ps;
+    float bs = ps + xor_f(ps, 16);
+    bs += xor_f(bs, 32);
+    if (__ballot(c < kGroup && alpha != 1.f) != 0ull) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] *= alpha;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) zacc[k] *= alpha;
+      if (c < kGroup)
+        for (int idx = j; idx < b - b0; idx += 4) pi_lds[c * SB + idx] *= alpha;
+    }
+    if (c < kGroup && j == 0) pi_lds[c * SB + (b - b0)] = bs;
+    m_run = m_new;
+  };
+
   // ---- quantised blocks [b0, bq1), in pairs (b0 and nq / 16 are even)
   const int bq1 = min(b1, nq >> 4);
   if (bq1 > b0) {
@@ -533,8 +559,9 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
     // block 0 and are masked.
     auto load_pair = [&](u4_t (&r)[3], int be, bool* ok) {
       const int cl = min(be, bq1 - 2);
-      const int pe = tbl[cl - b0];
-      const int po = tbl[cl + 1 - b0];
+      // block ids are wave-uniform: scalar registers keep the address math off the VALU
+      const int pe = __builtin_amdgcn_readfirstlane(tbl[cl - b0]);
+      const int po = __builtin_amdgcn_readfirstlane(tbl[cl + 1 - b0]);
       const bool in = pe >= 0 && (int64_t)pe < a.kivi_blocks && po >= 0 &&
                       (int64_t)po < a.kivi_blocks;
       *ok = in && be < bq1;
@@ -565,10 +592,20 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
           *reinterpret_cast<u4_t*>(stage + 1024 * kk + 16 * lane) = ring[k][kk];
         load_pair(ring[k], be + 2 * kKiviRing, &ring_ok[k]);
         if (!active) continue;
+        if (!ok) {
+          // a pair with an id outside the pool contributes nothing
+          if (c < kGroup && j == 0) {
+            pi_lds[c * SB + (be - b0)] = 0.f;
+            pi_lds[c * SB + (be + 1 - b0)] = 0.f;
+          }
+          continue;
+        }
 
-        // key scales and zero points of the lane's channels, folded into q
+        // key scales of the lane's channels folded into q (exact hi + lo), and the
+        // zero-point term sum_d z[d] q[h][d] from MFMAs whose A rows all hold z:
+        // it lands in every token row, so it starts both blocks' accumulators.
         h8_t qhi[4], qlo[4];
-        float zq = 0.f;
+        f4_t zsacc = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint8_t* km = stage + (i >> 1) * kKiviTileBytes + 512 + 2 * (32 * (i & 1) + 8 * j);
@@ -576,18 +613,14 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
           const h8_t z8 = *reinterpret_cast<const h8_t*>(km + 128);
           qhi[i] = qb[i] * s8;
           qlo[i] = __builtin_elementwise_fma(qb[i], s8, -qhi[i]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            zq = dot2(h2_t{qb[i][2 * e], qb[i][2 * e + 1]}, h2_t{z8[2 * e], z8[2 * e + 1]}, zq);
+          zsacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(z8, qb[i], zsacc, 0, 0, 0);
         }
-        zq += xor_f(zq, 16);
-        zq += xor_f(zq, 32);
 
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
           const int b = be + hb;
           const u2_t kent = *reinterpret_cast<const u2_t*>(stage + hb * kKiviTileBytes + 8 * lane);
-          f4_t sacc = f4_t{0.f, 0.f, 0.f, 0.f};
+          f4_t sacc = zsacc;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const h8_t kc = codes_to_h8(code_set(kent, i));
@@ -596,9 +629,9 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
           }
           float sv[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sv[i] = ok ? (sacc[i] + zq) * a.scale_log2 : -INFINITY;
+          for (int i = 0; i < 4; ++i) sv[i] = sacc[i] * a.scale_log2;
           float pv[4];
-          softmax_block(sv, b, pv);
+          softmax_full(sv, b, pv);
 
           const uint8_t* vt = stage + (2 + hb) * kKiviTileBytes;
           const u2_t vent = *reinterpret_cast<const u2_t*>(vt + 8 * lane);
