@@ -217,3 +217,57 @@ def test_capacity_layout_host_side():
     used = set(m.table_host[m.table_host >= 0].tolist())
     assert used.isdisjoint(set(m.free_stack.tolist()))
     assert len(used) + m.free_stack.size == m.pool_blocks
+
+
+def _decode_kivi(kivi_pool=0x20000, kivi_blocks=4, quant_lens=0x30000, **over):
+    a = _decode_args(**over)
+    return api.decode_step_kivi(a["shp"], a["q"], a["kv_pool"], a["pool_blocks"], kivi_pool,
+                                kivi_blocks, a["block_table"], a["max_blocks"], a["seq_lens"],
+                                quant_lens, a["meta_offsets"], a["batch"], a["total_blocks"],
+                                a["layer_begin"], a["layer_end"], a["scale"], a["out"],
+                                a["block_mass"], a["accumulate"], a["split_blocks"],
+                                a["workspace"], a["workspace_bytes"], stream=0)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(kivi_pool=0), KVS_E_NULL),
+    (dict(quant_lens=0), KVS_E_NULL),
+    (dict(q=0), KVS_E_NULL),
+    (dict(kivi_blocks=0), KVS_E_RANGE),
+    (dict(kivi_blocks=1 << 31), KVS_E_RANGE),
+    (dict(split_blocks=5), KVS_E_RANGE),            # 32-token pairs need even splits
+    (dict(kivi_pool=0x20008), KVS_E_ALIGN),
+    (dict(quant_lens=0x30002), KVS_E_ALIGN),
+    (dict(), KVS_E_WORKSPACE),
+])
+def test_kivi_decode_rejects_before_launch(over, code):
+    with pytest.raises(KvsError) as e:
+        _decode_kivi(**over)
+    assert e.value.code == code
+
+
+def test_kivi_quantize_validation_and_sizes():
+    shp = api.shape(80)
+    assert api.kivi_block_bytes(shp) * 16 == api.block_bytes(shp) * 3   # 3 bits per element
+    good = dict(kv_pool=0x1000, pool_blocks=8, kivi_pool=0x2000, kivi_blocks=8, pairs=0x3000,
+                n_pairs=2, workspace=0x10000, workspace_bytes=256)
+    cases = [(dict(kv_pool=0), KVS_E_NULL), (dict(pairs=0), KVS_E_NULL),
+             (dict(n_pairs=-1), KVS_E_RANGE), (dict(kivi_blocks=0), KVS_E_RANGE),
+             (dict(pool_blocks=1 << 31), KVS_E_RANGE), (dict(kivi_pool=0x2004), KVS_E_ALIGN),
+             (dict(workspace=0x10004), KVS_E_ALIGN), (dict(workspace_bytes=255), KVS_E_WORKSPACE)]
+    for over, code in cases:
+        a = dict(good, **over)
+        with pytest.raises(KvsError) as e:
+            api.kivi_quantize(shp, a["kv_pool"], a["pool_blocks"], a["kivi_pool"],
+                              a["kivi_blocks"], a["pairs"], a["n_pairs"], a["workspace"],
+                              a["workspace_bytes"], stream=0)
+        assert e.value.code == code, over
+    # nothing to do: no launch, no error
+    api.kivi_quantize(shp, 0x1000, 8, 0x2000, 8, 0x3000, 0, 0x10000, 256, stream=0)
+
+
+def test_kivi_quant_len_rule_matches_the_oracle():
+    from oracle import kivi as KV
+    from paged_gqa_kv_amd.session import kivi_quant_len
+    for n in list(range(0, 400)) + [131072, 1048576]:
+        assert kivi_quant_len(n) == KV.quant_boundary(n)

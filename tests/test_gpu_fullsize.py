@@ -18,6 +18,7 @@ import torch
 
 import workload as W
 from oracle import attention as OA
+from oracle import kivi as KV
 from oracle import scoring as OS
 from paged_gqa_kv_amd import api
 from paged_gqa_kv_amd.session import DecodeSession
@@ -42,6 +43,8 @@ def _run(name, alpha, steps=2, rows=8, oracle_layers=1, seqs_for_layer_mass=None
     wl = W.WORKLOADS[name]
     if kv_format == "e4m3":
         wl = W.as_e4m3(wl)
+    elif kv_format == "kivi2":
+        wl = W.as_kivi2(wl)
     m = W.materialise(wl, DEV)
     torch.cuda.synchronize()
     L = m.num_layers
@@ -80,8 +83,12 @@ def _run(name, alpha, steps=2, rows=8, oracle_layers=1, seqs_for_layer_mass=None
         layer = int(rng.integers(L))
         h = int(rng.integers(64))
         host = _host_layer(m, s, layer)
-        K, V = OA.gather_layer(host, np.arange(m.blocks[s]), m.lens[s], 0, kv_head=h // 8,
-                               kv_format=kv_format)
+        if kv_format == "kivi2":
+            K16, V16 = KV._gather16(host, np.arange(m.blocks[s]), m.lens[s], 0)
+            K, V = KV.kivi_kv(K16[h // 8], V16[h // 8], m.lens[s])
+        else:
+            K, V = OA.gather_layer(host, np.arange(m.blocks[s]), m.lens[s], 0, kv_head=h // 8,
+                                   kv_format=kv_format)
         ref, _ = OA.attend_head(qh[s, layer, h], K, V, scale)
         e = np.abs(out[s, layer, h] - ref).max()
         lim = np.abs(ref).max()
@@ -104,8 +111,12 @@ def _run(name, alpha, steps=2, rows=8, oracle_layers=1, seqs_for_layer_mass=None
     for layer, gm in one_layer.items():
         for s in seqs:
             host = _host_layer(m, s, layer)
-            _, ref = OA.decode_layer(qh[s, layer], host, np.arange(m.blocks[s]), m.lens[s], 0,
-                                     scale, kv_format)
+            if kv_format == "kivi2":
+                _, ref = KV.decode_layer(qh[s, layer], host, np.arange(m.blocks[s]), m.lens[s],
+                                         0, scale)
+            else:
+                _, ref = OA.decode_layer(qh[s, layer], host, np.arange(m.blocks[s]), m.lens[s],
+                                         0, scale, kv_format)
             got = gm[offsets[s]:offsets[s + 1]]
             assert np.all(np.abs(got - ref) <= P.MASS_RTOL * ref + 1e-7 * ref.max()), (layer, s)
         print(f"  layer {layer}: single-layer block mass matches the oracle", flush=True)
@@ -136,3 +147,12 @@ def test_fullsize_128k_context_e4m3():
 
 def test_fullsize_1m_context_e4m3():
     _run("decode-32L-1M", 0.15, steps=2, rows=4, oracle_layers=1, kv_format="e4m3")
+
+
+def test_fullsize_128k_context_kivi2():
+    _run("decode-80L-128K", 0.05, steps=2, rows=6, oracle_layers=1, kv_format="kivi2")
+
+
+def test_fullsize_shared_prefix_batch_kivi2():
+    _run("decode-80L-32xMixed-shared2K", 0.15, steps=2, rows=6, oracle_layers=1,
+         seqs_for_layer_mass=[0, 13], kv_format="kivi2")
