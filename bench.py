@@ -79,10 +79,10 @@ class HipEvents:
         self.hip.hipEventDestroy(ctypes.c_void_p(ev))
 
 
-def _traffic(workload: str, split_blocks: int):
+def _traffic(kernel: str, workload: str, split_blocks: int):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary,
     if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"paged_decode_gqa_{workload}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -318,7 +318,8 @@ def main():
     achieved = kv_bytes / dec_avg / 1e9
     if achieved > HBM_PEAK_GBPS and unique_bytes == kv_bytes:
         raise RuntimeError(f"measured {achieved:.0f} GB/s exceeds the HBM peak: a timing bug")
-    traffic = _traffic(wl.name, sess.split_blocks)
+    kernel = "paged_decode_kivi" if args.kv_format == "kivi2" else "paged_decode_gqa"
+    traffic = _traffic(kernel, wl.name, sess.split_blocks)
     tiers = np.bincount(rec["tier"], minlength=3)[:3].tolist()
 
     probe = None
@@ -372,7 +373,7 @@ def main():
         "frac_of_copy_probe": round(value / probe["gbps"], 4) if probe else None,
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_decode_kivi" if args.kv_format == "kivi2" else "paged_decode_gqa",
+            "kernel": kernel,
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
