@@ -72,7 +72,9 @@ typedef enum {
 #define KVS_DEV_BAD_OFFSETS    0x4u  /* meta_offsets inconsistent with seq_lens / total_blocks */
 #define KVS_DEV_STALE_STEP     0x8u  /* step <= a record's touch timestamp: record left unchanged */
 #define KVS_DEV_POOL_EXHAUSTED 0x10u /* kvs_append_kv: no free block, table row full or no record
-                                        capacity for a sequence that needed a block: not appended */
+                                        capacity for a sequence that needed a block: not appended;
+                                        kvs_kivi_advance: no free quantised block (or no room on
+                                        the fp16 free stack): boundary not moved */
 
 /* Model head shape.  The kernels support num_q_heads 64, num_kv_heads 8,
  * head_dim 128, block_tokens 16 and any num_layers >= 1 (Visual Reference
@@ -300,6 +302,37 @@ int kvs_kivi_quantize(const kvs_shape* shape,
                       const int32_t* pairs, int32_t n_pairs,
                       void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/* Workspace bytes kvs_kivi_advance needs for `batch` sequences (status header,
+ * job list). */
+size_t kvs_kivi_advance_workspace_bytes(int32_t batch);
+
+/* Move KIVI quantisation boundaries forward after appends: the fp16 residual
+ * window is where keys wait until 32 tokens form a whole group (Fitting a
+ * Million Tokens, Sec. 02).  For each sequence s, in batch order, with
+ * seq_lens[s] - quant_lens[s] >= residual_tokens + 32: the fp16 blocks of
+ * logical blocks quant_lens[s] / 16 and + 1 (ids in kv_pool) are quantised
+ * into two blocks taken from the top of the KIVI free stack (the first such
+ * sequence takes kivi_free[top - 1] for its even block and kivi_free[top - 2]
+ * for its odd one, the next the two below); those table entries then hold the
+ * KIVI ids, quant_lens[s] grows by 32, and the two fp16 ids are pushed onto
+ * fp16_free (the stack kvs_append_kv pops), pair by pair in batch order.  At
+ * most one pair per sequence per call, so a call after every append keeps
+ * quant_lens[s] == max(0, floor((seq_lens[s] - residual_tokens) / 32) * 32).
+ * With too few KIVI ids, later sequences are left unchanged and
+ * KVS_DEV_POOL_EXHAUSTED is raised; bad lengths raise KVS_DEV_BAD_SEQ_LEN, ids
+ * outside the pools KVS_DEV_BAD_BLOCK_ID.  Tops and stacks are device int32.
+ * Calls that overlap on one stream order race. */
+int kvs_kivi_advance(const kvs_shape* shape,
+                     const void* kv_pool, int64_t pool_blocks,
+                     void* kivi_pool, int64_t kivi_blocks,
+                     int32_t* block_table, int32_t max_blocks_per_seq,
+                     const int32_t* seq_lens, int32_t* quant_lens, int32_t batch,
+                     int32_t residual_tokens,
+                     const int32_t* kivi_free, int32_t kivi_free_capacity, int32_t* kivi_free_top,
+                     int32_t* fp16_free, int32_t fp16_free_capacity, int32_t* fp16_free_top,
+                     void* workspace, size_t workspace_bytes,
+                     void* stream);
 
 /* The decode step of kvs_decode_step over a KIVI cache: for sequence s, block
  * table entries b < quant_lens[s] / 16 are ids in kivi_pool (quantised blocks,

@@ -42,6 +42,7 @@ EXPORTS = (
     "kvs_stream_probe", "kvs_evict_workspace_bytes", "kvs_evict_candidates",
     "kvs_decode_step_e4m3", "kvs_append_workspace_bytes", "kvs_append_kv",
     "kvs_kivi_block_bytes", "kvs_kivi_quantize", "kvs_decode_step_kivi",
+    "kvs_kivi_advance_workspace_bytes", "kvs_kivi_advance",
 )
 
 
@@ -93,6 +94,10 @@ _SIGS = {
         ctypes.POINTER(Shape), _vp, _vp, _i64, _vp, _i64, _vp, _i32, _vp, _vp, _vp, _i32, _i64,
         _i32, _i32, ctypes.c_float, _vp, _vp, ctypes.c_int, _i32, _vp, _sz, _vp]),
     "kvs_kivi_block_bytes": (_sz, [ctypes.POINTER(Shape)]),
+    "kvs_kivi_advance_workspace_bytes": (_sz, [_i32]),
+    "kvs_kivi_advance": (ctypes.c_int, [ctypes.POINTER(Shape), _vp, _i64, _vp, _i64, _vp, _i32,
+                                        _vp, _vp, _i32, _i32, _vp, _i32, _vp, _vp, _i32, _vp,
+                                        _vp, _sz, _vp]),
     "kvs_kivi_quantize": (ctypes.c_int, [ctypes.POINTER(Shape), _vp, _i64, _vp, _i64, _vp, _i32,
                                          _vp, _sz, _vp]),
     "kvs_meta_init": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i64, _i32, _vp]),

@@ -167,6 +167,24 @@ def kivi_quantize(shp: Shape, kv_pool, pool_blocks: int, kivi_pool, kivi_blocks:
                                   _s(stream)))
 
 
+def kivi_advance_workspace_bytes(batch: int) -> int:
+    return lib().kvs_kivi_advance_workspace_bytes(batch)
+
+
+def kivi_advance(shp: Shape, kv_pool, pool_blocks: int, kivi_pool, kivi_blocks: int, block_table,
+                 max_blocks: int, seq_lens, quant_lens, batch: int, residual_tokens: int,
+                 kivi_free, kivi_free_capacity: int, kivi_free_top, fp16_free,
+                 fp16_free_capacity: int, fp16_free_top, workspace, workspace_bytes=None,
+                 stream=None) -> None:
+    ws_bytes = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    check(lib().kvs_kivi_advance(ctypes.byref(shp), _p(kv_pool), pool_blocks, _p(kivi_pool),
+                                 kivi_blocks, _p(block_table), max_blocks, _p(seq_lens),
+                                 _p(quant_lens), batch, residual_tokens, _p(kivi_free),
+                                 kivi_free_capacity, _p(kivi_free_top), _p(fp16_free),
+                                 fp16_free_capacity, _p(fp16_free_top), _p(workspace), ws_bytes,
+                                 _s(stream)))
+
+
 def meta_init(meta, meta_offsets, seq_ids, batch: int, max_blocks: int, total_blocks: int,
               anchor_blocks: int = 1, stream=None) -> None:
     check(lib().kvs_meta_init(_p(meta), _p(meta_offsets), _p(seq_ids), batch, max_blocks,

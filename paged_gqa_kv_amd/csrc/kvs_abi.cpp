@@ -464,6 +464,72 @@ int kvs_decode_step_kivi(const kvs_shape* shape, const void* q, const void* kv_p
                      split_blocks, workspace, workspace_bytes, stream);
 }
 
+size_t kvs_kivi_advance_workspace_bytes(int32_t batch) {
+  if (batch < 1) return 0;
+  return align_up(kHeader + 16u + (size_t)batch * 20u);
+}
+
+int kvs_kivi_advance(const kvs_shape* shape, const void* kv_pool, int64_t pool_blocks,
+                     void* kivi_pool, int64_t kivi_blocks, int32_t* block_table,
+                     int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t* quant_lens,
+                     int32_t batch, int32_t residual_tokens, const int32_t* kivi_free,
+                     int32_t kivi_free_capacity, int32_t* kivi_free_top, int32_t* fp16_free,
+                     int32_t fp16_free_capacity, int32_t* fp16_free_top, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!kv_pool || !kivi_pool || !block_table || !seq_lens || !quant_lens || !kivi_free ||
+      !kivi_free_top || !fp16_free || !fp16_free_top || !workspace)
+    return fail(KVS_E_NULL, "a required pointer is NULL");
+  rc = check_counts(batch, max_blocks_per_seq);
+  if (rc) return rc;
+  if (pool_blocks < 1 || pool_blocks > INT32_MAX || kivi_blocks < 1 || kivi_blocks > INT32_MAX)
+    return fail(KVS_E_RANGE, "pool sizes out of range");
+  if (residual_tokens < 0 || residual_tokens > 16 * max_blocks_per_seq)
+    return fail(KVS_E_RANGE, "residual_tokens %d out of range", residual_tokens);
+  if (kivi_free_capacity < 0 || fp16_free_capacity < 0)
+    return fail(KVS_E_RANGE, "free-stack capacities must be >= 0");
+  if ((uint64_t)shape->num_layers > 65535) return fail(KVS_E_RANGE, "num_layers > 65535");
+  if (!aligned(kv_pool, 16) || !aligned(kivi_pool, 16))
+    return fail(KVS_E_ALIGN, "pools must be 16-byte aligned");
+  if (!aligned(workspace, kAlign)) return fail(KVS_E_ALIGN, "workspace must be 256-byte aligned");
+  const size_t need = kvs_kivi_advance_workspace_bytes(batch);
+  if (workspace_bytes < need)
+    return fail(KVS_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  kvs::KiviAdvanceArgs a{};
+  a.table = block_table;
+  a.max_nb = max_blocks_per_seq;
+  a.seq_lens = seq_lens;
+  a.quant_lens = quant_lens;
+  a.residual = residual_tokens;
+  a.pool_blocks = pool_blocks;
+  a.kivi_blocks = kivi_blocks;
+  a.kivi_free = kivi_free;
+  a.kivi_free_capacity = kivi_free_capacity;
+  a.kivi_free_top = kivi_free_top;
+  a.fp16_free = fp16_free;
+  a.fp16_free_capacity = fp16_free_capacity;
+  a.fp16_free_top = fp16_free_top;
+  a.count = reinterpret_cast<int32_t*>(ws + kHeader);
+  a.jobs = reinterpret_cast<int32_t*>(ws + kHeader + 16u);
+  a.job_seq = reinterpret_cast<int32_t*>(ws + kHeader + 16u + (size_t)batch * 16u);
+  a.status = reinterpret_cast<uint32_t*>(ws);
+  kvs::KiviQuantArgs q{};
+  q.pool = static_cast<const uint8_t*>(kv_pool);
+  q.kivi = static_cast<uint8_t*>(kivi_pool);
+  q.pairs = a.jobs;
+  q.pool_blocks = pool_blocks;
+  q.kivi_blocks = kivi_blocks;
+  q.num_layers = shape->num_layers;
+  q.n_pairs = batch;
+  q.count = a.count;
+  q.status = a.status;
+  hipError_t e = kvs::launch_kivi_advance(a, q, batch, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "kivi_advance launch");
+  return ok();
+}
+
 size_t kvs_kivi_block_bytes(const kvs_shape* shape) {
   if (!shape) return 0;
   return (size_t)shape->num_layers * 2u * 8u * (size_t)kvs::kKiviTileBytes;

@@ -159,12 +159,36 @@ struct KiviQuantArgs {
   int64_t pool_blocks;
   int64_t kivi_blocks;
   int32_t num_layers;
-  int32_t n_pairs;
+  int32_t n_pairs;          // grid size (upper bound on pairs)
+  const int32_t* count;     // nullable: pairs at or past *count are skipped
+  uint32_t* status;
+};
+
+// KIVI boundary advance after appends (kvs_kivi_advance).
+struct KiviAdvanceArgs {
+  int32_t* table;           // [B][max_nb] in / out
+  int32_t max_nb;
+  const int32_t* seq_lens;
+  int32_t* quant_lens;      // in / out
+  int32_t residual;         // fp16 residual window (tokens)
+  int64_t pool_blocks;
+  int64_t kivi_blocks;
+  const int32_t* kivi_free;
+  int32_t kivi_free_capacity;
+  int32_t* kivi_free_top;   // in / out
+  int32_t* fp16_free;       // released fp16 ids are pushed here
+  int32_t fp16_free_capacity;
+  int32_t* fp16_free_top;   // in / out
+  int32_t* jobs;            // [B][4] workspace: src even, src odd, dst even, dst odd
+  int32_t* job_seq;         // [B] workspace: sequence of each job
+  int32_t* count;           // workspace: number of jobs
   uint32_t* status;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int batch, hipStream_t stream);
 hipError_t launch_kivi_quantize(const KiviQuantArgs& a, hipStream_t stream);
+hipError_t launch_kivi_advance(const KiviAdvanceArgs& adv, const KiviQuantArgs& q, int batch,
+                               hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int batch, hipStream_t stream);
 hipError_t launch_mass(const MassArgs& a, int batch, hipStream_t stream);
 hipError_t launch_score(const ScoreArgs& a, int batch, hipStream_t stream);

@@ -1083,6 +1083,7 @@ __global__ void __launch_bounds__(kQuantThreads) kivi_quantize(KiviQuantArgs a) 
   const int layer = blockIdx.y;
   const int g = blockIdx.z;
   const int tid = threadIdx.x;
+  if (a.count && pair >= *a.count) return;
   const int32_t* pr = a.pairs + (size_t)pair * 4;
   const int src[2] = {pr[0], pr[1]};
   const int dst[2] = {pr[2], pr[3]};
@@ -1160,6 +1161,124 @@ __global__ void __launch_bounds__(kQuantThreads) kivi_quantize(KiviQuantArgs a) 
   }
   reinterpret_cast<uint32_t*>(dst_tile(h, 0))[w] = kword;
   reinterpret_cast<uint32_t*>(dst_tile(h, 1))[w] = vword;
+}
+
+// ---------------------------------------------------------------------------
+// KIVI boundary advance.  kivi_advance_alloc (one work-group) walks the batch in
+// order; a sequence whose fp16 residual has reached residual + 32 tokens gets
+// its next 32-token pair quantised: two quantised blocks from the top of the
+// KIVI free stack (an exclusive prefix count over the sequences that advance)
+// and a job {fp16 even, fp16 odd, KIVI even, KIVI odd}.  kivi_quantize then
+// runs over the jobs, and kivi_advance_commit points the table entries at the
+// quantised blocks, grows quant_lens by 32 and pushes the two fp16 blocks onto
+// the fp16 free stack, in job order.
+// ---------------------------------------------------------------------------
+constexpr int kAdvanceThreads = 1024;
+
+__global__ void __launch_bounds__(kAdvanceThreads) kivi_advance_alloc(KiviAdvanceArgs a,
+                                                                      int batch) {
+  __shared__ int scan[kAdvanceThreads];
+  const int tid = threadIdx.x;
+  int top0 = *a.kivi_free_top;
+  if (top0 < 0 || top0 > a.kivi_free_capacity) {
+    if (tid == 0) flag(a.status, KVS_DEV_BAD_OFFSETS);
+    top0 = top0 < 0 ? 0 : a.kivi_free_capacity;
+  }
+  int carry = 0;
+  for (int base = 0; base < batch; base += kAdvanceThreads) {
+    const int s = base + tid;
+    int need = 0, src_e = -1, src_o = -1;
+    if (s < batch) {
+      const int n = a.seq_lens[s];
+      const int nq = a.quant_lens[s];
+      const bool valid = n >= 0 && nq >= 0 && (nq & 31) == 0 && nq <= n && n <= 16 * a.max_nb;
+      if (!valid) {
+        flag(a.status, KVS_DEV_BAD_SEQ_LEN);
+      } else if (n - nq >= a.residual + 32) {
+        const int b = nq >> 4;
+        src_e = a.table[(size_t)s * a.max_nb + b];
+        src_o = a.table[(size_t)s * a.max_nb + b + 1];
+        if (src_e >= 0 && src_e < a.pool_blocks && src_o >= 0 && src_o < a.pool_blocks) need = 1;
+        else flag(a.status, KVS_DEV_BAD_BLOCK_ID);
+      }
+    }
+    scan[tid] = need;
+    __syncthreads();
+    for (int off = 1; off < kAdvanceThreads; off <<= 1) {
+      const int v = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    const int job = carry + scan[tid] - need;          // this sequence's job index
+    if (need) {
+      if (2 * job + 2 <= top0) {
+        const int de = a.kivi_free[top0 - 1 - 2 * job];
+        const int dO = a.kivi_free[top0 - 2 - 2 * job];
+        const bool good = de >= 0 && de < a.kivi_blocks && dO >= 0 && dO < a.kivi_blocks;
+        int32_t* j4 = a.jobs + (size_t)job * 4;
+        // a job with a bad stack entry stays in place with ids -1: the
+        // quantiser skips it (raising the status bit) and commit ignores it
+        j4[0] = good ? src_e : -1;
+        j4[1] = good ? src_o : -1;
+        j4[2] = good ? de : -1;
+        j4[3] = good ? dO : -1;
+        a.job_seq[job] = good ? s : -1;
+        if (!good) flag(a.status, KVS_DEV_BAD_BLOCK_ID);
+      } else {
+        flag(a.status, KVS_DEV_POOL_EXHAUSTED);   // later sequences: no job written
+      }
+    }
+    carry += scan[kAdvanceThreads - 1];
+    __syncthreads();
+  }
+  // Jobs are granted in batch order, so the ones that found KIVI blocks are
+  // exactly jobs [0, granted); each consumed two stack entries.
+  if (tid == 0) {
+    const int granted = min(carry, top0 / 2);
+    *a.count = granted;
+    *a.kivi_free_top = top0 - 2 * granted;
+  }
+}
+
+__global__ void __launch_bounds__(256) kivi_advance_commit(KiviAdvanceArgs a) {
+  const int count = *a.count;
+  int ftop = *a.fp16_free_top;
+  const int tid = threadIdx.x;
+  // exclusive count of committed jobs before each job, in job order
+  __shared__ int done[256];
+  int pushed = 0;
+  for (int base = 0; base < count; base += 256) {
+    const int job = base + tid;
+    const int s = job < count ? a.job_seq[job] : -1;
+    const int ok = s >= 0 ? 1 : 0;
+    done[tid] = ok;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int v = tid >= off ? done[tid - off] : 0;
+      __syncthreads();
+      done[tid] += v;
+      __syncthreads();
+    }
+    const int before = pushed + done[tid] - ok;
+    if (ok) {
+      const int32_t* j4 = a.jobs + (size_t)job * 4;
+      const int b = a.quant_lens[s] >> 4;
+      a.table[(size_t)s * a.max_nb + b] = j4[2];
+      a.table[(size_t)s * a.max_nb + b + 1] = j4[3];
+      a.quant_lens[s] += 32;
+      const int slot = ftop + 2 * before;
+      if (slot + 2 <= a.fp16_free_capacity) {
+        a.fp16_free[slot] = j4[0];
+        a.fp16_free[slot + 1] = j4[1];
+      } else {
+        flag(a.status, KVS_DEV_POOL_EXHAUSTED);
+      }
+    }
+    pushed += done[255];
+    __syncthreads();
+  }
+  if (tid == 0) *a.fp16_free_top = min(ftop + 2 * pushed, a.fp16_free_capacity);
 }
 
 // ---------------------------------------------------------------------------
@@ -1373,6 +1492,16 @@ hipError_t launch_kivi_quantize(const KiviQuantArgs& a, hipStream_t stream) {
   if (a.num_layers > 65535) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kivi_quantize, dim3((uint32_t)a.n_pairs, (uint32_t)a.num_layers, 8),
                      dim3(kQuantThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_kivi_advance(const KiviAdvanceArgs& adv, const KiviQuantArgs& q, int batch,
+                               hipStream_t stream) {
+  if (q.num_layers > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kivi_advance_alloc, dim3(1), dim3(kAdvanceThreads), 0, stream, adv, batch);
+  hipLaunchKernelGGL(kivi_quantize, dim3((uint32_t)batch, (uint32_t)q.num_layers, 8),
+                     dim3(kQuantThreads), 0, stream, q);
+  hipLaunchKernelGGL(kivi_advance_commit, dim3(1), dim3(256), 0, stream, adv);
   return hipGetLastError();
 }
 

@@ -24,7 +24,7 @@ def kivi_quant_len(n: int) -> int:
 
 class DecodeSession:
     def __init__(self, m, layer_begin: int = 0, layer_end=None, split_blocks: int = 0,
-                 anchor_blocks: int = 1, stream=None):
+                 anchor_blocks: int = 1, stream=None, kivi_spare_blocks=None):
         self.m = m
         self.stream = stream
         L = m.num_layers
@@ -53,9 +53,9 @@ class DecodeSession:
         self.anchor_blocks = anchor_blocks
         self.reset_meta()
         if fmt == "kivi2":
-            self._build_kivi()
+            self._build_kivi(8 * B if kivi_spare_blocks is None else kivi_spare_blocks)
 
-    def _build_kivi(self):
+    def _build_kivi(self, spare: int):
         """Quantise every sequence's tokens below its KIVI boundary with the
         library's quantiser into a separate pool of quantised blocks, and point
         those table entries at it.  Pairs of fp16 blocks shared between
@@ -74,8 +74,9 @@ class DecodeSession:
                     pairs.append(src)
                 k = where[src]
                 kivi_table[s_, 2 * p:2 * p + 2] = (2 * k, 2 * k + 1)
-        n_blocks = max(2, 2 * len(pairs))
+        n_blocks = max(2, 2 * len(pairs) + spare)
         place = W.kivi_placement(m.workload, n_blocks)       # pair k -> blocks place[2k], place[2k+1]
+        self.kivi_free_host = place[2 * len(pairs):].copy()  # quantised blocks not in use
         for s_ in range(m.batch):
             nqb = int(self.quant_lens_host[s_]) // 16
             kivi_table[s_, :nqb] = place[kivi_table[s_, :nqb]]
@@ -146,20 +147,37 @@ class DecodeSession:
         """Append one token per sequence (updates the pool, table, seq_lens and
         records in place; the host copies of lengths are not touched)."""
         m = self.m
-        if self.kv_format == "kivi2":
-            raise NotImplementedError("append into a KIVI cache is not supported")
+        kivi = self.kv_format == "kivi2"
         if not hasattr(self, "free_stack"):
             dev = self.out.device
-            self.free_stack = torch.from_numpy(m.free_stack.astype(np.int32)).to(dev)
+            # capacity for every pool id: a KIVI cache returns fp16 blocks to this stack
+            stack = np.full(max(m.pool_blocks, 1), -1, dtype=np.int32)
+            stack[:m.free_stack.size] = m.free_stack
+            self.free_stack = torch.from_numpy(stack).to(dev)
             self.free_top = torch.tensor([int(m.free_stack.size)], dtype=torch.int32, device=dev)
             self.append_ws = torch.empty(api.append_workspace_bytes(m.batch), dtype=torch.uint8,
                                          device=dev)
             api.workspace_init(self.append_ws, stream=self.stream)
+            if kivi:
+                self.kivi_free = torch.from_numpy(self.kivi_free_host.astype(np.int32)).to(dev)
+                self.kivi_free_top = torch.tensor([int(self.kivi_free_host.size)],
+                                                  dtype=torch.int32, device=dev)
+                self.advance_ws = torch.empty(api.kivi_advance_workspace_bytes(m.batch),
+                                              dtype=torch.uint8, device=dev)
+                api.workspace_init(self.advance_ws, stream=self.stream)
         eb = 1 if m.workload.kv_format == "e4m3" else 2
-        api.append_kv(self.shape, eb, k_new, v_new, m.pool, m.pool_blocks, m.block_table,
+        table = self.kivi_table if kivi else m.block_table
+        api.append_kv(self.shape, eb, k_new, v_new, m.pool, m.pool_blocks, table,
                       m.max_blocks, m.seq_lens, self.free_stack, int(self.free_stack.numel()),
                       self.free_top, self.meta, m.meta_offsets, m.seq_ids, self.anchor_blocks,
                       m.batch, m.total_blocks, self.append_ws, stream=self.stream)
+        if kivi:
+            # quantise the pair that left the fp16 window, if any, and free its fp16 blocks
+            api.kivi_advance(self.shape, m.pool, m.pool_blocks, self.kivi_pool, self.kivi_blocks,
+                             table, m.max_blocks, m.seq_lens, self.quant_lens, m.batch, 128,
+                             self.kivi_free, int(self.kivi_free.numel()), self.kivi_free_top,
+                             self.free_stack, int(self.free_stack.numel()), self.free_top,
+                             self.advance_ws, stream=self.stream)
 
     def evict_candidates(self, now: int, alpha: float, active=None, exclude_pinned: int = 0):
         """(out_block int32 [B], out_key float64 [B]) device tensors."""
@@ -187,6 +205,8 @@ class DecodeSession:
             bits |= api.device_status(self.append_ws, self.stream)
         if hasattr(self, "kivi_ws"):
             bits |= api.device_status(self.kivi_ws, self.stream)
+        if hasattr(self, "advance_ws"):
+            bits |= api.device_status(self.advance_ws, self.stream)
         return bits
 
     def records(self):

@@ -140,3 +140,101 @@ def test_kivi_bad_quant_len_skips_the_sequence():
     sess.decode(q)
     torch.cuda.synchronize()
     assert sess.status() == 0
+
+
+def test_kivi_append_moves_the_boundary():
+    """70 steps of append -> advance -> decode -> score on KIVI caches.  The
+    oracle keeps every token's fp16 K/V and applies the window rule itself, so
+    it is independent of which fp16 blocks the GPU freed and reused."""
+    _case("KIVI append + boundary advance + decode + score, 70 steps, 2 layers")
+    lens0 = [150, 159, 190, 300, 47]
+    wl = W.as_kivi2(W.custom("kapp", 2, lens0, seed=17, spare_blocks=40))
+    m = W.materialise(wl, DEV, extra_blocks=6)
+    sess = DecodeSession(m, kivi_spare_blocks=30)
+    L, B = m.num_layers, m.batch
+    pool = m.pool.cpu().numpy()
+    hist_k, hist_v = [], []
+    for s in range(B):
+        pids = m.table_host[s, :m.blocks[s]]
+        blk = pool[pids]                                          # [nb][L][2][8][16][128]
+        kv = blk.transpose(1, 2, 3, 0, 4, 5).reshape(L, 2, 8, -1, 128)[:, :, :, :m.lens[s]]
+        hist_k.append(kv[:, 0].copy())
+        hist_v.append(kv[:, 1].copy())
+    lens = list(m.lens)
+    pol = OS.Policy(alpha=0.15)
+    gpol = api.policy(0.15)
+    offsets = m.meta_offsets.cpu().numpy()
+    state = OS.init_state(m.blocks, m.seq_ids.cpu().numpy())
+    top = int(m.free_stack.size)
+    for step in range(70):
+        k, v = W.new_token_kv(m, step)
+        top_before = int(sess.free_top.item()) if hasattr(sess, "free_top") else top
+        sess.append(k, v)
+        kh, vh = k.cpu().numpy(), v.cpu().numpy()
+        opened = advanced = 0
+        for s in range(B):
+            hist_k[s] = np.concatenate([hist_k[s], kh[s][:, :, None]], axis=2)
+            hist_v[s] = np.concatenate([hist_v[s], vh[s][:, :, None]], axis=2)
+            opened += lens[s] % 16 == 0
+            advanced += KV.quant_boundary(lens[s] + 1) > KV.quant_boundary(lens[s])
+            lens[s] += 1
+        q = W.make_query(m, step)
+        sess.decode(q)
+        sess.score(step, gpol)
+        torch.cuda.synchronize()
+        assert m.seq_lens.cpu().tolist() == lens
+        assert sess.quant_lens.cpu().tolist() == [KV.quant_boundary(n) for n in lens]
+        assert int(sess.free_top.item()) == top_before - opened + 2 * advanced
+        # decode against the oracle on the full history
+        qh = q.cpu().numpy()
+        out_ref = np.full(qh.shape, np.nan)
+        mass_ref = []
+        for s in range(B):
+            mass = np.zeros(-(-lens[s] // 16))
+            for layer in range(L):
+                for g in range(8):
+                    Kh, Vh = KV.kivi_kv(hist_k[s][layer, g], hist_v[s][layer, g], lens[s])
+                    for h in range(8 * g, 8 * g + 8):
+                        out_ref[s, layer, h], p = KV.OA.attend_head(qh[s, layer, h], Kh, Vh, SCALE)
+                        mass += KV.OA.block_sums(p, lens[s])
+            mass_ref.append(mass)
+        P.check_out(sess.out, out_ref, range(L))
+        P.check_mass(sess.mass, mass_ref, offsets)
+        blocks = [-(-n // 16) for n in lens]
+        state = OS.grow(state, blocks)
+        state, stale = OS.score_update(state, mass_ref, step, pol)
+        assert not stale.any()
+        rows = np.concatenate([offsets[s] + np.arange(nb) for s, nb in enumerate(blocks)])
+        P.check_records(sess.records()[rows], state, pol)
+    # every pair quantised along the way holds the oracle's bytes
+    kivi = sess.kivi_pool.cpu().numpy().reshape(sess.kivi_blocks, L, 2, 8, KV.TILE_BYTES)
+    tab = sess.kivi_table.cpu().numpy()
+    for s in range(B):
+        for p in range(KV.quant_boundary(lens[s]) // 32):
+            de, do = tab[s, 2 * p], tab[s, 2 * p + 1]
+            for layer in range(L):
+                for g in range(8):
+                    ke, ko, ve, vo = KV.pack_pair(hist_k[s][layer, g, 32 * p:32 * p + 32],
+                                                  hist_v[s][layer, g, 32 * p:32 * p + 32])
+                    assert kivi[de, layer, 0, g].tobytes() == ke and kivi[do, layer, 0, g].tobytes() == ko
+                    assert kivi[de, layer, 1, g].tobytes() == ve and kivi[do, layer, 1, g].tobytes() == vo
+    assert sess.status() == 0
+
+
+def test_kivi_advance_without_free_quantised_blocks():
+    _case("kvs_kivi_advance with one free quantised block: boundary kept, status bit")
+    wl = W.as_kivi2(W.custom("kex", 1, [159, 159], seed=2, spare_blocks=8))
+    m = W.materialise(wl, DEV, extra_blocks=2)
+    sess = DecodeSession(m, kivi_spare_blocks=3)      # 2 initial-free ids after 0 pairs, +1
+    assert int(sess.kivi_free_host.size) == 3
+    k, v = W.new_token_kv(m, 0)
+    sess.append(k, v)                                  # 160 tokens: both sequences want a pair
+    torch.cuda.synchronize()
+    assert sess.quant_lens.cpu().tolist() == [32, 0]   # the first takes two ids, the second finds one
+    assert int(sess.kivi_free_top.item()) == 1
+    assert sess.status() & api._abi.KVS_DEV_POOL_EXHAUSTED
+    q = W.make_query(m, 0)
+    sess.decode(q)
+    torch.cuda.synchronize()
+    lens = m.seq_lens.cpu().tolist()
+    assert lens == [160, 160]
