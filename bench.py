@@ -204,9 +204,6 @@ def main():
     if args.kv_format == "e4m3":
         wl = W.as_e4m3(wl)
     elif args.kv_format == "kivi2":
-        if args.append:
-            print("bench.py --append does not support --kv-format kivi2", file=sys.stderr)
-            sys.exit(2)
         wl = W.as_kivi2(wl)
     alpha = args.alpha if args.alpha is not None else wl.alphas[0]
     extra = 0
@@ -221,7 +218,9 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] inputs ready in {time.time() - t0:.1f} s; pool {m.pool.numel() * 2 / 2**30:.2f} GiB",
           file=sys.stderr, flush=True)
-    sess = DecodeSession(m, split_blocks=args.split_blocks)
+    # quantised blocks for the pairs that leave the fp16 window during the run
+    spare = 2 * m.batch * ((args.warmup + args.steps) // 32 + 2) if args.append else None
+    sess = DecodeSession(m, split_blocks=args.split_blocks, kivi_spare_blocks=spare)
     pol = api.policy(alpha)
     n_q = args.warmup + args.steps
     queries = [W.make_query(m, k) for k in range(n_q)]
@@ -304,11 +303,20 @@ def main():
         raise RuntimeError("a sequence got no eviction candidate")
 
     kv_bytes = sess.kv_bytes_per_step
+    fp16_bytes = sum(m.lens) * m.num_layers * 8 * 128 * 2 * 2
     if args.append:   # the average step reads the lengths in the middle of the run
         mean_tokens = float(lens_at_start.sum()) + m.batch * (args.steps + 1) / 2.0
         kv_bytes = int(mean_tokens * m.num_layers * 8 * 128 * 2 * sess.kv_elem_bytes)
+        fp16_bytes = int(mean_tokens * m.num_layers * 8 * 128 * 2 * 2)
+        if args.kv_format == "kivi2":   # stored bytes of each timed step's lengths
+            from paged_gqa_kv_amd.session import kivi_quant_len
+            per_step = []
+            for k in range(args.steps):
+                lens_k = lens_at_start + k + 1
+                nq = np.array([kivi_quant_len(n) for n in lens_k])
+                per_step.append(int((nq // 16 * 2 * 768 + (lens_k - nq) * 128 * 2 * 2).sum()))
+            kv_bytes = int(sum(per_step) / len(per_step)) * m.num_layers * 8
     unique_bytes = m.unique_blocks * 16 * m.num_layers * 8 * 128 * 2 * sess.kv_elem_bytes
-    fp16_bytes = sum(m.lens) * m.num_layers * 8 * 128 * 2 * 2
     if args.kv_format == "kivi2":
         resid = sum(m.lens) - int(sess.quant_lens_host.sum())
         unique_bytes = (sess.kivi_blocks * 2 * 768 + resid * 128 * 2 * 2) * m.num_layers * 8
