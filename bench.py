@@ -169,10 +169,16 @@ def _cpu_baseline(m, alpha, budget_s):
     r1 = resource.getrusage(resource.RUSAGE_SELF)
     cpu = (r1.ru_utime - r0.ru_utime) + (r1.ru_stime - r0.ru_stime)
     cores = max(1, round(cpu / max(wall + copy_s, 1e-9)))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = ", ".join(f"{d.get('internal_api')} x{d.get('num_threads')}" for d in threadpool_info())
+    except Exception:  # reporting only
+        blas = "unknown"
     return {
         "value": kv_bytes / wall / 1e9,
         "unit": "GB/s",
         "cores": cores,
+        "threadpools": blas,
         "kind": "oracle",
         "sample": (f"fp64 oracle decode of layers 0..{layers_done - 1} of {L} for all "
                    f"{m.batch} sequence(s) of step 0, plus scoring of all {m.total_blocks} "
@@ -226,10 +232,15 @@ def main():
     queries = [W.make_query(m, k) for k in range(n_q)]
     new_kv = [W.new_token_kv(m, k) for k in range(n_q)] if args.append else None
 
-    def run_step(k, idx):
+    def run_step(k, idx, mid=None):
+        """One step: [append], decode, score.  `mid` (an event) is recorded
+        between decode and scoring so the scoring kernels can be timed alone."""
         if new_kv is not None:
             sess.append(*new_kv[idx])
-        sess.step(queries[idx], k, pol)
+        sess.decode(queries[idx])
+        if mid is not None:
+            mid.record(torch.cuda.current_stream())
+        sess.score(k, pol)
     torch.cuda.synchronize()
 
     ev = HipEvents()
@@ -249,16 +260,24 @@ def main():
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     lens_at_start = m.seq_lens.cpu().numpy().copy()
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     start.record(stream)
     for k in range(args.steps):
+        if k:
+            bounds[k].record(stream)
         api.set_decode_events(*pairs[k])
-        run_step(k, args.warmup + k)
+        run_step(k, args.warmup + k, mids[k])
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     api.set_decode_events(None, None)
     total_ms = start.elapsed_time(end)
     decode_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
+    step_start = [start] + bounds[1:]
+    step_end = bounds[1:] + [end]
+    step_ms = sorted(a.elapsed_time(b) for a, b in zip(step_start, step_end))
+    score_ms = sorted(a.elapsed_time(b) for a, b in zip(mids, step_end))
     for a, b in pairs:
         ev.destroy(a)
         ev.destroy(b)
@@ -372,6 +391,10 @@ def main():
         "tokens_attended_per_s": round(sum(m.lens) * m.num_layers / t_step, 1),
         "fp16_equivalent_kv_gbps": round(fp16_bytes / t_step / 1e9, 2),
         "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
+        "step_ms_median": round(step_ms[len(step_ms) // 2], 4),
+        "step_ms_min": round(step_ms[0], 4),
+        "score_update_us_median": round(score_ms[len(score_ms) // 2] * 1e3, 2),
+        "records_scored_per_s_score_kernels": round(m.total_blocks / (score_ms[len(score_ms) // 2] / 1e3), 1),
         "decode_kernel_ms": round(dec_avg * 1e3, 4),
         "decode_share_of_step": round(dec_avg / t_step, 4),
         "tier_counts": tiers,
