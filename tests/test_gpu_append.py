@@ -102,3 +102,36 @@ def test_append_exhausts_the_free_stack():
     assert np.array_equal(m.seq_lens.cpu().numpy(), lens_h)
     assert int(sess.free_top.item()) == top == 0
     assert sess.status() & api._abi.KVS_DEV_POOL_EXHAUSTED
+
+
+def test_append_batch_larger_than_one_work_group():
+    """1,500 sequences: the allocation scan runs over two 1,024-sequence chunks
+    and carries its count across them."""
+    _case("append with batch 1500 (two allocation chunks), 1 layer, 18 steps")
+    rng = np.random.default_rng(4)
+    lens = [int(x) for x in rng.choice([15, 16, 17, 31, 32, 1], size=1500)]
+    wl = W.custom("wide", 1, lens, seed=6, spare_blocks=1500 * 2 + 10)
+    m = W.materialise(wl, DEV, extra_blocks=3)
+    sess = DecodeSession(m)
+    pool_h = m.pool.cpu().numpy().copy()
+    table_h = m.table_host.astype(np.int64).copy()
+    lens_h = np.array(m.lens, dtype=np.int64)
+    free_h = m.free_stack.astype(np.int64).copy()
+    top = int(free_h.size)
+    for step in range(18):
+        k, v = W.new_token_kv(m, step)
+        sess.append(k, v)
+        top, allocs, rejected = PG.append_step(pool_h, table_h, lens_h, free_h, top,
+                                               k.cpu().numpy(), v.cpu().numpy())
+        assert rejected == []
+    torch.cuda.synchronize()
+    assert np.array_equal(m.seq_lens.cpu().numpy(), lens_h)
+    assert int(sess.free_top.item()) == top
+    tab = m.block_table.cpu().numpy()
+    for s, n in enumerate(lens_h):
+        nb = -(-int(n) // 16)
+        assert np.array_equal(tab[s, :nb], table_h[s, :nb]), s
+    live = np.unique(table_h[table_h >= 0])
+    assert np.array_equal(_bits(m.pool[torch.from_numpy(live).to(DEV)].cpu().numpy()),
+                          _bits(pool_h[live]))
+    assert sess.status() == 0

@@ -238,3 +238,37 @@ def test_kivi_advance_without_free_quantised_blocks():
     torch.cuda.synchronize()
     lens = m.seq_lens.cpu().tolist()
     assert lens == [160, 160]
+
+
+def test_kivi_advance_batch_larger_than_one_work_group():
+    """1,300 sequences at 159 tokens all cross the window on the same append:
+    allocation scans two chunks and the commit kernel walks 1,300 jobs."""
+    _case("kvs_kivi_advance with 1300 simultaneous boundary moves, 1 layer")
+    wl = W.as_kivi2(W.custom("kwide", 1, [159] * 1300, seed=9, spare_blocks=2700))
+    m = W.materialise(wl, DEV, extra_blocks=2)
+    sess = DecodeSession(m, kivi_spare_blocks=2 * 1300)
+    free0 = sess.kivi_free_host.copy()
+    k, v = W.new_token_kv(m, 0)
+    sess.append(k, v)
+    torch.cuda.synchronize()
+    assert sess.status() == 0
+    assert sess.quant_lens.cpu().tolist() == [32] * 1300
+    assert int(sess.kivi_free_top.item()) == 0
+    tab = sess.kivi_table.cpu().numpy()
+    # batch order from the top of the stack: sequence s takes free0[-1 - 2s], free0[-2 - 2s]
+    for s in (0, 1, 1023, 1024, 1299):
+        assert tab[s, 0] == free0[free0.size - 1 - 2 * s] and tab[s, 1] == free0[free0.size - 2 - 2 * s]
+    # the freed fp16 blocks went onto the append stack, pair by pair in batch order
+    top = int(sess.free_top.item())
+    stack = sess.free_stack.cpu().numpy()
+    pushed = stack[top - 2 * 1300:top].reshape(1300, 2)
+    assert np.array_equal(pushed, m.table_host[:, :2].astype(np.int32))
+    kivi = sess.kivi_pool.cpu().numpy().reshape(sess.kivi_blocks, 1, 2, 8, KV.TILE_BYTES)
+    pool = m.pool.cpu().numpy()
+    for s in (0, 1024, 1299):
+        e, o = m.table_host[s, 0], m.table_host[s, 1]
+        for g in (0, 7):
+            K32 = np.concatenate([pool[e, 0, 0, g], pool[o, 0, 0, g]])
+            V32 = np.concatenate([pool[e, 0, 1, g], pool[o, 0, 1, g]])
+            ke, ko, ve, vo = KV.pack_pair(K32, V32)
+            assert kivi[tab[s, 0], 0, 0, g].tobytes() == ke and kivi[tab[s, 1], 0, 1, g].tobytes() == vo
