@@ -272,3 +272,28 @@ def test_kivi_advance_batch_larger_than_one_work_group():
             V32 = np.concatenate([pool[e, 0, 1, g], pool[o, 0, 1, g]])
             ke, ko, ve, vo = KV.pack_pair(K32, V32)
             assert kivi[tab[s, 0], 0, 0, g].tobytes() == ke and kivi[tab[s, 1], 0, 1, g].tobytes() == vo
+
+
+def test_mixed_precision_by_layer():
+    """fp16 for the first layer, KIVI for the rest (the per-layer escape hatch of
+    Fitting a Million Tokens, Sec. 02): two calls over layer ranges, the second
+    accumulating the block mass."""
+    _case("layer 0 fp16 + layers 1..2 KIVI, block mass accumulated across the two calls")
+    from oracle import attention as OA
+    m, sess = _kivi_session([600, 200, 1300], layers=3, seed=31)
+    import dataclasses
+    m16 = type(m)(**{**m.__dict__, "workload": dataclasses.replace(m.workload, kv_format="fp16")})
+    fp16 = DecodeSession(m16, layer_begin=0, layer_end=1)
+    q = W.make_query(m, 0)
+    fp16.decode(q)                                            # layer 0, fp16 pool
+    sess.mass.copy_(fp16.mass)
+    sess.decode(q, accumulate=1, layer_begin=1, layer_end=3)  # layers 1-2, KIVI cache
+    torch.cuda.synchronize()
+    pool = m.pool.cpu().numpy()
+    qh = q.cpu().numpy()
+    out0, mass0 = OA.decode_step(qh, pool, m.table_host, m.lens, SCALE, 0, 1)
+    out12, mass12 = KV.decode_step(qh, pool, m.table_host, m.lens, SCALE, 1, 3)
+    P.check_out(fp16.out, out0, [0])
+    P.check_out(sess.out, out12, [1, 2])
+    P.check_mass(sess.mass, [a + b for a, b in zip(mass0, mass12)], m.meta_offsets.cpu().numpy())
+    assert sess.status() == 0 and fp16.status() == 0
