@@ -93,6 +93,8 @@ def decode_layer(q_sl, pool, table_row, n_tokens: int, layer: int, scale: float,
 
     Returns out [64][D] fp64 and the block mass of this layer [nb] fp64.
     """
+    if n_tokens == 0:   # an empty sequence attends to nothing: zero output, no blocks
+        return np.zeros((q_sl.shape[0], q_sl.shape[-1]), dtype=np.float64), np.zeros(0)
     K, V = gather_layer(pool, table_row, n_tokens, layer, kv_format=kv_format)
     n_q = q_sl.shape[0]
     out = np.empty((n_q, K.shape[-1]), dtype=np.float64)

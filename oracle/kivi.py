@@ -150,6 +150,8 @@ def decode_layer(q_sl, pool, table_row, n: int, layer: int, scale: float):
 
     Returns out [64][D] fp64 and the block mass of this layer [nb] fp64.
     """
+    if n == 0:          # an empty sequence attends to nothing: zero output, no blocks
+        return np.zeros((q_sl.shape[0], HEAD_DIM), dtype=np.float64), np.zeros(0)
     K16, V16 = _gather16(pool, table_row, n, layer)
     out = np.empty((q_sl.shape[0], HEAD_DIM), dtype=np.float64)
     mass = np.zeros(-(-n // BLOCK_TOKENS), dtype=np.float64)

@@ -105,6 +105,8 @@ def init_state(blocks_per_seq, seq_ids, anchor_blocks: int = 1) -> ScoreState:
 def normalise(mass_seq):
     """Block mass divided by the sequence's largest block mass."""
     mass_seq = np.asarray(mass_seq, dtype=np.float64)
+    if mass_seq.size == 0:      # an empty sequence has no records
+        return mass_seq
     top = mass_seq.max()
     if top <= 0.0:
         return np.zeros_like(mass_seq)
@@ -180,13 +182,15 @@ def order_key(state: ScoreState, alpha: float):
 
 
 def eviction_candidates(state: ScoreState, t: int, alpha: float, active=None,
-                        exclude_pinned: bool = False):
+                        exclude_pinned: bool = False, nseq=None):
     """Per sequence, the record with the lowest decayed score at step t (brute
     force over its records; ties to the lowest logical block).  Returns
     (block index or -1, decayed score or +inf) per sequence; inactive
-    sequences and sequences with no eligible record give (-1, +inf)."""
+    sequences and sequences with no eligible record give (-1, +inf).  nseq: the
+    batch size, when trailing sequences may have no records."""
     s_now = decayed(state, t, alpha)
-    nseq = int(state.seq_index.max()) + 1 if state.seq_index.size else 0
+    if nseq is None:
+        nseq = int(state.seq_index.max()) + 1 if state.seq_index.size else 0
     blocks = np.full(nseq, -1, dtype=np.int64)
     scores = np.full(nseq, np.inf)
     for s in range(nseq):

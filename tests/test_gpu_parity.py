@@ -261,3 +261,51 @@ def test_unused_pool_blocks_are_nan_and_never_read():
     torch.cuda.synchronize()
     assert torch.isfinite(s.out).all() and torch.isfinite(s.mass).all()
     assert np.isfinite(s.records()["score"]).all()
+
+
+def test_empty_sequences_in_the_batch():
+    """R19: empty sequences have no records and zero output rows; the rest of the
+    batch is unaffected; an append gives an empty sequence its first block."""
+    _case("batch with empty sequences: decode, score, evict, then append one token")
+    from oracle import paging as PG
+    wl = W.custom("empty", 2, [0, 40, 0, 17, 300], seed=6, spare_blocks=10)
+    m = W.materialise(wl, DEV, extra_blocks=2)
+    assert m.blocks[0] == 0 and m.blocks[2] == 0
+    sess = DecodeSession(m)
+    h = P.host(m)
+    pol = OS.Policy(alpha=0.15)
+    gpol = api.policy(0.15)
+    offsets = m.meta_offsets.cpu().numpy()
+    state = OS.init_state(m.blocks, m.seq_ids.cpu().numpy())
+    live_rows = np.concatenate([offsets[s] + np.arange(nb) for s, nb in enumerate(m.blocks)])
+    for step in range(2):
+        q = W.make_query(m, step)
+        sess.step(q, step, gpol)
+        torch.cuda.synchronize()
+        out_ref, mass_ref = P.oracle_decode(h, q)
+        assert torch.count_nonzero(sess.out[[0, 2]]) == 0
+        P.check_out(sess.out, out_ref, range(2), seqs=[1, 3, 4])
+        P.check_mass(sess.mass, mass_ref, offsets, seqs=[1, 3, 4])
+        state, _ = OS.score_update(state, mass_ref, step, pol)
+        P.check_records(sess.records()[live_rows], state, pol)
+    blk, _ = sess.evict_candidates(1, 0.15)
+    ref_blk, _ = OS.eviction_candidates(state, 1, 0.15, nseq=m.batch)
+    assert blk.cpu().tolist() == ref_blk.tolist() and ref_blk[0] == -1 and ref_blk[2] == -1
+    # one append: the empty sequences open block 0
+    pool_h = m.pool.cpu().numpy().copy()
+    table_h = m.table_host.astype(np.int64).copy()
+    lens_h = np.array(m.lens, dtype=np.int64)
+    free_h = m.free_stack.astype(np.int64).copy()
+    k, v = W.new_token_kv(m, 9)
+    sess.append(k, v)
+    top, allocs, rejected = PG.append_step(pool_h, table_h, lens_h, free_h, int(free_h.size),
+                                           k.cpu().numpy(), v.cpu().numpy())
+    assert rejected == [] and [s for s, b, _ in allocs][:2] == [0, 2]
+    q = W.make_query(m, 9)
+    sess.decode(q)
+    torch.cuda.synchronize()
+    assert m.seq_lens.cpu().tolist() == lens_h.tolist()
+    out_ref, mass_ref = P.oracle_decode(dict(pool=pool_h, table=table_h, lens=list(lens_h)), q)
+    P.check_out(sess.out, out_ref, range(2))
+    P.check_mass(sess.mass, mass_ref, offsets)
+    assert sess.status() == 0

@@ -203,3 +203,17 @@ def test_saturated_logits_stay_finite():
     _, V = _loop_gather(pool.numpy(), m.table_host[0], n, 0, g)
     assert np.array_equal(out[0, 0, 8 * g], V[hot])
     assert np.isfinite(masses[0]).all()
+
+
+def test_empty_sequence_gives_zero_rows_and_no_blocks():
+    # R19: an empty sequence has no records and zero output rows, and the
+    # other sequences of the batch are computed as if it were absent
+    m = W.materialise(W.custom("empty", 2, [0, 40, 0, 17], seed=3, spare_blocks=4), "cpu")
+    assert m.blocks == [0, 3, 0, 2] and m.total_blocks == 5
+    q = np.random.default_rng(0).standard_normal((4, 2, 64, 128)).astype(np.float16)
+    out, mass = OA.decode_step(q, m.pool.numpy(), m.table_host, m.lens, 0.088)
+    assert np.all(out[[0, 2]] == 0) and mass[0].size == 0 and mass[2].size == 0
+    out2, mass2 = OA.decode_step(q[[1, 3]], m.pool.numpy(), m.table_host[[1, 3]],
+                                 [m.lens[1], m.lens[3]], 0.088)
+    assert np.array_equal(out[[1, 3]], out2)
+    assert all(np.array_equal(a, b) for a, b in zip([mass[1], mass[3]], mass2))

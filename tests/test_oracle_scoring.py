@@ -238,3 +238,15 @@ def test_eviction_candidates_ties_masks_and_pins():
     st2.score = np.array([0.3, 0.0, 0.2])
     st2.t_touch = np.array([5, S.NEVER, 5], dtype=np.uint64)
     assert S.eviction_candidates(st2, 6, 0.1)[0].tolist() == [1]
+
+
+def test_empty_sequences_have_no_records_and_no_candidate():
+    # R19: an empty sequence has no records; scoring and eviction skip it
+    st = S.init_state([0, 3, 0, 2], [10, 11, 12, 13])
+    assert st.score.size == 5
+    st, stale = S.score_update(st, [np.zeros(0), np.array([1.0, 2.0, 4.0]), np.zeros(0),
+                                    np.array([3.0, 3.0])], 0, S.Policy(alpha=0.5))
+    assert not stale.any()
+    np.testing.assert_allclose(st.score, [0.125, 0.25, 0.5, 0.5, 0.5])
+    b, sc = S.eviction_candidates(st, 1, 0.5, nseq=4)
+    assert b.tolist() == [-1, 0, -1, 0] and np.isinf(sc[[0, 2]]).all()

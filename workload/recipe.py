@@ -171,8 +171,8 @@ def query_seed(seed: int, step: int) -> int:
 
 def _layout(wl: Workload, extra_blocks: int = 0):
     lens = wl.lengths()
-    if any(n <= 0 for n in lens):
-        raise ValueError("every sequence needs at least one token")
+    if any(n < 0 for n in lens):
+        raise ValueError("sequence lengths must be >= 0")
     blocks = [math.ceil(n / BLOCK_TOKENS) for n in lens]
     shared_nb = math.ceil(wl.shared_prefix_tokens / BLOCK_TOKENS)
     used_shared = min(shared_nb, max(blocks)) if shared_nb else 0
@@ -184,7 +184,7 @@ def _layout(wl: Workload, extra_blocks: int = 0):
     perm = rng.permutation(pool).astype(np.int64)
     shared = perm[:used_shared]
     cursor = used_shared
-    max_nb = max(blocks) + extra_blocks
+    max_nb = max(max(blocks), 1) + extra_blocks
     table = np.full((wl.batch, max_nb), -1, dtype=np.int32)
     refcount = np.zeros(pool, dtype=np.int32)
     for s, nb in enumerate(blocks):
