@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import workload as W
+from oracle import attention as OA
 from oracle import scoring as OS
 from paged_gqa_kv_amd import api
 from paged_gqa_kv_amd.session import DecodeSession
@@ -308,4 +309,37 @@ def test_empty_sequences_in_the_batch():
     out_ref, mass_ref = P.oracle_decode(dict(pool=pool_h, table=table_h, lens=list(lens_h)), q)
     P.check_out(sess.out, out_ref, range(2))
     P.check_mass(sess.mass, mass_ref, offsets)
+    assert sess.status() == 0
+
+
+def test_uniform_attention_and_alpha_one_closed_forms():
+    """q = 0: every logit is 0, so each head attends uniformly (out = mean of V)
+    and a block's mass is proportional to its token count; with alpha = 1 the
+    EMA equals the normalised mass: token count / the sequence's largest block
+    token count (1 for full blocks; a lone partial block is its own maximum)."""
+    _case("q = 0 and alpha = 1: closed-form outputs, masses and scores")
+    wl = W.custom("uniform", 2, [40, 100, 16, 5], seed=14)
+    m = W.materialise(wl, DEV)
+    q = torch.zeros((m.batch, 2, 64, 128), dtype=torch.float16, device=DEV)
+    sess = DecodeSession(m, split_blocks=4)
+    sess.step(q, 0, api.policy(1.0))
+    torch.cuda.synchronize()
+    h = P.host(m)
+    offsets = m.meta_offsets.cpu().numpy()
+    out = sess.out.float().cpu().numpy()
+    mass = sess.mass.cpu().numpy().astype(np.float64)
+    rec = sess.records()
+    for s, n in enumerate(m.lens):
+        for layer in range(2):
+            K, V = OA.gather_layer(h["pool"], h["table"][s], n, layer)
+            mean = V.mean(axis=1)                                   # [8][128]
+            ref = np.repeat(mean, 8, axis=0)                        # head h reads KV head h // 8
+            assert np.abs(out[s, layer] - ref).max() <= 2e-3 * np.abs(ref).max()
+        nb = -(-n // 16)
+        counts = np.array([min(16, n - 16 * b) for b in range(nb)], dtype=np.float64)
+        got = mass[offsets[s]:offsets[s] + nb]
+        np.testing.assert_allclose(got, 2 * 64 * counts / n, rtol=1e-6)
+        E = rec["score"][offsets[s]:offsets[s] + nb]
+        np.testing.assert_allclose(E, counts / counts.max(), rtol=0, atol=1e-6)
+        assert np.all(E[counts == counts.max()] == 1.0)
     assert sess.status() == 0
