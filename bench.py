@@ -28,7 +28,21 @@ import time
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, published
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SRC = os.path.join(ROOT, "paged_gqa_kv_amd", "csrc", "kvs_kernels.hip")
+CSRC = os.path.join(ROOT, "paged_gqa_kv_amd", "csrc")
+# Sources a decode kernel is compiled from; a committed counter summary is used
+# only while their digest matches the one recorded with it.
+KERNEL_SOURCES = {
+    "paged_decode_gqa": ("kvs_decode.hip", "kvs_device.h", "kvs_internal.h"),
+    "paged_decode_kivi": ("kvs_kivi.hip", "kvs_device.h", "kvs_internal.h"),
+}
+
+
+def kernel_digest(kernel: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
 
 
 def _parse():
@@ -87,9 +101,7 @@ def _traffic(kernel: str, workload: str, split_blocks: int):
         return None
     with open(path) as f:
         rec = json.load(f)
-    with open(KERNEL_SRC, "rb") as f:
-        digest = hashlib.sha256(f.read()).hexdigest()
-    if rec.get("kernel_sha256") != digest or rec.get("split_blocks") != split_blocks:
+    if rec.get("kernel_sha256") != kernel_digest(kernel) or rec.get("split_blocks") != split_blocks:
         return None
     return rec.get("hbm_bytes_per_launch")
 

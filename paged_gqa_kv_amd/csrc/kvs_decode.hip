@@ -1,0 +1,441 @@
+// Paged GQA decode kernels over fp16 and FP8 E4M3 pools, and the split
+// combine and block-mass reduction shared with the KIVI decode:
+//   paged_decode_gqa  split-K decode: one wave per (sequence, layer, KV head,
+//                     split of blocks); QK^T and PV on MFMA; online softmax;
+//                     per-(layer, head, block) probability-mass partials.
+//   combine_splits    merges the splits of each (sequence, layer, head) into the
+//                     fp16 output and the per-split normalising weights.
+//   block_mass        sums the mass partials of every (layer, query head) into
+//                     one fp32 number per (sequence, block), in a fixed order.
+//
+// Sources: "KV-Cache Offloading for LLM Inference -- Visual Reference"
+// Sec. 2 (attention), Sec. 11 (EMA), Sec. 12 (priority, cut points);
+// "GQA Per-Head Scoring Streams" (head grouping, stream aggregation, the
+// 64-byte record); "KV cache offload" post, "Top row" (block tables);
+// "Fitting a Million Tokens", Sec. 02 (FP8 E4M3 and KIVI 2-bit KV).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "kvs.h"
+#include "kvs_device.h"
+#include "kvs_internal.h"
+
+namespace kvs {
+
+// ---------------------------------------------------------------------------
+// paged_decode_gqa
+//
+// One 64-lane wave owns (s, layer, g, split).  Lane l = 16 j + c.
+//  QK:  S^T[token][head] = K[token][:] . q[head][:] on v_mfma_f32_16x16x32_f16,
+//       A = the 16x128 key tile (lane reads 64 contiguous bytes of row c), B =
+//       the 8 queries of the group padded to 16 columns.  The result gives
+//       lane (j, c) the logits of head c for tokens 4j..4j+3.
+//  PV:  O^T[d][head] += V^T[d][token] P^T[token][head] on
+//       v_mfma_f32_16x16x16_f16.  P^T is exactly the QK result layout (after
+//       rounding to fp16).  V^T needs the value tile transposed: it is staged
+//       through 4 KiB of LDS, each lane reads 4 rows x 16 bytes, and byte
+//       permutes build the operand of each of the 8 output tiles.  Output tile
+//       k holds d = 8 m + k, so lane (j, c) ends with the 32 contiguous values
+//       d in [32 j, 32 j + 32) of head c.
+//  Online softmax in base 2: logits are scaled by scale * log2(e); a running
+//  maximum per head; the per-block mass of head c is kept in LDS relative to
+//  the current maximum and rescaled whenever that maximum grows.
+// ---------------------------------------------------------------------------
+// Stored K/V element formats.  A (layer, K|V, KV head) tile is 16 rows of 128
+// elements; a block holds, per layer, 8 key tiles then 8 value tiles.
+struct KvF16 {
+  static constexpr int kElemBytes = 2;
+  static constexpr int kLoads = 4;   // 16-byte loads per lane per tile
+  static constexpr int kRing = 2;    // ring slots (32 VGPRs each)
+};
+struct KvE4M3 {                      // FP8 E4M3 codes, no scale
+  static constexpr int kElemBytes = 1;
+  static constexpr int kLoads = 2;
+  static constexpr int kRing = 2;    // 16 VGPRs each; 3 and 4 measured slower
+};
+
+template <class F>
+struct BlockRegs {
+  u4_t k[F::kLoads];
+  u4_t v[F::kLoads];
+};
+
+template <class F>
+constexpr int tile_bytes() { return 16 * kHeadDim * F::kElemBytes; }
+
+// First of the 8 elements of a 128-element row that lane group j feeds to QK
+// step i (key and query alike, so the 128-term dot product is covered once).
+// Key load i of lane (j, c) reads bytes [64 i + 16 j, 64 i + 16 j + 16) of row
+// c: each load instruction reads whole 64-byte row segments.
+template <class F>
+__device__ __forceinline__ int qk_elem(int i, int j) {
+  if constexpr (F::kElemBytes == 2) return 32 * i + 8 * j;          // load i
+  else return 64 * (i >> 1) + 16 * j + 8 * (i & 1);                 // half i & 1 of load i >> 1
+}
+
+// Issues exactly 2 * F::kLoads 16-byte loads per lane: the key tile in the QK
+// operand layout above and the value tile in plain order (load i covers bytes
+// [1024 i, 1024 i + 1024)).  Always issuing the same number of loads on every
+// path lets the compiler wait for one ring slot precisely instead of draining
+// every load in flight.
+template <class F>
+__device__ __forceinline__ void load_block(BlockRegs<F>& r, const uint8_t* base, int lane, int c,
+                                           int j) {
+  const uint8_t* kp = base + c * (kHeadDim * F::kElemBytes) + j * 16;
+  const uint8_t* vp = base + 8 * tile_bytes<F>() + lane * 16;
+#pragma unroll
+  for (int i = 0; i < F::kLoads; ++i)
+    r.k[i] = plain_load(reinterpret_cast<const u4_t*>(kp + i * 64));
+#pragma unroll
+  for (int i = 0; i < F::kLoads; ++i)
+    r.v[i] = stream_load(reinterpret_cast<const u4_t*>(vp + i * 1024));
+}
+
+// Four E4M3 codes to four fp16 values (exact: every finite E4M3 value is an
+// fp16 value), with gfx950's packed scaled conversion at scale 1.
+__device__ __forceinline__ u2_t e4m3x4_to_f16(uint32_t w) {
+  const h2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  const h2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+  return u2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
+// Value tile of one ring slot to LDS as row-major fp16 [16][128].
+template <class F>
+__device__ __forceinline__ void stage_values(const BlockRegs<F>& r, u4_t* vstage, int lane) {
+  if constexpr (F::kElemBytes == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vstage[i * 64 + lane] = r.v[i];
+  } else {
+    // load i, lane l: row 8 i + l / 8, elements [16 (l % 8), 16 (l % 8) + 16)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const u2_t a = e4m3x4_to_f16(r.v[i][0]);
+      const u2_t b = e4m3x4_to_f16(r.v[i][1]);
+      const u2_t c2 = e4m3x4_to_f16(r.v[i][2]);
+      const u2_t d = e4m3x4_to_f16(r.v[i][3]);
+      const int base = (8 * i + (lane >> 3)) * 16 + 2 * (lane & 7);
+      vstage[base] = u4_t{a[0], a[1], b[0], b[1]};
+      vstage[base + 1] = u4_t{c2[0], c2[1], d[0], d[1]};
+    }
+  }
+}
+
+// QK operand i of one ring slot: 8 fp16 key elements from qk_elem(i, j) on.
+template <class F>
+__device__ __forceinline__ h8_t key_operand(const BlockRegs<F>& r, int i) {
+  if constexpr (F::kElemBytes == 2) {
+    return __builtin_bit_cast(h8_t, r.k[i]);
+  } else {
+    const u4_t w = r.k[i >> 1];
+    const u2_t a = e4m3x4_to_f16(w[(i & 1) * 2]);
+    const u2_t b = e4m3x4_to_f16(w[(i & 1) * 2 + 1]);
+    return __builtin_bit_cast(h8_t, u4_t{a[0], a[1], b[0], b[1]});
+  }
+}
+
+// Blocks whose loads are in flight per wave: the ring slot being processed
+// plus kRing - 1 ahead (32 VGPRs per slot).  Deeper rings at lower occupancy
+// measured no faster on gfx950.  One wave per work-group, one KV head each:
+// work-groups of 4 or 8 waves reading neighbouring heads measured no faster.
+template <class F>
+__global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_gqa(DecodeArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int SB = a.split_blocks;
+  // LDS layout (decode_lds_bytes): block ids, mass partials, value stage.
+  int32_t* tbl = reinterpret_cast<int32_t*>(smem);                          // [SB] block ids
+  float* pi_lds = reinterpret_cast<float*>(smem + (size_t)4 * SB);          // [8][SB]
+  u4_t* vstage = reinterpret_cast<u4_t*>(smem + (size_t)36 * SB);           // 16 x 16 chunks of 16 B
+
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15;
+  const int j = lane >> 4;
+
+  uint32_t w = blockIdx.x;
+  const uint32_t lgg_count = (uint32_t)a.n_layers * 8u;
+  const int lgg = (int)(w % lgg_count);
+  w /= lgg_count;
+  const int split = (int)(w % (uint32_t)a.n_splits);
+  const int s = (int)(w / (uint32_t)a.n_splits);
+  const int lr = lgg >> 3;
+  const int g = lgg & 7;
+  const int layer = a.layer_begin + lr;
+
+  int r0 = 0;
+  const bool report = (threadIdx.x == 0) && split == 0 && lgg == 0;
+  const int nb = seq_blocks(a.seq_lens, a.meta_off, s, a.max_nb, a.total_blocks, a.status,
+                            report, &r0);
+  const int b0 = split * SB;
+  if (nb < 0 || b0 >= nb) return;
+  const int b1 = min(nb, b0 + SB);
+  const int n = a.seq_lens[s];
+
+  // The split's block ids go to LDS once, so that no later block-id read waits
+  // on the vector-memory counter behind the in-flight K/V loads.
+  for (int i = threadIdx.x; i < b1 - b0; i += 64)
+    tbl[i] = a.table[(size_t)s * a.max_nb + b0 + i];
+  __syncthreads();
+
+  // B operand of QK: queries of the group, rows 8..15 zero.
+  h8_t qb[4];
+  if (c < kGroup) {
+    const uint16_t* qp =
+        a.q + ((((size_t)s * a.num_layers + layer) * kQHeads + kGroup * g + c) * kHeadDim);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qb[i] = *reinterpret_cast<const h8_t*>(qp + qk_elem<F>(i, j));
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qb[i] = h8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+
+  constexpr int64_t kLayerBytes = 16 * (int64_t)tile_bytes<F>();   // one block, one layer
+  const size_t block_stride = (size_t)a.num_layers * kLayerBytes;
+  const size_t tile_off = (size_t)layer * kLayerBytes + (size_t)g * tile_bytes<F>();
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  f4_t acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = f4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Physical block of logical block bidx of this split; positions past the
+  // split's end reuse its last block (a cached, in-bounds tile whose data is
+  // masked), and ids outside the pool read block 0 and are masked.
+  auto slot_block = [&](int bidx, bool* ok) -> const uint8_t* {
+    const int clamped = min(bidx, b1 - 1);
+    const int pid = tbl[clamped - b0];
+    const bool in_pool = pid >= 0 && (int64_t)pid < a.pool_blocks;
+    *ok = in_pool && bidx < b1;
+    return a.pool + (size_t)(in_pool ? pid : 0) * block_stride + tile_off;
+  };
+
+  constexpr int kRing = F::kRing;
+  BlockRegs<F> ring[kRing];
+  bool ring_ok[kRing];
+#pragma unroll
+  for (int k = 0; k < kRing; ++k)
+    load_block(ring[k], slot_block(b0 + k, &ring_ok[k]), lane, c, j);
+
+  bool saw_bad = false;
+  for (int bbase = b0; bbase < b1; bbase += kRing) {
+#pragma unroll
+    for (int k = 0; k < kRing; ++k) {
+      const int b = bbase + k;
+      const bool active = b < b1;
+      const bool cur_ok = ring_ok[k];
+      saw_bad |= active && !cur_ok;
+      const int valid = cur_ok ? min(16, n - 16 * b) : 0;
+
+      // ---- value tile to LDS (the slot's value registers are free after this)
+      stage_values<F>(ring[k], vstage, lane);
+
+      // ---- logits of 16 tokens x 16 (8 real) heads
+      f4_t sacc = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_operand<F>(ring[k], i), qb[i], sacc,
+                                                      0, 0, 0);
+
+      // ---- refill this slot with the block kRing ahead
+      load_block(ring[k], slot_block(b + kRing, &ring_ok[k]), lane, c, j);
+
+      float sv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[i] = sacc[i] * a.scale_log2;
+      if (valid < 16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * j + i >= valid) sv[i] = -INFINITY;
+      }
+
+      // ---- online softmax (per head = per c; the 4 lanes j share a head)
+      float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      bm = fmaxf(bm, xor_f(bm, 16));
+      bm = fmaxf(bm, xor_f(bm, 32));
+      const float m_new = fmaxf(m_run, bm);
+      const bool live = m_new != -INFINITY;
+      const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      float pv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pv[i] = live ? __builtin_amdgcn_exp2f(sv[i] - m_new) : 0.f;
+      const float ps = (pv[0] + pv[1]) + (pv[2] + pv[3]);
+      l_run = l_run * alpha + ps;
+      float bs = ps + xor_f(ps, 16);
+      bs += xor_f(bs, 32);
+
+      if (__ballot(c < kGroup && alpha != 1.f) != 0ull) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] *= alpha;
+        if (c < kGroup)
+          for (int idx = j; idx < b - b0; idx += 4) pi_lds[c * SB + idx] *= alpha;
+      }
+      if (active && c < kGroup && j == 0) pi_lds[c * SB + (b - b0)] = bs;
+      m_run = m_new;
+
+      // ---- PV: transposed value rows from LDS
+      u4_t R[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) R[i] = vstage[(4 * j + i) * 16 + c];
+      if (valid < 16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * j + i >= valid) R[i] = u4_t{0u, 0u, 0u, 0u};
+      }
+      const h4_t pb = h4_t{(_Float16)pv[0], (_Float16)pv[1], (_Float16)pv[2], (_Float16)pv[3]};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo01 = __builtin_amdgcn_perm(R[1][q], R[0][q], 0x05040100u);
+        const uint32_t lo23 = __builtin_amdgcn_perm(R[3][q], R[2][q], 0x05040100u);
+        const uint32_t hi01 = __builtin_amdgcn_perm(R[1][q], R[0][q], 0x07060302u);
+        const uint32_t hi23 = __builtin_amdgcn_perm(R[3][q], R[2][q], 0x07060302u);
+        acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+            __builtin_bit_cast(h4_t, u2_t{lo01, lo23}), pb, acc[2 * q], 0, 0, 0);
+        acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+            __builtin_bit_cast(h4_t, u2_t{hi01, hi23}), pb, acc[2 * q + 1], 0, 0, 0);
+      }
+    }
+  }
+  if (saw_bad && lane == 0) flag(a.status, KVS_DEV_BAD_BLOCK_ID);
+
+  // ---- split epilogue: statistics, partial output, mass partials
+  float lt = l_run + xor_f(l_run, 16);
+  lt += xor_f(lt, 32);
+  const size_t st = (((size_t)s * a.n_layers + lr) * kQHeads + kGroup * g + c) * a.n_splits + split;
+  if (c < kGroup) {
+    if (j == 0) a.ml[st] = make_float2(m_run, lt);
+    float* op = a.opart + st * kHeadDim + 32 * j;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<f4_t*>(op + 8 * i) = f4_t{acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
+      *reinterpret_cast<f4_t*>(op + 8 * i + 4) = f4_t{acc[4][i], acc[5][i], acc[6][i], acc[7][i]};
+    }
+  }
+  __syncthreads();
+  const int cnt = b1 - b0;
+  for (int hh = 0; hh < kGroup; ++hh) {
+    float* dst = a.pi + ((size_t)lr * kQHeads + kGroup * g + hh) * a.total_blocks + r0 + b0;
+    for (int bb = lane; bb < cnt; bb += 64) dst[bb] = pi_lds[hh * SB + bb];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// combine_splits: one wave per (s, layer, head).  Lane handles d = 2 lane, +1.
+//   M = max_k m_k, Lambda = sum_k l_k 2^(m_k - M), w_k = 2^(m_k - M) / Lambda,
+//   out = sum_k w_k o_k (fp16), and w_k is kept for the mass reduction.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(64) combine_splits(CombineArgs a) {
+  const int lane = threadIdx.x;
+  uint32_t w = blockIdx.x;
+  const int h = (int)(w % kQHeads);
+  w /= kQHeads;
+  const int lr = (int)(w % (uint32_t)a.n_layers);
+  const int s = (int)(w / (uint32_t)a.n_layers);
+  const int layer = a.layer_begin + lr;
+  uint32_t* outp = reinterpret_cast<uint32_t*>(
+      a.out + ((((size_t)s * a.num_layers + layer) * kQHeads + h) * kHeadDim));
+
+  int r0 = 0;
+  const int nb = seq_blocks(a.seq_lens, a.meta_off, s, a.max_nb, a.total_blocks, a.status,
+                            false, &r0);
+  if (nb <= 0) {
+    outp[lane] = 0u;
+    return;
+  }
+  const int nsp = (nb + a.split_blocks - 1) / a.split_blocks;
+  const size_t base = (((size_t)s * a.n_layers + lr) * kQHeads + h) * a.n_splits;
+
+  float M = -INFINITY;
+  for (int k = lane; k < nsp; k += 64) M = fmaxf(M, a.ml[base + k].x);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, xor_f(M, m));
+  double L = 0.0;
+  if (M != -INFINITY)
+    for (int k = lane; k < nsp; k += 64) {
+      const float2 v = a.ml[base + k];
+      L += (double)v.y * (double)__builtin_amdgcn_exp2f(v.x - M);
+    }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) L += __shfl_xor(L, m, 64);
+  const bool dead = !(L > 0.0);
+  const double invL = dead ? 0.0 : 1.0 / L;
+
+  for (int k = lane; k < nsp; k += 64) {
+    const float2 v = a.ml[base + k];
+    a.wsplit[base + k] = dead ? 0.f : (float)((double)__builtin_amdgcn_exp2f(v.x - M) * invL);
+  }
+  float o0 = 0.f, o1 = 0.f;
+  for (int k = 0; k < nsp; ++k) {
+    const float2 v = a.ml[base + k];
+    const float wk = dead ? 0.f : (float)((double)__builtin_amdgcn_exp2f(v.x - M) * invL);
+    const float2 ov = reinterpret_cast<const float2*>(a.opart + (base + k) * kHeadDim)[lane];
+    o0 = fmaf(wk, ov.x, o0);
+    o1 = fmaf(wk, ov.y, o1);
+  }
+  const _Float16 h0 = (_Float16)o0, h1 = (_Float16)o1;
+  outp[lane] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// block_mass: mass[s, b] = sum over (layer, query head) of pi * w_split, fp64
+// accumulation in a fixed order (row order within each wave, then waves in
+// order), so the result depends only on logical indices.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kMassThreads) block_mass(MassArgs a) {
+  __shared__ double red[kMassThreads / 64][64];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  constexpr int kWaves = kMassThreads / 64;
+  const int s = blockIdx.y;
+  int r0 = 0;
+  const int nb = seq_blocks(a.seq_lens, a.meta_off, s, a.max_nb, a.total_blocks, a.status,
+                            false, &r0);
+  if (nb <= 0 || (int)blockIdx.x * 64 >= nb) return;
+  const int b = blockIdx.x * 64 + lane;
+  const bool act = b < nb;
+  const int r = r0 + (act ? b : 0);
+  const int split = (act ? b : 0) / a.split_blocks;
+  const int rows = a.n_layers * kQHeads;
+  double acc = 0.0;
+  if (act) {
+    const float* pcol = a.pi + r;
+    const float* wcol = a.wsplit + (size_t)s * a.n_layers * kQHeads * a.n_splits + split;
+#pragma unroll 8
+    for (int row = wv; row < rows; row += kWaves)
+      acc += (double)pcol[(size_t)row * a.total_blocks] * (double)wcol[(size_t)row * a.n_splits];
+  }
+  red[wv][lane] = acc;
+  __syncthreads();
+  if (wv == 0 && act) {
+    double t = 0.0;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) t += red[k][lane];
+    if (a.accumulate) t += (double)a.mass[r];
+    a.mass[r] = (float)t;
+  }
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int batch, hipStream_t stream) {
+  const uint64_t wgs = (uint64_t)batch * a.n_splits * a.n_layers * 8u;
+  const size_t lds = decode_lds_bytes(a.split_blocks);
+  if (lds > kMaxDecodeLds) return hipErrorInvalidValue;
+  if (a.kv_format == KVS_KV_KIVI2) return launch_decode_kivi(a, batch, stream);
+  if (a.kv_format == KVS_KV_E4M3)
+    hipLaunchKernelGGL(paged_decode_gqa<KvE4M3>, dim3((uint32_t)wgs), dim3(64), lds, stream, a);
+  else
+    hipLaunchKernelGGL(paged_decode_gqa<KvF16>, dim3((uint32_t)wgs), dim3(64), lds, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineArgs& a, int batch, hipStream_t stream) {
+  const uint64_t wgs = (uint64_t)batch * a.n_layers * kQHeads;
+  hipLaunchKernelGGL(combine_splits, dim3((uint32_t)wgs), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_mass(const MassArgs& a, int batch, hipStream_t stream) {
+  const dim3 grid((a.max_nb + 63) / 64, batch);
+  hipLaunchKernelGGL(block_mass, grid, dim3(kMassThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace kvs

@@ -186,6 +186,7 @@ struct KiviAdvanceArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int batch, hipStream_t stream);
+hipError_t launch_decode_kivi(const DecodeArgs& a, int batch, hipStream_t stream);
 hipError_t launch_kivi_quantize(const KiviQuantArgs& a, hipStream_t stream);
 hipError_t launch_kivi_advance(const KiviAdvanceArgs& adv, const KiviQuantArgs& q, int batch,
                                hipStream_t stream);
