@@ -31,6 +31,9 @@ def _p(x):
     if x is None:
         return None
     if isinstance(x, torch.Tensor):
+        if not x.is_contiguous():
+            raise ValueError("tensors passed to the library must be contiguous "
+                             f"(got shape {tuple(x.shape)}, strides {x.stride()})")
         return ctypes.c_void_p(x.data_ptr())
     return ctypes.c_void_p(int(x))
 

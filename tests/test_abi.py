@@ -271,3 +271,12 @@ def test_kivi_quant_len_rule_matches_the_oracle():
     from paged_gqa_kv_amd.session import kivi_quant_len
     for n in list(range(0, 400)) + [131072, 1048576]:
         assert kivi_quant_len(n) == KV.quant_boundary(n)
+
+
+def test_binding_rejects_non_contiguous_tensors():
+    import torch
+    x = torch.zeros(4, 8)
+    with pytest.raises(ValueError, match="contiguous"):
+        api._p(x.t())
+    assert api._p(x).value == x.data_ptr()
+
