@@ -48,9 +48,13 @@ constexpr size_t kAlign = 256;
 // reads in flight to stay at HBM bandwidth, and on gfx950 about 56 KiB per
 // compute unit; within those, the longest splits measured fastest (fewer
 // partial results, longer streams per wave, fewer resident streams).
+// The KIVI decode is bound by instruction issue, not by bytes in flight: there
+// shorter splits measured faster (more, shorter waves even out the end of the
+// grid; 128 blocks: +3 % over 256 at 128K tokens, 64 slower again).
 constexpr uint64_t kChipInflightBytes = 16ull << 20;
 constexpr uint64_t kCuInflightBytes = 56ull << 10;
 constexpr int32_t kMaxAutoSplit = 1024;
+constexpr int32_t kMaxAutoSplitKivi = 128;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -115,7 +119,8 @@ bool format_valid(int32_t f) { return f == KVS_KV_FP16 || f == KVS_KV_E4M3 || f 
 int32_t choose_split(int32_t batch, int32_t max_nb, int32_t n_layers, int32_t kv_format) {
   const uint64_t streams = (uint64_t)batch * (uint64_t)n_layers * 8u;
   const uint64_t wave_inflight = wave_inflight_bytes(kv_format);
-  for (int32_t cand = kMaxAutoSplit; cand >= 16; cand >>= 1) {
+  const int32_t top = kv_format == KVS_KV_KIVI2 ? kMaxAutoSplitKivi : kMaxAutoSplit;
+  for (int32_t cand = top; cand >= 16; cand >>= 1) {
     const uint64_t waves = streams * (uint64_t)((max_nb + cand - 1) / cand);
     uint64_t per_cu = kvs::kLdsPerCu / kvs::decode_lds_bytes(cand);
     if (per_cu > 4u * kvs::kDecodeWavesPerSimd) per_cu = 4u * kvs::kDecodeWavesPerSimd;

@@ -75,7 +75,7 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
   const int c = lane & 15;
   const int j = lane >> 4;
 
-  uint32_t w = blockIdx.x;
+  uint32_t w = xcd_item(blockIdx.x, gridDim.x);
   const uint32_t lgg_count = (uint32_t)a.n_layers * 8u;
   const int lgg = (int)(w % lgg_count);
   w /= lgg_count;

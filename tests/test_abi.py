@@ -75,7 +75,8 @@ def test_split_policy():
     assert sb(8, 512, 4, "fp16") == 128     # 1,024 waves x 16 KiB in flight
     assert sb(8, 512, 4, "e4m3") == 64      # 2,048 waves x 8 KiB
     assert sb(1, 64, 1, "fp16") == 16       # too small to fill the chip: shortest split
-    assert sb(1, 8192, 80, "kivi2") == 256  # 6 KiB per wave: 12 waves per CU needed
+    assert sb(1, 8192, 80, "kivi2") == 128  # issue-bound: at most 128 blocks per split
+    assert sb(1, 256, 1, "kivi2") == 16     # 6 KiB per wave: 16 MiB in flight needs many waves
     assert api.score_workspace_bytes(1, 65536) >= 256 + 4 * 256
     assert api.score_workspace_bytes(0, 10) == 0
 
