@@ -362,14 +362,28 @@ __global__ void __launch_bounds__(64) combine_splits(CombineArgs a) {
     const float2 v = a.ml[base + k];
     a.wsplit[base + k] = dead ? 0.f : (float)((double)__builtin_amdgcn_exp2f(v.x - M) * invL);
   }
+  // Weighted sum of the partial outputs in split order.  Eight splits per
+  // round: their statistics and partial rows are all loaded before the first
+  // is used, so eight 512-byte rows are in flight per wave instead of one.
   float o0 = 0.f, o1 = 0.f;
-  for (int k = 0; k < nsp; ++k) {
-    const float2 v = a.ml[base + k];
+  auto add_split = [&](float2 v, float2 ov) {
     const float wk = dead ? 0.f : (float)((double)__builtin_amdgcn_exp2f(v.x - M) * invL);
-    const float2 ov = reinterpret_cast<const float2*>(a.opart + (base + k) * kHeadDim)[lane];
     o0 = fmaf(wk, ov.x, o0);
     o1 = fmaf(wk, ov.y, o1);
+  };
+  const float2* orow = reinterpret_cast<const float2*>(a.opart + base * kHeadDim) + lane;
+  int k = 0;
+  for (; k + 8 <= nsp; k += 8) {
+    float2 v[8], ov[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      v[u] = a.ml[base + k + u];
+      ov[u] = orow[(size_t)(k + u) * (kHeadDim / 2)];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) add_split(v[u], ov[u]);
   }
+  for (; k < nsp; ++k) add_split(a.ml[base + k], orow[(size_t)k * (kHeadDim / 2)]);
   const _Float16 h0 = (_Float16)o0, h1 = (_Float16)o1;
   outp[lane] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
                ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
@@ -377,20 +391,25 @@ __global__ void __launch_bounds__(64) combine_splits(CombineArgs a) {
 
 // ---------------------------------------------------------------------------
 // block_mass: mass[s, b] = sum over (layer, query head) of pi * w_split, fp64
-// accumulation in a fixed order (row order within each wave, then waves in
-// order), so the result depends only on logical indices.
+// accumulation in a fixed order, so the result depends only on logical
+// indices.  A work-group takes 32 blocks; its 32 row streams (two per wave:
+// lanes 0..31 and 32..63, each reading 128 contiguous bytes of a row) take rows
+// q, q + 32, q + 64, ... in order, and the 32 stream sums are added in stream
+// order.  32 blocks per work-group (not 64) gives a 128K-token sequence 256
+// work-groups, one per compute unit: with 128, half the chip's load slots sat
+// idle and the kernel read at half the rate.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(kMassThreads) block_mass(MassArgs a) {
-  __shared__ double red[kMassThreads / 64][64];
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  constexpr int kWaves = kMassThreads / 64;
+  constexpr int kStreams = kMassThreads / kMassCols;
+  __shared__ double red[kStreams][kMassCols];
+  const int col = threadIdx.x % kMassCols;
+  const int q = threadIdx.x / kMassCols;     // row stream; a wave holds two
   const int s = blockIdx.y;
   int r0 = 0;
   const int nb = seq_blocks(a.seq_lens, a.meta_off, s, a.max_nb, a.total_blocks, a.status,
                             false, &r0);
-  if (nb <= 0 || (int)blockIdx.x * 64 >= nb) return;
-  const int b = blockIdx.x * 64 + lane;
+  if (nb <= 0 || (int)blockIdx.x * kMassCols >= nb) return;
+  const int b = blockIdx.x * kMassCols + col;
   const bool act = b < nb;
   const int r = r0 + (act ? b : 0);
   const int split = (act ? b : 0) / a.split_blocks;
@@ -399,16 +418,29 @@ __global__ void __launch_bounds__(kMassThreads) block_mass(MassArgs a) {
   if (act) {
     const float* pcol = a.pi + r;
     const float* wcol = a.wsplit + (size_t)s * a.n_layers * kQHeads * a.n_splits + split;
-#pragma unroll 8
-    for (int row = wv; row < rows; row += kWaves)
-      acc += (double)pcol[(size_t)row * a.total_blocks] * (double)wcol[(size_t)row * a.n_splits];
+    // Rounds of 16 rows: all 32 loads of a round are issued before the first
+    // product (rows past the end re-read the last row, unconditionally, so no
+    // load sits behind a branch); the sum runs in row order and skips them.
+    constexpr int kRound = 16;
+    for (int row0 = q; row0 < rows; row0 += kStreams * kRound) {
+      float pv[kRound], wt[kRound];
+#pragma unroll
+      for (int u = 0; u < kRound; ++u) {
+        const int row = min(row0 + u * kStreams, rows - 1);
+        pv[u] = pcol[(size_t)row * a.total_blocks];
+        wt[u] = wcol[(size_t)row * a.n_splits];
+      }
+#pragma unroll
+      for (int u = 0; u < kRound; ++u)
+        if (row0 + u * kStreams < rows) acc += (double)pv[u] * (double)wt[u];
+    }
   }
-  red[wv][lane] = acc;
+  red[q][col] = acc;
   __syncthreads();
-  if (wv == 0 && act) {
+  if (q == 0 && act) {
     double t = 0.0;
 #pragma unroll
-    for (int k = 0; k < kWaves; ++k) t += red[k][lane];
+    for (int k = 0; k < kStreams; ++k) t += red[k][col];
     if (a.accumulate) t += (double)a.mass[r];
     a.mass[r] = (float)t;
   }
@@ -433,7 +465,7 @@ hipError_t launch_combine(const CombineArgs& a, int batch, hipStream_t stream) {
 }
 
 hipError_t launch_mass(const MassArgs& a, int batch, hipStream_t stream) {
-  const dim3 grid((a.max_nb + 63) / 64, batch);
+  const dim3 grid((a.max_nb + kMassCols - 1) / kMassCols, batch);
   hipLaunchKernelGGL(block_mass, grid, dim3(kMassThreads), 0, stream, a);
   return hipGetLastError();
 }

@@ -8,7 +8,8 @@
 
 namespace kvs {
 
-constexpr int kMassThreads = 1024;   // 16 waves share one 64-block column
+constexpr int kMassThreads = 1024;   // 16 waves share one 32-block column group
+constexpr int kMassCols = 32;
 constexpr int kScoreThreads = 256;   // records per scoring work-group
 constexpr size_t kMaxDecodeLds = 65536;  // dynamic LDS a decode work-group may request
 constexpr size_t kLdsPerCu = 163840;     // gfx950: 160 KiB of LDS per compute unit
