@@ -1,12 +1,9 @@
-// Paged GQA decode kernels over fp16 and FP8 E4M3 pools, and the split
-// combine and block-mass reduction shared with the KIVI decode:
+// Paged GQA decode kernel over fp16 and FP8 E4M3 pools:
 //   paged_decode_gqa  split-K decode: one wave per (sequence, layer, KV head,
 //                     split of blocks); QK^T and PV on MFMA; online softmax;
 //                     per-(layer, head, block) probability-mass partials.
-//   combine_splits    merges the splits of each (sequence, layer, head) into the
-//                     fp16 output and the per-split normalising weights.
-//   block_mass        sums the mass partials of every (layer, query head) into
-//                     one fp32 number per (sequence, block), in a fixed order.
+// The split combine and block-mass reduction that follow it are in
+// kvs_combine.hip.
 //
 // Sources: "KV-Cache Offloading for LLM Inference -- Visual Reference"
 // Sec. 2 (attention), Sec. 11 (EMA), Sec. 12 (priority, cut points);
@@ -317,135 +314,6 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_gqa(Deco
   }
 }
 
-// ---------------------------------------------------------------------------
-// combine_splits: one wave per (s, layer, head).  Lane handles d = 2 lane, +1.
-//   M = max_k m_k, Lambda = sum_k l_k 2^(m_k - M), w_k = 2^(m_k - M) / Lambda,
-//   out = sum_k w_k o_k (fp16), and w_k is kept for the mass reduction.
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(64) combine_splits(CombineArgs a) {
-  const int lane = threadIdx.x;
-  uint32_t w = blockIdx.x;
-  const int h = (int)(w % kQHeads);
-  w /= kQHeads;
-  const int lr = (int)(w % (uint32_t)a.n_layers);
-  const int s = (int)(w / (uint32_t)a.n_layers);
-  const int layer = a.layer_begin + lr;
-  uint32_t* outp = reinterpret_cast<uint32_t*>(
-      a.out + ((((size_t)s * a.num_layers + layer) * kQHeads + h) * kHeadDim));
-
-  int r0 = 0;
-  const int nb = seq_blocks(a.seq_lens, a.meta_off, s, a.max_nb, a.total_blocks, a.status,
-                            false, &r0);
-  if (nb <= 0) {
-    outp[lane] = 0u;
-    return;
-  }
-  const int nsp = (nb + a.split_blocks - 1) / a.split_blocks;
-  const size_t base = (((size_t)s * a.n_layers + lr) * kQHeads + h) * a.n_splits;
-
-  float M = -INFINITY;
-  for (int k = lane; k < nsp; k += 64) M = fmaxf(M, a.ml[base + k].x);
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, xor_f(M, m));
-  double L = 0.0;
-  if (M != -INFINITY)
-    for (int k = lane; k < nsp; k += 64) {
-      const float2 v = a.ml[base + k];
-      L += (double)v.y * (double)__builtin_amdgcn_exp2f(v.x - M);
-    }
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) L += __shfl_xor(L, m, 64);
-  const bool dead = !(L > 0.0);
-  const double invL = dead ? 0.0 : 1.0 / L;
-
-  for (int k = lane; k < nsp; k += 64) {
-    const float2 v = a.ml[base + k];
-    a.wsplit[base + k] = dead ? 0.f : (float)((double)__builtin_amdgcn_exp2f(v.x - M) * invL);
-  }
-  // Weighted sum of the partial outputs in split order.  Eight splits per
-  // round: their statistics and partial rows are all loaded before the first
-  // is used, so eight 512-byte rows are in flight per wave instead of one.
-  float o0 = 0.f, o1 = 0.f;
-  auto add_split = [&](float2 v, float2 ov) {
-    const float wk = dead ? 0.f : (float)((double)__builtin_amdgcn_exp2f(v.x - M) * invL);
-    o0 = fmaf(wk, ov.x, o0);
-    o1 = fmaf(wk, ov.y, o1);
-  };
-  const float2* orow = reinterpret_cast<const float2*>(a.opart + base * kHeadDim) + lane;
-  int k = 0;
-  for (; k + 8 <= nsp; k += 8) {
-    float2 v[8], ov[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      v[u] = a.ml[base + k + u];
-      ov[u] = orow[(size_t)(k + u) * (kHeadDim / 2)];
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) add_split(v[u], ov[u]);
-  }
-  for (; k < nsp; ++k) add_split(a.ml[base + k], orow[(size_t)k * (kHeadDim / 2)]);
-  const _Float16 h0 = (_Float16)o0, h1 = (_Float16)o1;
-  outp[lane] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-}
-
-// ---------------------------------------------------------------------------
-// block_mass: mass[s, b] = sum over (layer, query head) of pi * w_split, fp64
-// accumulation in a fixed order, so the result depends only on logical
-// indices.  A work-group takes 32 blocks; its 32 row streams (two per wave:
-// lanes 0..31 and 32..63, each reading 128 contiguous bytes of a row) take rows
-// q, q + 32, q + 64, ... in order, and the 32 stream sums are added in stream
-// order.  32 blocks per work-group (not 64) gives a 128K-token sequence 256
-// work-groups, one per compute unit: with 128, half the chip's load slots sat
-// idle and the kernel read at half the rate.
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(kMassThreads) block_mass(MassArgs a) {
-  constexpr int kStreams = kMassThreads / kMassCols;
-  __shared__ double red[kStreams][kMassCols];
-  const int col = threadIdx.x % kMassCols;
-  const int q = threadIdx.x / kMassCols;     // row stream; a wave holds two
-  const int s = blockIdx.y;
-  int r0 = 0;
-  const int nb = seq_blocks(a.seq_lens, a.meta_off, s, a.max_nb, a.total_blocks, a.status,
-                            false, &r0);
-  if (nb <= 0 || (int)blockIdx.x * kMassCols >= nb) return;
-  const int b = blockIdx.x * kMassCols + col;
-  const bool act = b < nb;
-  const int r = r0 + (act ? b : 0);
-  const int split = (act ? b : 0) / a.split_blocks;
-  const int rows = a.n_layers * kQHeads;
-  double acc = 0.0;
-  if (act) {
-    const float* pcol = a.pi + r;
-    const float* wcol = a.wsplit + (size_t)s * a.n_layers * kQHeads * a.n_splits + split;
-    // Rounds of 16 rows: all 32 loads of a round are issued before the first
-    // product (rows past the end re-read the last row, unconditionally, so no
-    // load sits behind a branch); the sum runs in row order and skips them.
-    constexpr int kRound = 16;
-    for (int row0 = q; row0 < rows; row0 += kStreams * kRound) {
-      float pv[kRound], wt[kRound];
-#pragma unroll
-      for (int u = 0; u < kRound; ++u) {
-        const int row = min(row0 + u * kStreams, rows - 1);
-        pv[u] = pcol[(size_t)row * a.total_blocks];
-        wt[u] = wcol[(size_t)row * a.n_splits];
-      }
-#pragma unroll
-      for (int u = 0; u < kRound; ++u)
-        if (row0 + u * kStreams < rows) acc += (double)pv[u] * (double)wt[u];
-    }
-  }
-  red[q][col] = acc;
-  __syncthreads();
-  if (q == 0 && act) {
-    double t = 0.0;
-#pragma unroll
-    for (int k = 0; k < kStreams; ++k) t += red[k][col];
-    if (a.accumulate) t += (double)a.mass[r];
-    a.mass[r] = (float)t;
-  }
-}
-
 hipError_t launch_decode(const DecodeArgs& a, int batch, hipStream_t stream) {
   const uint64_t wgs = (uint64_t)batch * a.n_splits * a.n_layers * 8u;
   const size_t lds = decode_lds_bytes(a.split_blocks);
@@ -455,18 +323,6 @@ hipError_t launch_decode(const DecodeArgs& a, int batch, hipStream_t stream) {
     hipLaunchKernelGGL(paged_decode_gqa<KvE4M3>, dim3((uint32_t)wgs), dim3(64), lds, stream, a);
   else
     hipLaunchKernelGGL(paged_decode_gqa<KvF16>, dim3((uint32_t)wgs), dim3(64), lds, stream, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_combine(const CombineArgs& a, int batch, hipStream_t stream) {
-  const uint64_t wgs = (uint64_t)batch * a.n_layers * kQHeads;
-  hipLaunchKernelGGL(combine_splits, dim3((uint32_t)wgs), dim3(64), 0, stream, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_mass(const MassArgs& a, int batch, hipStream_t stream) {
-  const dim3 grid((a.max_nb + kMassCols - 1) / kMassCols, batch);
-  hipLaunchKernelGGL(block_mass, grid, dim3(kMassThreads), 0, stream, a);
   return hipGetLastError();
 }
 
