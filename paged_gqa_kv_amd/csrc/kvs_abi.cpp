@@ -48,13 +48,17 @@ constexpr size_t kAlign = 256;
 // reads in flight to stay at HBM bandwidth, and on gfx950 about 56 KiB per
 // compute unit; within those, the longest splits measured fastest (fewer
 // partial results, longer streams per wave, fewer resident streams).
-// The KIVI decode is bound by instruction issue, not by bytes in flight: there
-// shorter splits measured faster (more, shorter waves even out the end of the
-// grid; 128 blocks: +3 % over 256 at 128K tokens, 64 slower again).
+// The E4M3 and KIVI decodes are limited by their instruction stream more than
+// by bytes in flight, and measured fastest at shorter splits than fp16: E4M3
+// at 512 blocks (one wave per SIMD at 1,024 leaves its conversions and
+// softmax exposed: -10 %), KIVI at 128 (more, shorter waves even out the end
+// of the grid: +3 % over 256 at 128K tokens; 64 slower again).
 constexpr uint64_t kChipInflightBytes = 16ull << 20;
 constexpr uint64_t kCuInflightBytes = 56ull << 10;
 constexpr int32_t kMaxAutoSplit = 1024;
+constexpr int32_t kMaxAutoSplitE4M3 = 512;
 constexpr int32_t kMaxAutoSplitKivi = 128;
+constexpr uint64_t kChipSimds = 1024;   // gfx950: 256 compute units x 4 SIMDs
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -101,16 +105,37 @@ int check_counts(int32_t batch, int32_t max_blocks) {
   return KVS_OK;
 }
 
-// The largest power-of-two split in [16, 1024] whose launch keeps enough
-// bytes in flight on the whole chip (wave count) and per compute unit (waves
-// that fit the LDS a split needs, at most kDecodeWavesPerSimd per SIMD).
-// Reads one decode wave keeps in flight: two fp16 or E4M3 blocks (K and V tiles
-// of its KV head), or two 32-token quantised pairs (4 tiles of 768 bytes each).
+// The largest power-of-two split in [16, the format's cap] whose launch keeps
+// enough bytes in flight on the whole chip (wave count) and per compute unit
+// (waves that fit the LDS a split needs, at most the kernel's waves per SIMD).
+// Reads one decode wave keeps in flight: two fp16 blocks or two two-block E4M3
+// steps (K and V tiles of its KV head), or two 32-token quantised pairs (4
+// tiles of 768 bytes each).
 uint64_t wave_inflight_bytes(int32_t kv_format) {
   switch (kv_format) {
     case KVS_KV_FP16: return 2ull * 2ull * 4096ull;
-    case KVS_KV_E4M3: return 2ull * 2ull * 2048ull;
+    case KVS_KV_E4M3: return 2ull * 2ull * 2ull * 2048ull;
     default: return 2ull * 4ull * (uint64_t)kvs::kKiviTileBytes;
+  }
+}
+
+uint64_t waves_per_simd(int32_t kv_format) {
+  return kv_format == KVS_KV_E4M3 ? kvs::kDecodeWavesPerSimdE4M3 : kvs::kDecodeWavesPerSimd;
+}
+
+// Waves the grid must provide per SIMD (1,024 SIMDs on gfx950).  The E4M3
+// decode needs two: with one wave per SIMD its conversions and softmax are not
+// hidden behind the loads (8 sequences x 8K x 4 layers: 4.5 TB/s at split 128,
+// 1,024 waves, against 5.0 TB/s at split 64, 2,048 waves).
+uint64_t min_grid_waves(int32_t kv_format) {
+  return kv_format == KVS_KV_E4M3 ? 2u * kChipSimds : 0u;
+}
+
+int32_t max_auto_split(int32_t kv_format) {
+  switch (kv_format) {
+    case KVS_KV_FP16: return kMaxAutoSplit;
+    case KVS_KV_E4M3: return kMaxAutoSplitE4M3;
+    default: return kMaxAutoSplitKivi;
   }
 }
 
@@ -119,12 +144,13 @@ bool format_valid(int32_t f) { return f == KVS_KV_FP16 || f == KVS_KV_E4M3 || f 
 int32_t choose_split(int32_t batch, int32_t max_nb, int32_t n_layers, int32_t kv_format) {
   const uint64_t streams = (uint64_t)batch * (uint64_t)n_layers * 8u;
   const uint64_t wave_inflight = wave_inflight_bytes(kv_format);
-  const int32_t top = kv_format == KVS_KV_KIVI2 ? kMaxAutoSplitKivi : kMaxAutoSplit;
-  for (int32_t cand = top; cand >= 16; cand >>= 1) {
+  const uint64_t cu_waves = 4u * waves_per_simd(kv_format);
+  for (int32_t cand = max_auto_split(kv_format); cand >= 16; cand >>= 1) {
     const uint64_t waves = streams * (uint64_t)((max_nb + cand - 1) / cand);
     uint64_t per_cu = kvs::kLdsPerCu / kvs::decode_lds_bytes(cand);
-    if (per_cu > 4u * kvs::kDecodeWavesPerSimd) per_cu = 4u * kvs::kDecodeWavesPerSimd;
-    if (waves * wave_inflight >= kChipInflightBytes && per_cu * wave_inflight >= kCuInflightBytes)
+    if (per_cu > cu_waves) per_cu = cu_waves;
+    if (waves * wave_inflight >= kChipInflightBytes && per_cu * wave_inflight >= kCuInflightBytes &&
+        waves >= min_grid_waves(kv_format))
       return cand;
   }
   return 16;

@@ -44,18 +44,28 @@ namespace kvs {
 struct KvF16 {
   static constexpr int kElemBytes = 2;
   static constexpr int kLoads = 4;   // 16-byte loads per lane per tile
+  static constexpr int kPer = 1;     // blocks per step
   static constexpr int kRing = 2;    // ring slots (32 VGPRs each)
+  static constexpr int kWavesPerSimd = kDecodeWavesPerSimd;
 };
 struct KvE4M3 {                      // FP8 E4M3 codes, no scale
   static constexpr int kElemBytes = 1;
   static constexpr int kLoads = 2;
-  static constexpr int kRing = 2;    // 16 VGPRs each; 3 and 4 measured slower
+  static constexpr int kPer = 2;     // two blocks per step: more independent work per wave
+  static constexpr int kRing = 2;    // ring slots (32 VGPRs each); 3 measured no faster
+  static constexpr int kWavesPerSimd = kDecodeWavesPerSimdE4M3;
 };
 
 template <class F>
 struct BlockRegs {
   u4_t k[F::kLoads];
   u4_t v[F::kLoads];
+};
+
+// One ring slot: the kPer blocks of one step.
+template <class F>
+struct StepRegs {
+  BlockRegs<F> blk[F::kPer];
 };
 
 template <class F>
@@ -97,23 +107,30 @@ __device__ __forceinline__ u2_t e4m3x4_to_f16(uint32_t w) {
   return u2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
-// Value tile of one ring slot to LDS as row-major fp16 [16][128].
+// Value tile of block p of a step to the 4 KiB LDS stage, as stored: fp16
+// [16][128] (one block per step), or E4M3 codes [16][128] at byte 2048 p.
 template <class F>
-__device__ __forceinline__ void stage_values(const BlockRegs<F>& r, u4_t* vstage, int lane) {
+__device__ __forceinline__ void stage_values(const BlockRegs<F>& r, u4_t* vstage, int lane,
+                                             int p) {
+#pragma unroll
+  for (int i = 0; i < F::kLoads; ++i) vstage[p * 128 + i * 64 + lane] = r.v[i];
+}
+
+// The PV operand rows of block p: R[i] = 8 fp16 values, elements [8 c, 8 c + 8)
+// of value row 4 j + i (E4M3 codes are converted here, after the LDS read).
+template <class F>
+__device__ __forceinline__ void value_rows(const u4_t* vstage, int p, int j, int c, u4_t (&R)[4]) {
   if constexpr (F::kElemBytes == 2) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vstage[i * 64 + lane] = r.v[i];
+    for (int i = 0; i < 4; ++i) R[i] = vstage[(4 * j + i) * 16 + c];
   } else {
-    // load i, lane l: row 8 i + l / 8, elements [16 (l % 8), 16 (l % 8) + 16)
+    const uint8_t* tile = reinterpret_cast<const uint8_t*>(vstage) + 2048 * p;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const u2_t a = e4m3x4_to_f16(r.v[i][0]);
-      const u2_t b = e4m3x4_to_f16(r.v[i][1]);
-      const u2_t c2 = e4m3x4_to_f16(r.v[i][2]);
-      const u2_t d = e4m3x4_to_f16(r.v[i][3]);
-      const int base = (8 * i + (lane >> 3)) * 16 + 2 * (lane & 7);
-      vstage[base] = u4_t{a[0], a[1], b[0], b[1]};
-      vstage[base + 1] = u4_t{c2[0], c2[1], d[0], d[1]};
+    for (int i = 0; i < 4; ++i) {
+      const u2_t w = *reinterpret_cast<const u2_t*>(tile + (4 * j + i) * 128 + 8 * c);
+      const u2_t lo = e4m3x4_to_f16(w[0]);
+      const u2_t hi = e4m3x4_to_f16(w[1]);
+      R[i] = u4_t{lo[0], lo[1], hi[0], hi[1]};
     }
   }
 }
@@ -136,7 +153,7 @@ __device__ __forceinline__ h8_t key_operand(const BlockRegs<F>& r, int i) {
 // measured no faster on gfx950.  One wave per work-group, one KV head each:
 // work-groups of 4 or 8 waves reading neighbouring heads measured no faster.
 template <class F>
-__global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_gqa(DecodeArgs a) {
+__global__ void __launch_bounds__(64, F::kWavesPerSimd) paged_decode_gqa(DecodeArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int SB = a.split_blocks;
   // LDS layout (decode_lds_bytes): block ids, mass partials, value stage.
@@ -206,88 +223,119 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_gqa(Deco
   };
 
   constexpr int kRing = F::kRing;
-  BlockRegs<F> ring[kRing];
-  bool ring_ok[kRing];
+  constexpr int kPer = F::kPer;
+  StepRegs<F> ring[kRing];
+  bool ring_ok[kRing][kPer];
+  auto load_step = [&](StepRegs<F>& r, bool (&ok)[kPer], int bfirst) {
 #pragma unroll
-  for (int k = 0; k < kRing; ++k)
-    load_block(ring[k], slot_block(b0 + k, &ring_ok[k]), lane, c, j);
+    for (int p = 0; p < kPer; ++p)
+      load_block(r.blk[p], slot_block(bfirst + p, &ok[p]), lane, c, j);
+  };
+#pragma unroll
+  for (int k = 0; k < kRing; ++k) load_step(ring[k], ring_ok[k], b0 + k * kPer);
 
   bool saw_bad = false;
-  for (int bbase = b0; bbase < b1; bbase += kRing) {
+  for (int bbase = b0; bbase < b1; bbase += kRing * kPer) {
 #pragma unroll
     for (int k = 0; k < kRing; ++k) {
-      const int b = bbase + k;
-      const bool active = b < b1;
-      const bool cur_ok = ring_ok[k];
-      saw_bad |= active && !cur_ok;
-      const int valid = cur_ok ? min(16, n - 16 * b) : 0;
-
-      // ---- value tile to LDS (the slot's value registers are free after this)
-      stage_values<F>(ring[k], vstage, lane);
-
-      // ---- logits of 16 tokens x 16 (8 real) heads
-      f4_t sacc = f4_t{0.f, 0.f, 0.f, 0.f};
+      const int bs = bbase + k * kPer;        // first block of this step
+      bool active[kPer];
+      int valid[kPer];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_operand<F>(ring[k], i), qb[i], sacc,
-                                                      0, 0, 0);
-
-      // ---- refill this slot with the block kRing ahead
-      load_block(ring[k], slot_block(b + kRing, &ring_ok[k]), lane, c, j);
-
-      float sv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sv[i] = sacc[i] * a.scale_log2;
-      if (valid < 16) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (4 * j + i >= valid) sv[i] = -INFINITY;
+      for (int p = 0; p < kPer; ++p) {
+        active[p] = bs + p < b1;
+        saw_bad |= active[p] && !ring_ok[k][p];
+        valid[p] = ring_ok[k][p] ? min(16, n - 16 * (bs + p)) : 0;
       }
 
-      // ---- online softmax (per head = per c; the 4 lanes j share a head)
-      float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      // ---- value tiles to LDS (the slot's value registers are free after this)
+#pragma unroll
+      for (int p = 0; p < kPer; ++p) stage_values<F>(ring[k].blk[p], vstage, lane, p);
+
+      // ---- logits of 16 tokens x 16 (8 real) heads per block
+      f4_t sacc[kPer];
+#pragma unroll
+      for (int p = 0; p < kPer; ++p) sacc[p] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int p = 0; p < kPer; ++p)
+          sacc[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_operand<F>(ring[k].blk[p], i),
+                                                           qb[i], sacc[p], 0, 0, 0);
+
+      // ---- refill this slot with the step kRing ahead
+      load_step(ring[k], ring_ok[k], bs + kRing * kPer);
+
+      float sv[kPer][4];
+#pragma unroll
+      for (int p = 0; p < kPer; ++p) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[p][i] = sacc[p][i] * a.scale_log2;
+        if (valid[p] < 16) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (4 * j + i >= valid[p]) sv[p][i] = -INFINITY;
+        }
+      }
+
+      // ---- online softmax over the step (per head = per c; the 4 lanes j share a head)
+      float bm = -INFINITY;
+#pragma unroll
+      for (int p = 0; p < kPer; ++p)
+        bm = fmaxf(bm, fmaxf(fmaxf(sv[p][0], sv[p][1]), fmaxf(sv[p][2], sv[p][3])));
       bm = fmaxf(bm, xor_f(bm, 16));
       bm = fmaxf(bm, xor_f(bm, 32));
       const float m_new = fmaxf(m_run, bm);
       const bool live = m_new != -INFINITY;
       const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-      float pv[4];
+      float pv[kPer][4];
+      float bsum[kPer];
+      float ps_all = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pv[i] = live ? __builtin_amdgcn_exp2f(sv[i] - m_new) : 0.f;
-      const float ps = (pv[0] + pv[1]) + (pv[2] + pv[3]);
-      l_run = l_run * alpha + ps;
-      float bs = ps + xor_f(ps, 16);
-      bs += xor_f(bs, 32);
+      for (int p = 0; p < kPer; ++p) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pv[p][i] = live ? __builtin_amdgcn_exp2f(sv[p][i] - m_new) : 0.f;
+        const float ps = (pv[p][0] + pv[p][1]) + (pv[p][2] + pv[p][3]);
+        ps_all = p == 0 ? ps : ps_all + ps;
+        bsum[p] = ps + xor_f(ps, 16);
+        bsum[p] += xor_f(bsum[p], 32);
+      }
+      l_run = l_run * alpha + ps_all;
 
       if (__ballot(c < kGroup && alpha != 1.f) != 0ull) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[q] *= alpha;
         if (c < kGroup)
-          for (int idx = j; idx < b - b0; idx += 4) pi_lds[c * SB + idx] *= alpha;
+          for (int idx = j; idx < bs - b0; idx += 4) pi_lds[c * SB + idx] *= alpha;
       }
-      if (active && c < kGroup && j == 0) pi_lds[c * SB + (b - b0)] = bs;
+#pragma unroll
+      for (int p = 0; p < kPer; ++p)
+        if (active[p] && c < kGroup && j == 0) pi_lds[c * SB + (bs + p - b0)] = bsum[p];
       m_run = m_new;
 
       // ---- PV: transposed value rows from LDS
-      u4_t R[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) R[i] = vstage[(4 * j + i) * 16 + c];
-      if (valid < 16) {
+      for (int p = 0; p < kPer; ++p) {
+        u4_t R[4];
+        value_rows<F>(vstage, p, j, c, R);
+        if (valid[p] < 16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (4 * j + i >= valid) R[i] = u4_t{0u, 0u, 0u, 0u};
-      }
-      const h4_t pb = h4_t{(_Float16)pv[0], (_Float16)pv[1], (_Float16)pv[2], (_Float16)pv[3]};
+          for (int i = 0; i < 4; ++i)
+            if (4 * j + i >= valid[p]) R[i] = u4_t{0u, 0u, 0u, 0u};
+        }
+        const h4_t pb = h4_t{(_Float16)pv[p][0], (_Float16)pv[p][1], (_Float16)pv[p][2],
+                             (_Float16)pv[p][3]};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t lo01 = __builtin_amdgcn_perm(R[1][q], R[0][q], 0x05040100u);
-        const uint32_t lo23 = __builtin_amdgcn_perm(R[3][q], R[2][q], 0x05040100u);
-        const uint32_t hi01 = __builtin_amdgcn_perm(R[1][q], R[0][q], 0x07060302u);
-        const uint32_t hi23 = __builtin_amdgcn_perm(R[3][q], R[2][q], 0x07060302u);
-        acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-            __builtin_bit_cast(h4_t, u2_t{lo01, lo23}), pb, acc[2 * q], 0, 0, 0);
-        acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-            __builtin_bit_cast(h4_t, u2_t{hi01, hi23}), pb, acc[2 * q + 1], 0, 0, 0);
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t lo01 = __builtin_amdgcn_perm(R[1][q], R[0][q], 0x05040100u);
+          const uint32_t lo23 = __builtin_amdgcn_perm(R[3][q], R[2][q], 0x05040100u);
+          const uint32_t hi01 = __builtin_amdgcn_perm(R[1][q], R[0][q], 0x07060302u);
+          const uint32_t hi23 = __builtin_amdgcn_perm(R[3][q], R[2][q], 0x07060302u);
+          acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+              __builtin_bit_cast(h4_t, u2_t{lo01, lo23}), pb, acc[2 * q], 0, 0, 0);
+          acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+              __builtin_bit_cast(h4_t, u2_t{hi01, hi23}), pb, acc[2 * q + 1], 0, 0, 0);
+        }
       }
     }
   }

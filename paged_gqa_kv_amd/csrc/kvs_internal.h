@@ -14,6 +14,7 @@ constexpr int kScoreThreads = 256;   // records per scoring work-group
 constexpr size_t kMaxDecodeLds = 65536;  // dynamic LDS a decode work-group may request
 constexpr size_t kLdsPerCu = 163840;     // gfx950: 160 KiB of LDS per compute unit
 constexpr int kDecodeWavesPerSimd = 3;   // decode kernel launch bound (VGPR budget)
+constexpr int kDecodeWavesPerSimdE4M3 = 2;   // E4M3 decode: two blocks per step need more VGPRs
 
 // LDS of one decode work-group (one wave): the split's block ids (4 B each),
 // per-block mass partials of the 8 heads (32 B each) and the 4 KiB value stage.

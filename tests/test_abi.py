@@ -70,10 +70,10 @@ def test_split_policy():
     def sb(batch, max_nb, layers, fmt):
         return api.decode_split_blocks(api.shape(layers), batch, max_nb, 0, layers, 0, fmt)
     assert sb(1, 8192, 80, "fp16") == 1024  # 128K context, fp16: 4 waves per CU suffice
-    assert sb(1, 8192, 80, "e4m3") == 512   # E4M3 halves the bytes per wave: 7 waves per CU
+    assert sb(1, 8192, 80, "e4m3") == 512   # E4M3: at most 512 blocks per split
     assert sb(1, 65536, 32, "fp16") == 1024
     assert sb(8, 512, 4, "fp16") == 128     # 1,024 waves x 16 KiB in flight
-    assert sb(8, 512, 4, "e4m3") == 64      # 2,048 waves x 8 KiB
+    assert sb(8, 512, 4, "e4m3") == 64      # E4M3 wants 2 waves per SIMD: 2,048 waves
     assert sb(1, 64, 1, "fp16") == 16       # too small to fill the chip: shortest split
     assert sb(1, 8192, 80, "kivi2") == 128  # issue-bound: at most 128 blocks per split
     assert sb(1, 256, 1, "kivi2") == 16     # 6 KiB per wave: 16 MiB in flight needs many waves
