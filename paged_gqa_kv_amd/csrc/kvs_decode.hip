@@ -283,8 +283,7 @@ __global__ void __launch_bounds__(64, F::kWavesPerSimd) paged_decode_gqa(DecodeA
 #pragma unroll
       for (int p = 0; p < kPer; ++p)
         bm = fmaxf(bm, fmaxf(fmaxf(sv[p][0], sv[p][1]), fmaxf(sv[p][2], sv[p][3])));
-      bm = fmaxf(bm, xor_f(bm, 16));
-      bm = fmaxf(bm, xor_f(bm, 32));
+      bm = head_max4(bm);
       const float m_new = fmaxf(m_run, bm);
       const bool live = m_new != -INFINITY;
       const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
@@ -297,8 +296,7 @@ __global__ void __launch_bounds__(64, F::kWavesPerSimd) paged_decode_gqa(DecodeA
         for (int i = 0; i < 4; ++i) pv[p][i] = live ? __builtin_amdgcn_exp2f(sv[p][i] - m_new) : 0.f;
         const float ps = (pv[p][0] + pv[p][1]) + (pv[p][2] + pv[p][3]);
         ps_all = p == 0 ? ps : ps_all + ps;
-        bsum[p] = ps + xor_f(ps, 16);
-        bsum[p] += xor_f(bsum[p], 32);
+        bsum[p] = head_sum4(ps);
       }
       l_run = l_run * alpha + ps_all;
 
@@ -342,8 +340,7 @@ __global__ void __launch_bounds__(64, F::kWavesPerSimd) paged_decode_gqa(DecodeA
   if (saw_bad && lane == 0) flag(a.status, KVS_DEV_BAD_BLOCK_ID);
 
   // ---- split epilogue: statistics, partial output, mass partials
-  float lt = l_run + xor_f(l_run, 16);
-  lt += xor_f(lt, 32);
+  const float lt = head_sum4(l_run);
   const size_t st = (((size_t)s * a.n_layers + lr) * kQHeads + kGroup * g + c) * a.n_splits + split;
   if (c < kGroup) {
     if (j == 0) a.ml[st] = make_float2(m_run, lt);

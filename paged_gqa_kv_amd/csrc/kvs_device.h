@@ -45,6 +45,29 @@ __device__ __forceinline__ uint32_t xcd_item(uint32_t w, uint32_t grid) {
 
 __device__ __forceinline__ float xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// Maximum / sum of v over the 4 lanes l, l ^ 16, l ^ 32, l ^ 48 (the 4 lanes j
+// that hold one head in the MFMA output layout).  gfx950's permlane16 and
+// permlane32 swaps hand each lane both values of its pair (l, l ^ 16), then
+// (l, l ^ 32), in VALU registers -- {v[l], v[l ^ 16]} and {v[l], v[l ^ 32]} in
+// some order, as an in-bounds lane probe on the GPU showed -- so each step is
+// one swap and one max or add, with no LDS round trip and no lane-index
+// arithmetic.  max and + are commutative, so the order within a pair does not
+// change the result: it equals v[l] op v[l ^ 16], then op the l ^ 32 partner.
+// Every lane of the wave must be active.
+__device__ __forceinline__ float head_max4(float v) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+__device__ __forceinline__ float head_sum4(float v) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 __device__ __forceinline__ void flag(uint32_t* status, uint32_t bit) {
   atomicOr(status, bit);
 }

@@ -139,8 +139,7 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
   // to the running maximum and keeps the block's probability mass in LDS.
   auto softmax_block = [&](const float (&sv)[4], int b, float (&pv)[4]) {
     float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    bm = fmaxf(bm, xor_f(bm, 16));
-    bm = fmaxf(bm, xor_f(bm, 32));
+    bm = head_max4(bm);
     const float m_new = fmaxf(m_run, bm);
     const bool live = m_new != -INFINITY;
     const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
@@ -148,8 +147,7 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
     for (int i = 0; i < 4; ++i) pv[i] = live ? __builtin_amdgcn_exp2f(sv[i] - m_new) : 0.f;
     const float ps = (pv[0] + pv[1]) + (pv[2] + pv[3]);
     l_run = l_run * alpha + ps;
-    float bs = ps + xor_f(ps, 16);
-    bs += xor_f(bs, 32);
+    const float bs = head_sum4(ps);
     if (__ballot(c < kGroup && alpha != 1.f) != 0ull) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc[k] *= alpha;
@@ -162,29 +160,37 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
     m_run = m_new;
   };
 
-  // The same for a block whose 16 logits are all finite (m_new is finite, so
-  // no masked-out head needs guarding).
-  auto softmax_full = [&](const float (&sv)[4], int b, float (&pv)[4]) {
-    float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    bm = fmaxf(bm, xor_f(bm, 16));
-    bm = fmaxf(bm, xor_f(bm, 32));
+  // One update for the two blocks of a quantised pair (32 tokens, all logits
+  // finite, so no masked-out head needs guarding); returns p relative to the
+  // running maximum and keeps both blocks' probability mass in LDS.
+  auto softmax_pair = [&](const float (&sv)[2][4], int be, float (&pv)[2][4]) {
+    float bm = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
+                     fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
+    bm = head_max4(bm);
     const float m_new = fmaxf(m_run, bm);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float ps[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_new);
-    const float ps = (pv[0] + pv[1]) + (pv[2] + pv[3]);
-    l_run = l_run * alpha + ps;
-    float bs = ps + xor_f(ps, 16);
-    bs += xor_f(bs, 32);
+    for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pv[hb][i] = __builtin_amdgcn_exp2f(sv[hb][i] - m_new);
+      ps[hb] = (pv[hb][0] + pv[hb][1]) + (pv[hb][2] + pv[hb][3]);
+    }
+    l_run = l_run * alpha + (ps[0] + ps[1]);
+    const float bs0 = head_sum4(ps[0]);
+    const float bs1 = head_sum4(ps[1]);
     if (__ballot(c < kGroup && alpha != 1.f) != 0ull) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc[k] *= alpha;
 #pragma unroll
       for (int k = 0; k < 4; ++k) zacc[k] *= alpha;
       if (c < kGroup)
-        for (int idx = j; idx < b - b0; idx += 4) pi_lds[c * SB + idx] *= alpha;
+        for (int idx = j; idx < be - b0; idx += 4) pi_lds[c * SB + idx] *= alpha;
     }
-    if (c < kGroup && j == 0) pi_lds[c * SB + (b - b0)] = bs;
+    if (c < kGroup && j == 0) {
+      pi_lds[c * SB + (be - b0)] = bs0;
+      pi_lds[c * SB + (be + 1 - b0)] = bs1;
+    }
     m_run = m_new;
   };
 
@@ -264,26 +270,34 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
           zsacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(z8, qb[i], zsacc, 0, 0, 0);
         }
 
+        // ---- logits of both blocks (two independent MFMA chains), one softmax update
+        f4_t sacc[2] = {zsacc, zsacc};
+        u2_t kent[2];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+          kent[hb] = *reinterpret_cast<const u2_t*>(stage + hb * kKiviTileBytes + 8 * lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            const h8_t kc = codes_to_h8(code_set(kent[hb], i));
+            sacc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc, qhi[i], sacc[hb], 0, 0, 0);
+            sacc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc, qlo[i], sacc[hb], 0, 0, 0);
+          }
+        float sv[2][4];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sv[hb][i] = sacc[hb][i] * a.scale_log2;
+        float pv[2][4];
+        softmax_pair(sv, be, pv);
+
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
-          const int b = be + hb;
-          const u2_t kent = *reinterpret_cast<const u2_t*>(stage + hb * kKiviTileBytes + 8 * lane);
-          f4_t sacc = zsacc;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const h8_t kc = codes_to_h8(code_set(kent, i));
-            sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc, qhi[i], sacc, 0, 0, 0);
-            sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc, qlo[i], sacc, 0, 0, 0);
-          }
-          float sv[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sv[i] = sacc[i] * a.scale_log2;
-          float pv[4];
-          softmax_full(sv, b, pv);
-
           const uint8_t* vt = stage + (2 + hb) * kKiviTileBytes;
           const u2_t vent = *reinterpret_cast<const u2_t*>(vt + 8 * lane);
-          const h4_t pb4 = h4_t{(_Float16)pv[0], (_Float16)pv[1], (_Float16)pv[2], (_Float16)pv[3]};
+          const h4_t pb4 = h4_t{(_Float16)pv[hb][0], (_Float16)pv[hb][1], (_Float16)pv[hb][2],
+                                (_Float16)pv[hb][3]};
 #pragma unroll
           for (int grp = 0; grp < 4; ++grp) {
             const h4_t s4 = *reinterpret_cast<const h4_t*>(vt + 512 + 2 * (16 * grp + 4 * j));
@@ -346,13 +360,11 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
   if (saw_bad && lane == 0) flag(a.status, KVS_DEV_BAD_BLOCK_ID);
 
   // ---- split epilogue: statistics, partial output (+ value zero-point terms), mass partials
-  float lt = l_run + xor_f(l_run, 16);
-  lt += xor_f(lt, 32);
+  const float lt = head_sum4(l_run);
   float zt[4];
 #pragma unroll
   for (int grp = 0; grp < 4; ++grp) {
-    zt[grp] = zacc[grp] + xor_f(zacc[grp], 16);
-    zt[grp] += xor_f(zt[grp], 32);
+    zt[grp] = head_sum4(zacc[grp]);
   }
   if (c < kGroup) {
     if (j == 0) a.ml[st] = make_float2(m_run, lt);
