@@ -61,6 +61,12 @@ __device__ __forceinline__ float head_max4(float v) {
   return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 
+// Value of lane l ^ 8: the other half of the lane's 16-lane row (a DPP row
+// rotation by 8 within each row).
+__device__ __forceinline__ float swap8(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float head_sum4(float v) {
   auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   v = __uint_as_float(p[0]) + __uint_as_float(p[1]);

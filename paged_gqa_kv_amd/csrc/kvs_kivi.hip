@@ -115,16 +115,20 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
   for (int i = lane; i < b1 - b0; i += 64) tbl[i] = a.table[(size_t)s * a.max_nb + b0 + i];
   __syncthreads();
 
-  // B operand of QK: queries of the group, channels 32 i + 8 j .. + 8; rows 8..15 zero.
+  // B operand of QK: queries of the group, channels 32 i + 8 j .. + 8.  Columns
+  // 8..15 repeat heads 0..7.  In a quantised pair the first block's logits are
+  // taken from columns 0..7 and the second block's from columns 8..15, so that
+  // every lane holds a real (block, head) value through the softmax; a lane's
+  // half of the wave (hi) says which block of the pair it carries.  Columns
+  // 8..15 of the output accumulators collect the second blocks and are added
+  // to columns 0..7 at the end of the split.
+  const bool hi = c >= kGroup;
   h8_t qb[4];
-  if (c < kGroup) {
-    const uint16_t* qp =
-        a.q + ((((size_t)s * a.num_layers + layer) * kQHeads + kGroup * g + c) * kHeadDim);
+  {
+    const uint16_t* qp = a.q + ((((size_t)s * a.num_layers + layer) * kQHeads + kGroup * g +
+                                 (c & (kGroup - 1))) * kHeadDim);
 #pragma unroll
     for (int i = 0; i < 4; ++i) qb[i] = *reinterpret_cast<const h8_t*>(qp + 32 * i + 8 * j);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) qb[i] = h8_t{0, 0, 0, 0, 0, 0, 0, 0};
   }
 
   float m_run = -INFINITY;
@@ -140,6 +144,7 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
   auto softmax_block = [&](const float (&sv)[4], int b, float (&pv)[4]) {
     float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     bm = head_max4(bm);
+    bm = fmaxf(bm, swap8(bm));   // both halves keep the same running maximum
     const float m_new = fmaxf(m_run, bm);
     const bool live = m_new != -INFINITY;
     const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
@@ -161,36 +166,29 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
   };
 
   // One update for the two blocks of a quantised pair (32 tokens, all logits
-  // finite, so no masked-out head needs guarding); returns p relative to the
-  // running maximum and keeps both blocks' probability mass in LDS.
-  auto softmax_pair = [&](const float (&sv)[2][4], int be, float (&pv)[2][4]) {
-    float bm = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
-                     fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
+  // finite): lanes of the lower half hold the first block, lanes of the upper
+  // half the second, for the same heads.  Returns p relative to the running
+  // maximum and keeps both blocks' probability mass in LDS.
+  auto softmax_pair = [&](const float (&sv)[4], int be, float (&pv)[4]) {
+    float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     bm = head_max4(bm);
+    bm = fmaxf(bm, swap8(bm));
     const float m_new = fmaxf(m_run, bm);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float ps[2];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pv[hb][i] = __builtin_amdgcn_exp2f(sv[hb][i] - m_new);
-      ps[hb] = (pv[hb][0] + pv[hb][1]) + (pv[hb][2] + pv[hb][3]);
-    }
-    l_run = l_run * alpha + (ps[0] + ps[1]);
-    const float bs0 = head_sum4(ps[0]);
-    const float bs1 = head_sum4(ps[1]);
-    if (__ballot(c < kGroup && alpha != 1.f) != 0ull) {
+    for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_new);
+    const float ps = (pv[0] + pv[1]) + (pv[2] + pv[3]);
+    l_run = l_run * alpha + ps;
+    const float bs = head_sum4(ps);
+    if (__ballot(alpha != 1.f) != 0ull) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc[k] *= alpha;
 #pragma unroll
       for (int k = 0; k < 4; ++k) zacc[k] *= alpha;
-      if (c < kGroup)
+      if (!hi)
         for (int idx = j; idx < be - b0; idx += 4) pi_lds[c * SB + idx] *= alpha;
     }
-    if (c < kGroup && j == 0) {
-      pi_lds[c * SB + (be - b0)] = bs0;
-      pi_lds[c * SB + (be + 1 - b0)] = bs1;
-    }
+    if (j == 0) pi_lds[(c & (kGroup - 1)) * SB + (be + (hi ? 1 : 0) - b0)] = bs;
     m_run = m_new;
   };
 
@@ -284,27 +282,35 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
             sacc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc, qhi[i], sacc[hb], 0, 0, 0);
             sacc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc, qlo[i], sacc[hb], 0, 0, 0);
           }
-        float sv[2][4];
+        float sv[4];
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sv[hb][i] = sacc[hb][i] * a.scale_log2;
-        float pv[2][4];
+        for (int i = 0; i < 4; ++i) sv[i] = (hi ? sacc[1][i] : sacc[0][i]) * a.scale_log2;
+        float pv[4];
         softmax_pair(sv, be, pv);
 
+        // ---- PV.  Each lane's probabilities belong to its own block, so the value
+        // zero-point term (each lane against its block's zero points) is one pass;
+        // the products with the codes run per block, with the other half's
+        // probabilities zeroed.
+        const h4_t pb4 = h4_t{(_Float16)pv[0], (_Float16)pv[1], (_Float16)pv[2], (_Float16)pv[3]};
+        {
+          const uint8_t* vz = stage + (hi ? 3 : 2) * kKiviTileBytes + 640;
+#pragma unroll
+          for (int grp = 0; grp < 4; ++grp) {
+            const h4_t z4 = *reinterpret_cast<const h4_t*>(vz + 2 * (16 * grp + 4 * j));
+            zacc[grp] = dot2(h2_t{pb4[2], pb4[3]}, h2_t{z4[2], z4[3]},
+                             dot2(h2_t{pb4[0], pb4[1]}, h2_t{z4[0], z4[1]}, zacc[grp]));
+          }
+        }
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
+          const h4_t pbm = (hi == (hb == 1)) ? pb4 : h4_t{0, 0, 0, 0};
           const uint8_t* vt = stage + (2 + hb) * kKiviTileBytes;
           const u2_t vent = *reinterpret_cast<const u2_t*>(vt + 8 * lane);
-          const h4_t pb4 = h4_t{(_Float16)pv[hb][0], (_Float16)pv[hb][1], (_Float16)pv[hb][2],
-                                (_Float16)pv[hb][3]};
 #pragma unroll
           for (int grp = 0; grp < 4; ++grp) {
             const h4_t s4 = *reinterpret_cast<const h4_t*>(vt + 512 + 2 * (16 * grp + 4 * j));
-            const h4_t z4 = *reinterpret_cast<const h4_t*>(vt + 640 + 2 * (16 * grp + 4 * j));
-            const h4_t bp = pb4 * s4;
-            zacc[grp] = dot2(h2_t{pb4[2], pb4[3]}, h2_t{z4[2], z4[3]},
-                             dot2(h2_t{pb4[0], pb4[1]}, h2_t{z4[0], z4[1]}, zacc[grp]));
+            const h4_t bp = pbm * s4;
             const h8_t vc = codes_to_h8(code_set(vent, grp));
             acc[2 * grp] = __builtin_amdgcn_mfma_f32_16x16x16f16(
                 h4_t{vc[0], vc[1], vc[2], vc[3]}, bp, acc[2 * grp], 0, 0, 0);
@@ -343,7 +349,8 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
                                                       0, 0, 0);
       float sv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sv[i] = 4 * j + i < valid ? sacc[i] * a.scale_log2 : -INFINITY;
+      for (int i = 0; i < 4; ++i)
+        sv[i] = (!hi && 4 * j + i < valid) ? sacc[i] * a.scale_log2 : -INFINITY;
       float pv[4];
       softmax_block(sv, b, pv);
       const h4_t pb4 = h4_t{(_Float16)pv[0], (_Float16)pv[1], (_Float16)pv[2], (_Float16)pv[3]};
@@ -360,12 +367,19 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
   if (saw_bad && lane == 0) flag(a.status, KVS_DEV_BAD_BLOCK_ID);
 
   // ---- split epilogue: statistics, partial output (+ value zero-point terms), mass partials
-  const float lt = head_sum4(l_run);
+  // The upper half's columns (second blocks of the pairs) join the lower half's.
+  float lt = head_sum4(l_run);
+  lt += swap8(lt);
   float zt[4];
 #pragma unroll
   for (int grp = 0; grp < 4; ++grp) {
     zt[grp] = head_sum4(zacc[grp]);
+    zt[grp] += swap8(zt[grp]);
   }
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[k][i] += swap8(acc[k][i]);
   if (c < kGroup) {
     if (j == 0) a.ml[st] = make_float2(m_run, lt);
     float* op = a.opart + st * kHeadDim + 4 * j;
