@@ -58,6 +58,15 @@ __device__ __forceinline__ float block_reduce_max(float v, float* red) {
   return r;
 }
 
+// Up to this many chunks per sequence (4,096 records), score_update takes each
+// sequence's maximum straight from the block mass (every work-group reads its
+// sequence's whole mass: at most 16 KiB, eight loads in flight per thread) and
+// seq_chunk_max is not launched: one launch fewer per step (8 x 8K tokens:
+// 11 -> 7 us).  Longer sequences use the two-kernel form, which measured
+// faster from 8,192 records on.  max is exact in any order, so both forms give
+// the same bits.
+constexpr int kDirectMaxChunks = 16;
+
 __global__ void __launch_bounds__(kScoreThreads) seq_chunk_max(ScoreArgs a) {
   __shared__ float red[kScoreThreads / 64];
   const int s = blockIdx.y;
@@ -85,13 +94,26 @@ __global__ void __launch_bounds__(kScoreThreads) score_update(ScoreArgs a) {
   __shared__ float red[kScoreThreads / 64];
   const int s = blockIdx.y;
   const int chunk = blockIdx.x;
+  const bool direct = a.max_chunks <= kDirectMaxChunks;
   int r0 = 0;
-  const int nb = seq_records(a.meta_off, a.seq_lens, s, a.max_nb, a.total_blocks, a.status, false, &r0);
+  const int nb = seq_records(a.meta_off, a.seq_lens, s, a.max_nb, a.total_blocks, a.status,
+                             direct && threadIdx.x == 0 && chunk == 0, &r0);
   if (nb <= 0 || chunk * kScoreThreads >= nb) return;
-  const int nch = (nb + kScoreThreads - 1) / kScoreThreads;
   float M = 0.f;
-  for (int k = threadIdx.x; k < nch; k += kScoreThreads)
-    M = fmaxf(M, a.chunk_max[(size_t)s * a.max_chunks + k]);
+  if (direct) {
+    // indices past the end re-read the last record: harmless for a maximum
+    for (int k0 = threadIdx.x; k0 < nb; k0 += 8 * kScoreThreads) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = a.mass[r0 + min(k0 + u * kScoreThreads, nb - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) M = fmaxf(M, v[u]);
+    }
+  } else {
+    const int nch = (nb + kScoreThreads - 1) / kScoreThreads;
+    for (int k = threadIdx.x; k < nch; k += kScoreThreads)
+      M = fmaxf(M, a.chunk_max[(size_t)s * a.max_chunks + k]);
+  }
   M = block_reduce_max(M, red);
 
   const int b = chunk * kScoreThreads + threadIdx.x;
@@ -255,7 +277,8 @@ __global__ void __launch_bounds__(kScoreThreads) meta_init(MetaInitArgs a) {
 
 hipError_t launch_score(const ScoreArgs& a, int batch, hipStream_t stream) {
   const dim3 grid(a.max_chunks, batch);
-  hipLaunchKernelGGL(seq_chunk_max, grid, dim3(kScoreThreads), 0, stream, a);
+  if (a.max_chunks > kDirectMaxChunks)
+    hipLaunchKernelGGL(seq_chunk_max, grid, dim3(kScoreThreads), 0, stream, a);
   hipLaunchKernelGGL(score_update, grid, dim3(kScoreThreads), 0, stream, a);
   return hipGetLastError();
 }
