@@ -444,12 +444,8 @@ int decode_step(int32_t kv_format, const kvs_shape* shape, const void* q, const 
     e = hipEventRecord(g_ev_after, st);
     if (e != hipSuccess) return hip_fail(e, "recording the after-decode event");
   }
-  e = kvs::launch_combine(c, batch, st);
-  if (e != hipSuccess) return hip_fail(e, "combine_splits launch");
-  if (total_blocks > 0) {
-    e = kvs::launch_mass(m, batch, st);
-    if (e != hipSuccess) return hip_fail(e, "block_mass launch");
-  }
+  e = kvs::launch_combine_mass(c, m, batch, st);
+  if (e != hipSuccess) return hip_fail(e, "combine / block_mass launch");
   return ok();
 }
 

@@ -22,9 +22,7 @@ namespace kvs {
 //   M = max_k m_k, Lambda = sum_k l_k 2^(m_k - M), w_k = 2^(m_k - M) / Lambda,
 //   out = sum_k w_k o_k (fp16), and w_k is kept for the mass reduction.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(64) combine_splits(CombineArgs a) {
-  const int lane = threadIdx.x;
-  uint32_t w = blockIdx.x;
+__device__ __forceinline__ void combine_row(const CombineArgs& a, uint32_t w, int lane) {
   const int h = (int)(w % kQHeads);
   w /= kQHeads;
   const int lr = (int)(w % (uint32_t)a.n_layers);
@@ -89,6 +87,10 @@ __global__ void __launch_bounds__(64) combine_splits(CombineArgs a) {
                ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
 }
 
+__global__ void __launch_bounds__(64) combine_splits(CombineArgs a) {
+  combine_row(a, blockIdx.x, threadIdx.x);
+}
+
 // ---------------------------------------------------------------------------
 // block_mass: mass[s, b] = sum over (layer, query head) of pi * w_split, fp64
 // accumulation in a fixed order, so the result depends only on logical
@@ -99,17 +101,15 @@ __global__ void __launch_bounds__(64) combine_splits(CombineArgs a) {
 // work-groups, one per compute unit: with 128, half the chip's load slots sat
 // idle and the kernel read at half the rate.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(kMassThreads) block_mass(MassArgs a) {
+// Mass of the 32 blocks of column group cg of sequence s, with the weight of
+// (row, split) at wt[row * wstride + split].
+__device__ __forceinline__ void mass_columns(const MassArgs& a, int s, int cg, int nb, int r0,
+                                             const float* wt, int wstride,
+                                             double (*red)[kMassCols]) {
   constexpr int kStreams = kMassThreads / kMassCols;
-  __shared__ double red[kStreams][kMassCols];
   const int col = threadIdx.x % kMassCols;
   const int q = threadIdx.x / kMassCols;     // row stream; a wave holds two
-  const int s = blockIdx.y;
-  int r0 = 0;
-  const int nb = seq_blocks(a.seq_lens, a.meta_off, s, a.max_nb, a.total_blocks, a.status,
-                            false, &r0);
-  if (nb <= 0 || (int)blockIdx.x * kMassCols >= nb) return;
-  const int b = blockIdx.x * kMassCols + col;
+  const int b = cg * kMassCols + col;
   const bool act = b < nb;
   const int r = r0 + (act ? b : 0);
   const int split = (act ? b : 0) / a.split_blocks;
@@ -117,22 +117,22 @@ __global__ void __launch_bounds__(kMassThreads) block_mass(MassArgs a) {
   double acc = 0.0;
   if (act) {
     const float* pcol = a.pi + r;
-    const float* wcol = a.wsplit + (size_t)s * a.n_layers * kQHeads * a.n_splits + split;
+    const float* wcol = wt + split;
     // Rounds of 16 rows: all 32 loads of a round are issued before the first
     // product (rows past the end re-read the last row, unconditionally, so no
     // load sits behind a branch); the sum runs in row order and skips them.
     constexpr int kRound = 16;
     for (int row0 = q; row0 < rows; row0 += kStreams * kRound) {
-      float pv[kRound], wt[kRound];
+      float pv[kRound], wv[kRound];
 #pragma unroll
       for (int u = 0; u < kRound; ++u) {
         const int row = min(row0 + u * kStreams, rows - 1);
         pv[u] = pcol[(size_t)row * a.total_blocks];
-        wt[u] = wcol[(size_t)row * a.n_splits];
+        wv[u] = wcol[(size_t)row * wstride];
       }
 #pragma unroll
       for (int u = 0; u < kRound; ++u)
-        if (row0 + u * kStreams < rows) acc += (double)pv[u] * (double)wt[u];
+        if (row0 + u * kStreams < rows) acc += (double)pv[u] * (double)wv[u];
     }
   }
   red[q][col] = acc;
@@ -146,10 +146,91 @@ __global__ void __launch_bounds__(kMassThreads) block_mass(MassArgs a) {
   }
 }
 
+__global__ void __launch_bounds__(kMassThreads) block_mass(MassArgs a) {
+  __shared__ double red[kMassThreads / kMassCols][kMassCols];
+  const int s = blockIdx.y;
+  int r0 = 0;
+  const int nb = seq_blocks(a.seq_lens, a.meta_off, s, a.max_nb, a.total_blocks, a.status,
+                            false, &r0);
+  if (nb <= 0 || (int)blockIdx.x * kMassCols >= nb) return;
+  const float* wt = a.wsplit + (size_t)s * a.n_layers * kQHeads * a.n_splits;
+  mass_columns(a, s, blockIdx.x, nb, r0, wt, a.n_splits, red);
+}
+
+// ---------------------------------------------------------------------------
+// combine_mass: both steps above in one launch, for small problems, where the
+// launch and the wait between the two kernels are a visible part of the step
+// (8 sequences x 8K tokens x 4 layers: 5.5 + 4.7 us of kernels in a 0.2 ms
+// step).  The first work-groups combine 16 (sequence, layer, head) rows each,
+// one per wave.  The others reduce the mass of 32 blocks, computing the split
+// weights they need themselves from the split statistics: per (layer, head)
+// row, M = max_k m_k, Lambda = sum_k l_k 2^(m_k - M) in split order, w_k =
+// 2^(m_k - M) / Lambda, into LDS.  That costs every mass work-group a read of
+// all its sequence's statistics, which is why it is kept for small problems.
+// ---------------------------------------------------------------------------
+constexpr int kFusedMaxWeights = 4096;   // (layer, head) rows x splits in LDS
+
+__global__ void __launch_bounds__(kMassThreads) combine_mass(CombineArgs c, MassArgs a,
+                                                             uint32_t comb_wgs,
+                                                             uint32_t col_groups) {
+  constexpr uint32_t kRowsPerWg = kMassThreads / 64;
+  if (blockIdx.x < comb_wgs) {
+    const uint32_t row = blockIdx.x * kRowsPerWg + (threadIdx.x >> 6);
+    const uint32_t total_rows = (gridDim.x - comb_wgs) / col_groups * (uint32_t)c.n_layers * kQHeads;
+    if (row < total_rows) combine_row(c, row, threadIdx.x & 63);
+    return;
+  }
+  __shared__ double red[kMassThreads / kMassCols][kMassCols];
+  __shared__ float wl[kFusedMaxWeights];
+  const uint32_t mw = blockIdx.x - comb_wgs;
+  const int s = (int)(mw / col_groups);
+  const int cg = (int)(mw % col_groups);
+  int r0 = 0;
+  const int nb = seq_blocks(a.seq_lens, a.meta_off, s, a.max_nb, a.total_blocks, a.status,
+                            false, &r0);
+  if (nb <= 0 || cg * kMassCols >= nb) return;
+  const int nsp = (nb + a.split_blocks - 1) / a.split_blocks;
+  const int rows = a.n_layers * kQHeads;
+  for (int row = threadIdx.x; row < rows; row += kMassThreads) {
+    const float2* st = c.ml + ((size_t)s * rows + row) * a.n_splits;
+    float M = -INFINITY;
+    for (int k = 0; k < nsp; ++k) M = fmaxf(M, st[k].x);
+    double L = 0.0;
+    if (M != -INFINITY)
+      for (int k = 0; k < nsp; ++k) L += (double)st[k].y * (double)__builtin_amdgcn_exp2f(st[k].x - M);
+    const bool dead = !(L > 0.0);
+    const double invL = dead ? 0.0 : 1.0 / L;
+    for (int k = 0; k < nsp; ++k)
+      wl[row * nsp + k] = dead ? 0.f : (float)((double)__builtin_amdgcn_exp2f(st[k].x - M) * invL);
+  }
+  __syncthreads();
+  mass_columns(a, s, cg, nb, r0, wl, nsp, red);
+}
+
 hipError_t launch_combine(const CombineArgs& a, int batch, hipStream_t stream) {
   const uint64_t wgs = (uint64_t)batch * a.n_layers * kQHeads;
   hipLaunchKernelGGL(combine_splits, dim3((uint32_t)wgs), dim3(64), 0, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_combine_mass(const CombineArgs& c, const MassArgs& a, int batch,
+                               hipStream_t stream) {
+  const uint64_t rows = (uint64_t)a.n_layers * kQHeads;
+  const uint64_t col_groups = ((uint64_t)a.max_nb + kMassCols - 1) / kMassCols;
+  const uint64_t weights = rows * (uint64_t)a.n_splits;
+  // fused while the weights fit the LDS table and the statistics every mass
+  // work-group re-reads stay under 2 MiB in total
+  if (a.total_blocks > 0 && weights <= (uint64_t)kFusedMaxWeights &&
+      weights * 8u * col_groups * (uint64_t)batch <= (2ull << 20)) {
+    const uint64_t comb_wgs = ((uint64_t)batch * rows + kMassThreads / 64 - 1) / (kMassThreads / 64);
+    const uint64_t wgs = comb_wgs + col_groups * (uint64_t)batch;
+    hipLaunchKernelGGL(combine_mass, dim3((uint32_t)wgs), dim3(kMassThreads), 0, stream, c, a,
+                       (uint32_t)comb_wgs, (uint32_t)col_groups);
+    return hipGetLastError();
+  }
+  hipError_t e = launch_combine(c, batch, stream);
+  if (e != hipSuccess || a.total_blocks <= 0) return e;
+  return launch_mass(a, batch, stream);
 }
 
 hipError_t launch_mass(const MassArgs& a, int batch, hipStream_t stream) {

@@ -194,6 +194,10 @@ hipError_t launch_kivi_advance(const KiviAdvanceArgs& adv, const KiviQuantArgs& 
                                hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int batch, hipStream_t stream);
 hipError_t launch_mass(const MassArgs& a, int batch, hipStream_t stream);
+// combine, then mass (mass only when total_blocks > 0): one fused launch for
+// small problems, the two kernels otherwise
+hipError_t launch_combine_mass(const CombineArgs& c, const MassArgs& m, int batch,
+                               hipStream_t stream);
 hipError_t launch_score(const ScoreArgs& a, int batch, hipStream_t stream);
 hipError_t launch_classify(const ScoreArgs& a, int batch, hipStream_t stream);
 hipError_t launch_meta_init(const MetaInitArgs& a, int batch, hipStream_t stream);
