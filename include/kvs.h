@@ -141,9 +141,11 @@ size_t kvs_meta_layout(size_t* offsets, int n);
 #define KVS_KV_KIVI2 2  /* kvs_decode_step_kivi: 2-bit KIVI blocks + fp16 residual */
 
 /* Blocks per split used for this problem when split_blocks == 0 is passed (a
- * power of two in [16, 1024], chosen from the sizes and the stored format
- * kv_format, one of KVS_KV_*); otherwise split_blocks itself if valid (for
- * KVS_KV_KIVI2 it must also be even).  0 if any argument is invalid. */
+ * power of two in [16, 1024] -- at most 512 for KVS_KV_E4M3 and 128 for
+ * KVS_KV_KIVI2 -- chosen from the sizes and the stored format kv_format, one of
+ * KVS_KV_*, so that the launch keeps enough reads in flight); otherwise
+ * split_blocks itself if valid (for KVS_KV_KIVI2 it must also be even).  0 if
+ * any argument is invalid. */
 int32_t kvs_decode_split_blocks(const kvs_shape* shape, int32_t kv_format, int32_t batch,
                                 int32_t max_blocks_per_seq, int32_t layer_begin,
                                 int32_t layer_end, int32_t split_blocks);
