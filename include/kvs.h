@@ -424,6 +424,37 @@ int kvs_evict_candidates(const kvs_block_meta* meta, const int32_t* meta_offsets
                          int32_t* out_block, double* out_key, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* kvs_decode_step over an fp16 pool, with pairs of sequences that share
+ * blocks (a prefix cache's refcounted blocks, KV cache offload post, "Top
+ * row") decoded by one wave: each block the two hold at the same logical
+ * position is read from HBM once and scored for both.  Outputs, block mass
+ * and every other argument, size and rule are those of kvs_decode_step, and
+ * the results are bit-identical to it whatever the pairing.
+ *  pair_role  int32 [batch], device: pair_role[a] = b together with
+ *             pair_role[b] = -2 - a links sequences a and b (a != b); -1 marks
+ *             an unpaired sequence.  Entries whose partner does not link back
+ *             are treated as unpaired.  A split of a linked pair is decoded
+ *             jointly when both sequences hold its first block as the same
+ *             physical block; other splits are decoded separately.
+ *  split_blocks  at most 512 (a paired work-group holds both sequences' mass
+ *             partials in LDS); 0 chooses as kvs_decode_split_blocks does for
+ *             KVS_KV_FP16, capped at 512.  The workspace must fit
+ *             kvs_decode_workspace_bytes(..., KVS_KV_FP16, ..., that split).
+ * KVS_E_NULL when pair_role is NULL; KVS_E_RANGE for a split above 512. */
+int kvs_decode_step_paired(const kvs_shape* shape,
+                           const void* q,
+                           const void* kv_pool, int64_t pool_blocks,
+                           const int32_t* block_table, int32_t max_blocks_per_seq,
+                           const int32_t* seq_lens, const int32_t* pair_role,
+                           const int32_t* meta_offsets,
+                           int32_t batch, int64_t total_blocks,
+                           int32_t layer_begin, int32_t layer_end,
+                           float scale,
+                           void* out, float* block_mass, int accumulate,
+                           int32_t split_blocks,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 /* Workspace bytes kvs_append_kv needs (status header + two words per sequence). */
 size_t kvs_append_workspace_bytes(int32_t batch);
 

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvs.so")
-SOURCES = ["kvs_decode.hip", "kvs_combine.hip", "kvs_kivi.hip", "kvs_score.hip", "kvs_append.hip", "kvs_util.hip",
+SOURCES = ["kvs_decode.hip", "kvs_decode_paired.hip", "kvs_combine.hip", "kvs_kivi.hip", "kvs_score.hip", "kvs_append.hip", "kvs_util.hip",
            "kvs_abi.cpp"]
 ARCH = "gfx950"
 

@@ -323,7 +323,7 @@ namespace {
 int decode_step(int32_t kv_format, const kvs_shape* shape, const void* q, const void* kv_pool,
                 int64_t pool_blocks, const void* kivi_pool, int64_t kivi_blocks,
                 const int32_t* block_table, int32_t max_blocks_per_seq,
-                const int32_t* seq_lens, const int32_t* quant_lens,
+                const int32_t* seq_lens, const int32_t* quant_lens, const int32_t* pair_role,
                 const int32_t* meta_offsets, int32_t batch,
                 int64_t total_blocks, int32_t layer_begin, int32_t layer_end, float scale,
                 void* out, float* block_mass, int accumulate, int32_t split_blocks,
@@ -361,6 +361,18 @@ int decode_step(int32_t kv_format, const kvs_shape* shape, const void* q, const 
       !aligned(meta_offsets, 4))
     return fail(KVS_E_ALIGN, "int32 / fp32 arrays must be 4-byte aligned");
   if (!aligned(workspace, kAlign)) return fail(KVS_E_ALIGN, "workspace must be 256-byte aligned");
+  if (pair_role) {
+    if (kv_format != KVS_KV_FP16)
+      return fail(KVS_E_RANGE, "paired decode runs over fp16 pools only");
+    if (!aligned(pair_role, 4)) return fail(KVS_E_ALIGN, "pair_role must be 4-byte aligned");
+    if (split_blocks > kvs::kMaxPairSplit)
+      return fail(KVS_E_RANGE, "split_blocks %d above %d for a paired decode", split_blocks,
+                  kvs::kMaxPairSplit);
+    if (split_blocks == 0) {
+      split_blocks = choose_split(batch, max_blocks_per_seq, layer_end - layer_begin, kv_format);
+      if (split_blocks > kvs::kMaxPairSplit) split_blocks = kvs::kMaxPairSplit;
+    }
+  }
   DecodeLayout L;
   if (!decode_layout(shape, kv_format, batch, max_blocks_per_seq, total_blocks, layer_begin,
                      layer_end, split_blocks, &L))
@@ -398,6 +410,7 @@ int decode_step(int32_t kv_format, const kvs_shape* shape, const void* q, const 
   d.kivi = static_cast<const uint8_t*>(kivi_pool);
   d.kivi_blocks = kivi ? kivi_blocks : 0;
   d.quant_lens = kivi ? quant_lens : nullptr;
+  d.pair_role = pair_role;
   d.ml = reinterpret_cast<float2*>(ws + L.ml);
   d.opart = reinterpret_cast<float*>(ws + L.opart);
   d.pi = reinterpret_cast<float*>(ws + L.pi);
@@ -460,7 +473,7 @@ int kvs_decode_step(const kvs_shape* shape, const void* q, const void* kv_pool, 
                     float* block_mass, int accumulate, int32_t split_blocks, void* workspace,
                     size_t workspace_bytes, void* stream) {
   return decode_step(KVS_KV_FP16, shape, q, kv_pool, pool_blocks, nullptr, 0, block_table,
-                     max_blocks_per_seq, seq_lens, nullptr, meta_offsets, batch, total_blocks, layer_begin, layer_end, scale,
+                     max_blocks_per_seq, seq_lens, nullptr, nullptr, meta_offsets, batch, total_blocks, layer_begin, layer_end, scale,
                      out, block_mass, accumulate, split_blocks, workspace, workspace_bytes, stream);
 }
 
@@ -472,9 +485,24 @@ int kvs_decode_step_e4m3(const kvs_shape* shape, const void* q, const void* kv_p
                          float* block_mass, int accumulate, int32_t split_blocks, void* workspace,
                          size_t workspace_bytes, void* stream) {
   return decode_step(KVS_KV_E4M3, shape, q, kv_pool, pool_blocks, nullptr, 0, block_table,
-                     max_blocks_per_seq, seq_lens, nullptr, meta_offsets, batch, total_blocks,
+                     max_blocks_per_seq, seq_lens, nullptr, nullptr, meta_offsets, batch, total_blocks,
                      layer_begin, layer_end, scale, out, block_mass, accumulate, split_blocks,
                      workspace, workspace_bytes, stream);
+}
+
+int kvs_decode_step_paired(const kvs_shape* shape, const void* q, const void* kv_pool,
+                           int64_t pool_blocks, const int32_t* block_table,
+                           int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                           const int32_t* pair_role, const int32_t* meta_offsets, int32_t batch,
+                           int64_t total_blocks, int32_t layer_begin, int32_t layer_end,
+                           float scale, void* out, float* block_mass, int accumulate,
+                           int32_t split_blocks, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (!pair_role) return fail(KVS_E_NULL, "pair_role is NULL");
+  return decode_step(KVS_KV_FP16, shape, q, kv_pool, pool_blocks, nullptr, 0, block_table,
+                     max_blocks_per_seq, seq_lens, nullptr, pair_role, meta_offsets, batch,
+                     total_blocks, layer_begin, layer_end, scale, out, block_mass, accumulate,
+                     split_blocks, workspace, workspace_bytes, stream);
 }
 
 int kvs_decode_step_kivi(const kvs_shape* shape, const void* q, const void* kv_pool,
@@ -486,7 +514,8 @@ int kvs_decode_step_kivi(const kvs_shape* shape, const void* q, const void* kv_p
                          float* block_mass, int accumulate, int32_t split_blocks, void* workspace,
                          size_t workspace_bytes, void* stream) {
   return decode_step(KVS_KV_KIVI2, shape, q, kv_pool, pool_blocks, kivi_pool, kivi_blocks,
-                     block_table, max_blocks_per_seq, seq_lens, quant_lens, meta_offsets, batch,
+                     block_table, max_blocks_per_seq, seq_lens, quant_lens, nullptr, meta_offsets,
+                     batch,
                      total_blocks, layer_begin, layer_end, scale, out, block_mass, accumulate,
                      split_blocks, workspace, workspace_bytes, stream);
 }

@@ -22,6 +22,8 @@ constexpr int kQHeads = 64;
 constexpr int kTileBytes = 16 * kHeadDim * 2;          // fp16 (layer, K|V, KV head) tile: 4 KiB
 static_assert(decode_lds_bytes(1024) <= kMaxDecodeLds, "largest split must fit the LDS bound");
 static_assert(decode_lds_bytes(0) == kTileBytes, "value stage holds one fp16 tile");
+static_assert(decode_pair_lds_bytes(kMaxPairSplit) <= kMaxDecodeLds / 1.5,
+              "paired splits keep 4 work-groups per CU");
 
 // XCD-aware order of the decode grids.  Work-group w goes to XCD w % 8 (the
 // dispatcher deals work-groups round-robin over the 8 XCDs, each with its own

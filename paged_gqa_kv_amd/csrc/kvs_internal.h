@@ -22,6 +22,13 @@ constexpr size_t decode_lds_bytes(int32_t split_blocks) {
   return (size_t)36 * (size_t)split_blocks + 4096;
 }
 
+// LDS of one paired decode work-group: block ids of both sequences, mass
+// partials of 16 (sequence, head) columns and the 4 KiB value stage.
+constexpr size_t decode_pair_lds_bytes(int32_t split_blocks) {
+  return (size_t)72 * (size_t)split_blocks + 4096;
+}
+constexpr int32_t kMaxPairSplit = 512;   // paired splits: LDS and 4 work-groups per CU
+
 struct DecodeArgs {
   const uint16_t* q;        // fp16 bits [B][num_layers][64][128]
   const uint8_t* pool;      // [P][num_layers][2][8][16][128] fp16 values or E4M3 codes
@@ -41,6 +48,7 @@ struct DecodeArgs {
   const uint8_t* kivi;      // KVS_KV_KIVI2: quantised pool [kivi_blocks][num_layers][2][8][768]
   int64_t kivi_blocks;
   const int32_t* quant_lens;  // KVS_KV_KIVI2: [B] quantised tokens per sequence
+  const int32_t* pair_role;   // nullable: pairs of sequences decoded by one wave (fp16)
   float2* ml;               // [B][n_layers][64][n_splits]: (running max, sum), base 2
   float* opart;             // [B][n_layers][64][n_splits][128]
   float* pi;                // [n_layers][64][total_blocks]
@@ -192,6 +200,7 @@ hipError_t launch_decode_kivi(const DecodeArgs& a, int batch, hipStream_t stream
 hipError_t launch_kivi_quantize(const KiviQuantArgs& a, hipStream_t stream);
 hipError_t launch_kivi_advance(const KiviAdvanceArgs& adv, const KiviQuantArgs& q, int batch,
                                hipStream_t stream);
+hipError_t launch_decode_pair(const DecodeArgs& a, int batch, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int batch, hipStream_t stream);
 hipError_t launch_mass(const MassArgs& a, int batch, hipStream_t stream);
 // combine, then mass (mass only when total_blocks > 0): one fused launch for

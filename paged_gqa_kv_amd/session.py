@@ -15,6 +15,23 @@ import workload as W
 from . import api
 
 
+def pair_plan(table_host, blocks) -> np.ndarray:
+    """pair_role for kvs_decode_step_paired: sequences whose first block is the
+    same physical block (a shared prefix), paired in batch order; -1 for the
+    rest.  Only a plan: the decode is bit-identical with or without it."""
+    B = len(blocks)
+    role = np.full(B, -1, dtype=np.int32)
+    groups = {}
+    for s in range(B):
+        if blocks[s] > 0:
+            groups.setdefault(int(table_host[s, 0]), []).append(s)
+    for members in groups.values():
+        for a, b in zip(members[0::2], members[1::2]):
+            role[a] = b
+            role[b] = -2 - a
+    return role
+
+
 def kivi_quant_len(n: int) -> int:
     """Quantised tokens of an n-token sequence under a KIVI cache: the newest
     ~128 tokens stay fp16 and the boundary is snapped down to a whole 32-token
@@ -24,7 +41,7 @@ def kivi_quant_len(n: int) -> int:
 
 class DecodeSession:
     def __init__(self, m, layer_begin: int = 0, layer_end=None, split_blocks: int = 0,
-                 anchor_blocks: int = 1, stream=None, kivi_spare_blocks=None):
+                 anchor_blocks: int = 1, stream=None, kivi_spare_blocks=None, pair_role=None):
         self.m = m
         self.stream = stream
         L = m.num_layers
@@ -39,6 +56,17 @@ class DecodeSession:
                                                     self.layer_end, split_blocks, fmt)
         if self.split_blocks == 0:
             raise ValueError(f"invalid split_blocks {split_blocks}")
+        # paired decode (fp16): pair_role as kvs_decode_step_paired takes it, or
+        # "auto" for pair_plan's shared-prefix pairs; splits of at most 512 blocks
+        self.pair_role = None
+        if pair_role is not None:
+            if fmt != "fp16":
+                raise ValueError("paired decode runs over fp16 pools only")
+            if isinstance(pair_role, str) and pair_role == "auto":
+                pair_role = pair_plan(m.table_host, m.blocks)
+            self.pair_role = torch.as_tensor(np.asarray(pair_role, dtype=np.int32), device=dev)
+            if split_blocks == 0:
+                self.split_blocks = min(self.split_blocks, 512)
         self.out = torch.zeros((B, L, 64, 128), dtype=torch.float16, device=dev)
         self.mass = torch.zeros(max(m.total_blocks, 1), dtype=torch.float32, device=dev)
         ws_bytes = api.decode_workspace_bytes(self.shape, B, m.max_blocks, m.total_blocks,
@@ -126,6 +154,12 @@ class DecodeSession:
                                  self.quant_lens, m.meta_offsets, m.batch, m.total_blocks, lb, le,
                                  sc, self.out, self.mass, accumulate, self.split_blocks, self.ws,
                                  stream=self.stream)
+            return
+        if self.pair_role is not None:
+            api.decode_step_paired(self.shape, q, m.pool, m.pool_blocks, m.block_table,
+                                   m.max_blocks, m.seq_lens, self.pair_role, m.meta_offsets,
+                                   m.batch, m.total_blocks, lb, le, sc, self.out, self.mass,
+                                   accumulate, self.split_blocks, self.ws, stream=self.stream)
             return
         fn = api.decode_step_e4m3 if self.kv_format == "e4m3" else api.decode_step
         fn(self.shape, q, m.pool, m.pool_blocks, m.block_table, m.max_blocks, m.seq_lens,

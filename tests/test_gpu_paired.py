@@ -1,0 +1,115 @@
+"""GPU: the paired decode (kvs_decode_step_paired), where one wave serves two
+sequences that share blocks, gives the unpaired decode's bits and the
+oracle's values, whatever the pairing array holds."""
+import numpy as np
+import pytest
+import torch
+
+import workload as W
+from paged_gqa_kv_amd import api
+from paged_gqa_kv_amd.session import DecodeSession, pair_plan
+
+from . import parity as P
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _case(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16 if t.dtype == torch.float16 else torch.int32)
+
+
+def _shared_workload(seed=9, layers=2):
+    # an 18-block (288-token) shared prefix; 100 and 40 tokens are shorter than
+    # it, so their last shared block is partial for them and full for others
+    lens = [700, 100, 333, 288, 1000, 40, 517]
+    return W.materialise(W.custom("pair", layers, lens, seed=seed, spare_blocks=6,
+                                  shared_prefix_tokens=288), DEV)
+
+
+@pytest.mark.parametrize("split_blocks", [4, 8, 0])
+def test_paired_decode_bits_and_oracle(split_blocks):
+    _case(f"paired vs unpaired decode, shared 288-token prefix, split_blocks={split_blocks}")
+    m = _shared_workload()
+    role = pair_plan(m.table_host, m.blocks)
+    assert (role >= 0).sum() == 3 and (role <= -2).sum() == 3
+    par = DecodeSession(m, split_blocks=split_blocks, pair_role=role)
+    assert par.split_blocks <= 512
+    ref = DecodeSession(m, split_blocks=par.split_blocks)
+    h = P.host(m)
+    offs = m.meta_offsets.cpu().numpy()
+    for step in range(2):
+        q = W.make_query(m, step)
+        ref.decode(q)
+        par.decode(q)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(par.out), _bits(ref.out)), step
+        assert torch.equal(_bits(par.mass), _bits(ref.mass)), step
+        out_ref, mass_ref = P.oracle_decode(h, q)
+        P.check_out(par.out, out_ref, range(m.num_layers))
+        P.check_mass(par.mass, mass_ref, offs)
+    assert par.status() == 0 and ref.status() == 0
+
+
+def test_inconsistent_pair_roles_change_nothing():
+    _case("pair_role arrays with broken, one-sided, self and out-of-range links")
+    m = _shared_workload(seed=3)
+    B = m.batch
+    ref = DecodeSession(m, split_blocks=8)
+    q = W.make_query(m, 0)
+    ref.decode(q)
+    torch.cuda.synchronize()
+    roles = {
+        "one-sided": [1] + [-1] * (B - 1),
+        "links elsewhere": [1, -2 - 5] + [-1] * (B - 2),
+        "self": [0] + [-1] * (B - 1),
+        "out of range": [B + 3, -2 - 0] + [-1] * (B - 2),
+        "negative partner": [-2 - (B + 7)] + [-1] * (B - 1),
+        "second below first": [-3, 0] + [-1] * (B - 2),      # pair (1, 0)
+        "all unpaired": [-1] * B,
+        "everyone with 0": [3] + [-2 - 0] * (B - 1),          # 0 -> 3 linked; the others point at 0
+    }
+    for name, role in roles.items():
+        par = DecodeSession(m, split_blocks=8, pair_role=np.asarray(role, dtype=np.int32))
+        par.decode(q)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(par.out), _bits(ref.out)), name
+        assert torch.equal(_bits(par.mass), _bits(ref.mass)), name
+        assert par.status() == 0, name
+
+
+def test_pairs_without_shared_blocks():
+    _case("pairs whose sequences share no block: every split decoded separately")
+    m = W.materialise(W.custom("nopair", 2, [300, 517, 64, 1], seed=12, spare_blocks=4), DEV)
+    ref = DecodeSession(m, split_blocks=4)
+    par = DecodeSession(m, split_blocks=4, pair_role=np.asarray([1, -2, 3, -4], dtype=np.int32))
+    q = W.make_query(m, 1)
+    ref.decode(q)
+    par.decode(q)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(par.out), _bits(ref.out))
+    assert torch.equal(_bits(par.mass), _bits(ref.mass))
+
+
+def test_paired_decode_rejects_before_launch():
+    _case("paired entry point: NULL pair_role, split above 512, non-fp16 session")
+    m = _shared_workload(seed=5)
+    sess = DecodeSession(m, split_blocks=8, pair_role="auto")
+    with pytest.raises(api.KvsError):
+        api.decode_step_paired(sess.shape, W.make_query(m, 0), m.pool, m.pool_blocks,
+                               m.block_table, m.max_blocks, m.seq_lens, None, m.meta_offsets,
+                               m.batch, m.total_blocks, 0, m.num_layers, api.DEFAULT_SCALE,
+                               sess.out, sess.mass, 0, 8, sess.ws)
+    with pytest.raises(api.KvsError):
+        api.decode_step_paired(sess.shape, W.make_query(m, 0), m.pool, m.pool_blocks,
+                               m.block_table, m.max_blocks, m.seq_lens, sess.pair_role,
+                               m.meta_offsets, m.batch, m.total_blocks, 0, m.num_layers,
+                               api.DEFAULT_SCALE, sess.out, sess.mass, 0, 1024, sess.ws)
+    with pytest.raises(ValueError):
+        DecodeSession(W.materialise(W.as_e4m3(W.WORKLOADS["decode-1L-1K"]), DEV),
+                      pair_role="auto")
