@@ -32,6 +32,54 @@ def pair_plan(table_host, blocks) -> np.ndarray:
     return role
 
 
+def pair_loaded_tokens(table_host, lens, role, split_blocks: int) -> int:
+    """Tokens whose keys and values kvs_decode_step_paired loads per (layer,
+    KV head).  A split is joint when its two sequences are linked both ways,
+    both reach the split's first position and hold the same block there; in a
+    joint split a position where both hold the same block is loaded once, for
+    the larger of the two token counts.  Every other split loads its own
+    sequence's tokens, as the unpaired decode does."""
+    role = np.asarray(role)
+    B, SB = len(lens), int(split_blocks)
+    lens = np.asarray(lens, dtype=np.int64)
+    nb = (lens + 15) // 16
+    tbl = table_host
+
+    def link_of(s):   # (first, second) of s's mutual link, or None
+        o = int(role[s])
+        other = o if o >= 0 else -2 - o
+        if o == -1 or other == s or not 0 <= other < B:
+            return None
+        if o >= 0 and int(role[other]) == -2 - s:
+            return s, other
+        if o <= -2 and int(role[other]) == s:
+            return other, s
+        return None
+
+    tokens = 0
+    for s in range(B):
+        link = link_of(s)
+        for b0 in range(0, int(nb[s]), SB):
+            b1 = min(int(nb[s]), b0 + SB)
+            joint = (link is not None and b0 < nb[link[0]] and b0 < nb[link[1]]
+                     and tbl[link[0], b0] == tbl[link[1], b0])
+            if not joint:
+                tokens += int(min(lens[s], 16 * b1) - 16 * b0)
+                continue
+            if link[0] != s:
+                continue   # loaded by the first sequence's work-groups
+            p = link[1]
+            b1p = min(int(nb[p]), b0 + SB)
+            for b in range(b0, max(b1, b1p)):
+                va = int(min(16, lens[s] - 16 * b)) if b < b1 else 0
+                vb = int(min(16, lens[p] - 16 * b)) if b < b1p else 0
+                if va and vb and tbl[s, b] == tbl[p, b]:
+                    tokens += max(va, vb)
+                else:
+                    tokens += va + vb
+    return tokens
+
+
 def kivi_quant_len(n: int) -> int:
     """Quantised tokens of an n-token sequence under a KIVI cache: the newest
     ~128 tokens stay fp16 and the boundary is snapped down to a whole 32-token
@@ -137,6 +185,18 @@ class DecodeSession:
             nq = int(self.quant_lens_host.sum())
             return (nq // 16 * 2 * 768 + (sum(self.m.lens) - nq) * 128 * 2 * 2) * layers * 8
         return sum(self.m.lens) * layers * 8 * 128 * 2 * self.kv_elem_bytes
+
+    @property
+    def kv_bytes_loaded_per_step(self) -> int:
+        """Stored KV bytes the decode kernels load per step: kv_bytes_per_step,
+        less what a pairing shares (pair_loaded_tokens)."""
+        if self.pair_role is None:
+            return self.kv_bytes_per_step
+        m = self.m
+        tokens = pair_loaded_tokens(m.table_host, m.lens, self.pair_role.cpu().numpy(),
+                                    self.split_blocks)
+        layers = self.layer_end - self.layer_begin
+        return tokens * layers * 8 * 128 * 2 * self.kv_elem_bytes
 
     def reset_meta(self):
         m = self.m

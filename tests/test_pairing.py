@@ -1,0 +1,73 @@
+"""Host logic of the paired decode: pair_plan's links and the count of tokens
+the paired kernel loads (pair_loaded_tokens), against closed forms."""
+import numpy as np
+import pytest
+
+import workload as W
+from workload.recipe import _layout
+from paged_gqa_kv_amd.session import pair_loaded_tokens, pair_plan
+
+
+def _tables(lens, shared_tokens, seed=3):
+    wl = W.custom("pairs", 1, lens, seed=seed, spare_blocks=2, shared_prefix_tokens=shared_tokens)
+    lens, blocks, _, _, table, _, _, _ = _layout(wl)
+    return list(lens), blocks, table
+
+
+def test_pair_plan_links_sharers_in_batch_order():
+    lens = [700, 100, 0, 333, 288, 1000, 40]
+    _, blocks, table = _tables(lens, 288)
+    role = pair_plan(table, blocks)
+    # sharers (non-empty) in batch order: 0 1 3 4 5 6 -> pairs (0,1) (3,4) (5,6)
+    assert role.tolist() == [1, -2, -1, 4, -5, 6, -7]
+
+
+def test_pair_plan_leaves_odd_one_and_private_sequences_alone():
+    lens = [500, 20, 300]
+    _, blocks, table = _tables(lens, 0)          # no shared prefix: every first block differs
+    assert (pair_plan(table, blocks) == -1).all()
+    _, blocks, table = _tables(lens, 64)          # three sharers: (0, 1) paired, 2 alone
+    assert pair_plan(table, blocks).tolist() == [1, -2, -1]
+
+
+@pytest.mark.parametrize("split_blocks", [1, 3, 8, 128, 1024])
+def test_loaded_tokens_closed_form_for_shared_prefix(split_blocks):
+    # every position of the prefix range is the same block for both sequences
+    # of a pair, so each pair saves min(len_a, len_b, prefix) tokens at any split
+    rng = np.random.default_rng(11)
+    prefix = 2048
+    lens = rng.integers(1, 6000, size=20).tolist() + [prefix, 2047, 2049, 16]
+    _, blocks, table = _tables(lens, prefix)
+    role = pair_plan(table, blocks)
+    saved = sum(min(lens[a], lens[b], prefix) for a in range(len(lens))
+                for b in [int(role[a])] if b >= 0)
+    assert pair_loaded_tokens(table, lens, role, split_blocks) == sum(lens) - saved
+
+
+def test_loaded_tokens_without_links_is_every_token():
+    lens = [700, 100, 333, 288, 1000, 40, 517]
+    _, blocks, table = _tables(lens, 288)
+    B = len(lens)
+    for role in ([-1] * B,
+                 [1] + [-1] * (B - 1),                 # one-sided
+                 [0] + [-1] * (B - 1),                 # self
+                 [B + 3, -2] + [-1] * (B - 2),         # out of range
+                 [1, -2 - 5] + [-1] * (B - 2)):        # partner links elsewhere
+        assert pair_loaded_tokens(table, lens, np.asarray(role), 4) == sum(lens)
+
+
+def test_loaded_tokens_split_joint_only_at_equal_first_block():
+    # sequence 1 diverges at position 2: with 2-block splits the second split
+    # starts on different blocks and is not joint; with 4-block splits it is,
+    # and the differing positions are loaded for both sequences
+    table = np.array([[0, 1, 2, 3], [0, 1, 5, 6]], dtype=np.int32)
+    lens = [64, 60]
+    role = np.array([1, -2])
+    assert pair_loaded_tokens(table, lens, role, 2) == 32 + 32 + 28
+    assert pair_loaded_tokens(table, lens, role, 4) == 32 + 32 + 28
+    # reversed roles: sequence 1 is the first of the pair; same loads
+    assert pair_loaded_tokens(table, lens, np.array([-3, 0]), 4) == 92
+    # the shorter sequence ends inside the shared range
+    table = np.array([[0, 1, 2, 3], [0, 1, 2, 7]], dtype=np.int32)
+    assert pair_loaded_tokens(table, [64, 40], role, 4) == 64
+    assert pair_loaded_tokens(table, [64, 40], role, 1) == 64
