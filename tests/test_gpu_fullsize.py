@@ -38,8 +38,9 @@ def _host_layer(m, s, layer):
 
 
 def _run(name, alpha, steps=2, rows=8, oracle_layers=1, seqs_for_layer_mass=None,
-         kv_format="fp16"):
-    print(f"\n[case] full size {name} ({kv_format} KV), alpha {alpha}, {steps} steps", flush=True)
+         kv_format="fp16", pair=False):
+    print(f"\n[case] full size {name} ({kv_format} KV{', paired' if pair else ''}), alpha {alpha}, "
+          f"{steps} steps", flush=True)
     wl = W.WORKLOADS[name]
     if kv_format == "e4m3":
         wl = W.as_e4m3(wl)
@@ -48,7 +49,7 @@ def _run(name, alpha, steps=2, rows=8, oracle_layers=1, seqs_for_layer_mass=None
     m = W.materialise(wl, DEV)
     torch.cuda.synchronize()
     L = m.num_layers
-    sess = DecodeSession(m)
+    sess = DecodeSession(m, pair_role="auto" if pair else None)
     pol = OS.Policy(alpha=alpha)
     gpol = api.policy(alpha)
     offsets = m.meta_offsets.cpu().numpy()
@@ -64,6 +65,17 @@ def _run(name, alpha, steps=2, rows=8, oracle_layers=1, seqs_for_layer_mass=None
         assert not stale.any()
     torch.cuda.synchronize()
     assert sess.status() == 0
+    if pair:
+        # the paired decode gives the unpaired decode's bits at the same split
+        ref = DecodeSession(m, split_blocks=sess.split_blocks)
+        ref.decode(q)
+        torch.cuda.synchronize()
+        assert torch.equal(ref.out.view(torch.int16), sess.out.view(torch.int16))
+        assert torch.equal(ref.mass.view(torch.int32), sess.mass.view(torch.int32))
+        assert ref.status() == 0
+        del ref
+        print(f"  paired decode bit-identical to the unpaired decode at split "
+              f"{sess.split_blocks}", flush=True)
     err, near = P.check_records(sess.records(), state, pol)
     print(f"  scoring: max |dE| {err:.2e}, {near} labels inside the cut-point band", flush=True)
 
@@ -135,6 +147,11 @@ def test_fullsize_128k_context_alpha_015():
 def test_fullsize_shared_prefix_batch():
     _run("decode-80L-32xMixed-shared2K", 0.15, steps=2, rows=12, oracle_layers=1,
          seqs_for_layer_mass=[0, 7, 31])
+
+
+def test_fullsize_shared_prefix_batch_paired():
+    _run("decode-80L-32xMixed-shared2K", 0.15, steps=2, rows=8, oracle_layers=1,
+         seqs_for_layer_mass=[0, 1, 30], pair=True)
 
 
 def test_fullsize_1m_context():
