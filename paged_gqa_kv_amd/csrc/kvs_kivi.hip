@@ -23,9 +23,9 @@ namespace kvs {
 // The split-K decode above over a KIVI cache (Fitting a Million Tokens, Sec.
 // 02: 2-bit codes plus fp16 scales, dequantised inside the attention kernel).
 // Quantised blocks come in 32-token pairs (one key group).  A wave loads a
-// pair's four 768-byte tiles of its (layer, KV head) with three coalesced
-// 16-byte loads per lane into a register ring, stages them in LDS and works on
-// the codes directly, never forming dequantised keys or values:
+// pair's four 768-byte tiles of its (layer, KV head) with one coalesced
+// 16-byte load per lane and tile into a register slot, stages them in LDS and
+// works on the codes directly, never forming dequantised keys or values:
 //  QK:  S^T[t][h] = sum_d c[t][d] (q[h][d] s[d]) + sum_d q[h][d] z[d].  The
 //       pair's per-channel scales fold into the query as an fp16 pair
 //       q s = hi + lo (v_pk_mul_f16, then v_pk_fma_f16 of the remainder:
@@ -42,7 +42,11 @@ namespace kvs {
 //  fp16 residual blocks (from quant_lens[s] on) run one by one with the same
 //  operand layouts (value tile transposed through LDS).
 // ---------------------------------------------------------------------------
-constexpr int kKiviRing = 2;     // 32-token pairs in flight per wave
+// 32-token pairs in flight per wave.  A pair is staged in LDS as soon as its
+// loads land, so one slot already overlaps the next pair's loads with this
+// pair's arithmetic; two slots measured 4 % slower (more registers, larger
+// loop body) in this issue-bound kernel.
+constexpr int kKiviRing = 1;
 
 // The 8 codes of one set (code m at bits 4 m, 4 m + 1 of w, other bits 0) as
 // fp16 0..3: E2M1 reads a nibble 0..3 as 0, 0.5, 1, 1.5; the scale 2 makes
@@ -198,18 +202,17 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
     const size_t kblock = (size_t)a.num_layers * 16 * kKiviTileBytes;
     const size_t ktile = ((size_t)(layer * 2) * 8 + g) * kKiviTileBytes;
     const size_t vtile = ((size_t)(layer * 2 + 1) * 8 + g) * kKiviTileBytes;
-    // lane's 16-byte pieces: byte 1024 k + 16 lane of [K even | K odd | V even | V odd]
-    int piece_tile[3], piece_off[3];
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const int P = 1024 * k + 16 * lane;
-      piece_tile[k] = P / kKiviTileBytes;
-      piece_off[k] = P - piece_tile[k] * kKiviTileBytes;
-    }
+    // A lane loads 16 bytes of each of the pair's four 768-byte tiles [K even |
+    // K odd | V even | V odd] and writes them to the same place in the stage.
+    // Lanes 48..63 repeat lanes 0..15: the same bytes in the same load
+    // instruction (no extra memory traffic) and the same values to the same LDS
+    // bytes.  Each load so has one wave-uniform base, held in scalar registers,
+    // and the pair's address arithmetic stays off the VALU.
+    const uint32_t voff = 16u * (uint32_t)(lane < 48 ? lane : lane - 48);
     // Loads of the pair starting at block be; pairs past the split's quantised
     // range reuse its last pair (in-bounds, unused), ids outside the pool read
     // block 0 and are masked.
-    auto load_pair = [&](u4_t (&r)[3], int be, bool* ok) {
+    auto load_pair = [&](u4_t (&r)[4], int be, bool* ok) {
       const int cl = min(be, bq1 - 2);
       // block ids are wave-uniform: scalar registers keep the address math off the VALU
       const int pe = __builtin_amdgcn_readfirstlane(tbl[cl - b0]);
@@ -219,15 +222,13 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
       *ok = in && be < bq1;
       const uint8_t* pe_p = a.kivi + (size_t)(in ? pe : 0) * kblock;
       const uint8_t* po_p = a.kivi + (size_t)(in ? po : 0) * kblock;
-#pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const int ti = piece_tile[k];
-        const uint8_t* base = ((ti & 1) ? po_p : pe_p) + ((ti & 2) ? vtile : ktile);
-        r[k] = stream_load(reinterpret_cast<const u4_t*>(base + piece_off[k]));
-      }
+      r[0] = stream_load(reinterpret_cast<const u4_t*>(pe_p + ktile + voff));
+      r[1] = stream_load(reinterpret_cast<const u4_t*>(po_p + ktile + voff));
+      r[2] = stream_load(reinterpret_cast<const u4_t*>(pe_p + vtile + voff));
+      r[3] = stream_load(reinterpret_cast<const u4_t*>(po_p + vtile + voff));
     };
 
-    u4_t ring[kKiviRing][3];
+    u4_t ring[kKiviRing][4];
     bool ring_ok[kKiviRing];
 #pragma unroll
     for (int k = 0; k < kKiviRing; ++k) load_pair(ring[k], b0 + 2 * k, &ring_ok[k]);
@@ -240,8 +241,8 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
         const bool ok = ring_ok[k];
         saw_bad |= active && !ok;
 #pragma unroll
-        for (int kk = 0; kk < 3; ++kk)
-          *reinterpret_cast<u4_t*>(stage + 1024 * kk + 16 * lane) = ring[k][kk];
+        for (int t = 0; t < 4; ++t)
+          *reinterpret_cast<u4_t*>(stage + kKiviTileBytes * t + voff) = ring[k][t];
         load_pair(ring[k], be + 2 * kKiviRing, &ring_ok[k]);
         if (!active) continue;
         if (!ok) {
@@ -256,32 +257,35 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
         // key scales of the lane's channels folded into q (exact hi + lo), and the
         // zero-point term sum_d z[d] q[h][d] from MFMAs whose A rows all hold z:
         // it lands in every token row, so it starts both blocks' accumulators.
-        h8_t qhi[4], qlo[4];
         f4_t zsacc = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint8_t* km = stage + (i >> 1) * kKiviTileBytes + 512 + 2 * (32 * (i & 1) + 8 * j);
-          const h8_t s8 = *reinterpret_cast<const h8_t*>(km);
-          const h8_t z8 = *reinterpret_cast<const h8_t*>(km + 128);
-          qhi[i] = qb[i] * s8;
-          qlo[i] = __builtin_elementwise_fma(qb[i], s8, -qhi[i]);
-          zsacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(z8, qb[i], zsacc, 0, 0, 0);
+          const uint8_t* km = stage + (i >> 1) * kKiviTileBytes + 640 + 2 * (32 * (i & 1) + 8 * j);
+          zsacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const h8_t*>(km), qb[i],
+                                                         zsacc, 0, 0, 0);
         }
 
-        // ---- logits of both blocks (two independent MFMA chains), one softmax update
+        // ---- logits of both blocks (two independent MFMA chains), one softmax update.
+        // The scaled query of channel slice i is formed just before its MFMAs, so
+        // only one slice's hi / lo operands are live at a time.
         f4_t sacc[2] = {zsacc, zsacc};
         u2_t kent[2];
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
           kent[hb] = *reinterpret_cast<const u2_t*>(stage + hb * kKiviTileBytes + 8 * lane);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+          const uint8_t* km = stage + (i >> 1) * kKiviTileBytes + 512 + 2 * (32 * (i & 1) + 8 * j);
+          const h8_t s8 = *reinterpret_cast<const h8_t*>(km);
+          const h8_t qhi = qb[i] * s8;
+          const h8_t qlo = __builtin_elementwise_fma(qb[i], s8, -qhi);
 #pragma unroll
           for (int hb = 0; hb < 2; ++hb) {
             const h8_t kc = codes_to_h8(code_set(kent[hb], i));
-            sacc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc, qhi[i], sacc[hb], 0, 0, 0);
-            sacc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc, qlo[i], sacc[hb], 0, 0, 0);
+            sacc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc, qhi, sacc[hb], 0, 0, 0);
+            sacc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc, qlo, sacc[hb], 0, 0, 0);
           }
+        }
         float sv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) sv[i] = (hi ? sacc[1][i] : sacc[0][i]) * a.scale_log2;
