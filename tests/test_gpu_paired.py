@@ -56,6 +56,54 @@ def test_paired_decode_bits_and_oracle(split_blocks):
     assert par.status() == 0 and ref.status() == 0
 
 
+def _check_pairing(m, role, split_blocks, step=0):
+    par = DecodeSession(m, split_blocks=split_blocks, pair_role=np.asarray(role, dtype=np.int32))
+    ref = DecodeSession(m, split_blocks=split_blocks)
+    q = W.make_query(m, step)
+    ref.decode(q)
+    par.decode(q)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(par.out), _bits(ref.out))
+    assert torch.equal(_bits(par.mass), _bits(ref.mass))
+    out_ref, mass_ref = P.oracle_decode(P.host(m), q)
+    P.check_out(par.out, out_ref, range(m.num_layers))
+    P.check_mass(par.mass, mass_ref, m.meta_offsets.cpu().numpy())
+    assert par.status() == 0 and ref.status() == 0
+
+
+@pytest.mark.parametrize("split_blocks", [4, 16])
+def test_paired_decode_first_sequence_shorter(split_blocks):
+    _case(f"pairs whose first sequence is the shorter one, split_blocks={split_blocks}")
+    m = _shared_workload(seed=4)
+    # reverse every link of the shared-prefix plan: the second sequence of each
+    # pair becomes the first, so joint splits run past the first one's end
+    plan = pair_plan(m.table_host, m.blocks)
+    role = np.full(m.batch, -1, dtype=np.int32)
+    for a_, b_ in ((a_, int(plan[a_])) for a_ in range(m.batch) if plan[a_] >= 0):
+        role[b_] = a_
+        role[a_] = -2 - b_
+    _check_pairing(m, role, split_blocks)
+
+
+def test_paired_decode_shared_blocks_between_private_ones():
+    _case("pairs sharing blocks at some positions only (shared, private, shared again)")
+    m = W.materialise(W.custom("mix", 2, [300, 250, 180, 400], seed=21, spare_blocks=4), DEV)
+    # make sequence 1 share sequence 0's blocks at positions 0-3 and 8-11 (4-7
+    # stay its own), and sequence 3 share sequence 2's blocks at positions 4-7
+    # and 9 (not at 0-3 or 8); the tables on both sides of the boundary change
+    # together.  Splits of 4 then have joint splits after private ones, and a
+    # shared position inside a split that is not joint.
+    t = m.table_host
+    for b in (0, 1, 2, 3, 8, 9, 10, 11):
+        t[1, b] = t[0, b]
+    for b in (4, 5, 6, 7, 9):
+        t[3, b] = t[2, b]
+    m.block_table.copy_(torch.from_numpy(t).to(DEV))
+    role = [1, -2, 3, -4]
+    for sb in (4, 8, 16):
+        _check_pairing(m, role, sb)
+
+
 def test_inconsistent_pair_roles_change_nothing():
     _case("pair_role arrays with broken, one-sided, self and out-of-range links")
     m = _shared_workload(seed=3)
