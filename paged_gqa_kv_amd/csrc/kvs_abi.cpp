@@ -109,8 +109,9 @@ int check_counts(int32_t batch, int32_t max_blocks) {
 // enough bytes in flight on the whole chip (wave count) and per compute unit
 // (waves that fit the LDS a split needs, at most the kernel's waves per SIMD).
 // Reads one decode wave keeps in flight: two fp16 blocks or two two-block E4M3
-// steps (K and V tiles of its KV head), or two 32-token quantised pairs (4
-// tiles of 768 bytes each).
+// steps (K and V tiles of its KV head).  For KIVI the figure is a sizing
+// constant of two 32-token pairs (4 tiles of 768 bytes each): the kernel has
+// one pair's loads in flight while it works on the previous pair from LDS.
 uint64_t wave_inflight_bytes(int32_t kv_format) {
   switch (kv_format) {
     case KVS_KV_FP16: return 2ull * 2ull * 4096ull;
@@ -452,7 +453,7 @@ int decode_step(int32_t kv_format, const kvs_shape* shape, const void* q, const 
     if (e != hipSuccess) return hip_fail(e, "recording the before-decode event");
   }
   e = kvs::launch_decode(d, batch, st);
-  if (e != hipSuccess) return hip_fail(e, "paged_decode_gqa launch");
+  if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
   if (g_ev_after) {
     e = hipEventRecord(g_ev_after, st);
     if (e != hipSuccess) return hip_fail(e, "recording the after-decode event");
@@ -473,8 +474,9 @@ int kvs_decode_step(const kvs_shape* shape, const void* q, const void* kv_pool, 
                     float* block_mass, int accumulate, int32_t split_blocks, void* workspace,
                     size_t workspace_bytes, void* stream) {
   return decode_step(KVS_KV_FP16, shape, q, kv_pool, pool_blocks, nullptr, 0, block_table,
-                     max_blocks_per_seq, seq_lens, nullptr, nullptr, meta_offsets, batch, total_blocks, layer_begin, layer_end, scale,
-                     out, block_mass, accumulate, split_blocks, workspace, workspace_bytes, stream);
+                     max_blocks_per_seq, seq_lens, nullptr, nullptr, meta_offsets, batch,
+                     total_blocks, layer_begin, layer_end, scale, out, block_mass, accumulate,
+                     split_blocks, workspace, workspace_bytes, stream);
 }
 
 int kvs_decode_step_e4m3(const kvs_shape* shape, const void* q, const void* kv_pool,
@@ -485,9 +487,9 @@ int kvs_decode_step_e4m3(const kvs_shape* shape, const void* q, const void* kv_p
                          float* block_mass, int accumulate, int32_t split_blocks, void* workspace,
                          size_t workspace_bytes, void* stream) {
   return decode_step(KVS_KV_E4M3, shape, q, kv_pool, pool_blocks, nullptr, 0, block_table,
-                     max_blocks_per_seq, seq_lens, nullptr, nullptr, meta_offsets, batch, total_blocks,
-                     layer_begin, layer_end, scale, out, block_mass, accumulate, split_blocks,
-                     workspace, workspace_bytes, stream);
+                     max_blocks_per_seq, seq_lens, nullptr, nullptr, meta_offsets, batch,
+                     total_blocks, layer_begin, layer_end, scale, out, block_mass, accumulate,
+                     split_blocks, workspace, workspace_bytes, stream);
 }
 
 int kvs_decode_step_paired(const kvs_shape* shape, const void* q, const void* kv_pool,
@@ -515,9 +517,8 @@ int kvs_decode_step_kivi(const kvs_shape* shape, const void* q, const void* kv_p
                          size_t workspace_bytes, void* stream) {
   return decode_step(KVS_KV_KIVI2, shape, q, kv_pool, pool_blocks, kivi_pool, kivi_blocks,
                      block_table, max_blocks_per_seq, seq_lens, quant_lens, nullptr, meta_offsets,
-                     batch,
-                     total_blocks, layer_begin, layer_end, scale, out, block_mass, accumulate,
-                     split_blocks, workspace, workspace_bytes, stream);
+                     batch, total_blocks, layer_begin, layer_end, scale, out, block_mass,
+                     accumulate, split_blocks, workspace, workspace_bytes, stream);
 }
 
 size_t kvs_kivi_advance_workspace_bytes(int32_t batch) {
