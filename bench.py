@@ -63,8 +63,9 @@ def _parse():
     ap.add_argument("--append", action="store_true",
                     help="each step first appends one token per sequence (kvs_append_kv)")
     ap.add_argument("--pair-sharers", action="store_true",
-                    help="fp16: pair sequences that share their first block "
-                         "(kvs_decode_step_paired), so a shared block is loaded once per pair")
+                    help="fp16 / E4M3: pair sequences that share their first block "
+                         "(kvs_decode_step_paired, kvs_decode_step_e4m3_paired), so a shared "
+                         "block is loaded once per pair")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="approximate CPU time budget of the oracle baseline (0 = skip)")
     ap.add_argument("--copy-probe-gib", type=float, default=4.0,
@@ -215,8 +216,8 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this path shards by "
               "sequence or by block range across GPUs, which is not built here.", file=sys.stderr)
         sys.exit(2)
-    if args.pair_sharers and (args.kv_format != "fp16" or args.append):
-        print("--pair-sharers runs the fp16 decode without appends", file=sys.stderr)
+    if args.pair_sharers and (args.kv_format == "kivi2" or args.append):
+        print("--pair-sharers runs the fp16 or E4M3 decode without appends", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -455,6 +455,31 @@ int kvs_decode_step_paired(const kvs_shape* shape,
                            void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* kvs_decode_step_paired over an FP8 E4M3 pool: the decode of
+ * kvs_decode_step_e4m3 with pairs of sequences that share blocks decoded by one
+ * wave.  That decode takes blocks two at a time from the split's first block;
+ * a pair shares a step when no position of its two blocks holds different
+ * physical blocks in the two sequences (a position only one of them reaches is
+ * loaded for that one), and decodes the two positions separately otherwise.
+ * The results are bit-identical to kvs_decode_step_e4m3 whatever the pairing.
+ * pair_role, split_blocks (at most 512; 0 chooses as kvs_decode_split_blocks
+ * does for KVS_KV_E4M3, capped at 256) and every other argument as in
+ * kvs_decode_step_paired; the workspace must fit
+ * kvs_decode_workspace_bytes(..., KVS_KV_E4M3, ..., that split). */
+int kvs_decode_step_e4m3_paired(const kvs_shape* shape,
+                                const void* q,
+                                const void* kv_pool, int64_t pool_blocks,
+                                const int32_t* block_table, int32_t max_blocks_per_seq,
+                                const int32_t* seq_lens, const int32_t* pair_role,
+                                const int32_t* meta_offsets,
+                                int32_t batch, int64_t total_blocks,
+                                int32_t layer_begin, int32_t layer_end,
+                                float scale,
+                                void* out, float* block_mass, int accumulate,
+                                int32_t split_blocks,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 /* Workspace bytes kvs_append_kv needs (status header + two words per sequence). */
 size_t kvs_append_workspace_bytes(int32_t batch);
 

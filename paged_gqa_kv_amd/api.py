@@ -161,6 +161,20 @@ def decode_step_paired(shp: Shape, q, kv_pool, pool_blocks: int, block_table, ma
                                        split_blocks, _p(workspace), ws_bytes, _s(stream)))
 
 
+def decode_step_e4m3_paired(shp: Shape, q, kv_pool, pool_blocks: int, block_table,
+                            max_blocks: int, seq_lens, pair_role, meta_offsets, batch: int,
+                            total_blocks: int, layer_begin: int, layer_end: int, scale: float,
+                            out, block_mass, accumulate: int, split_blocks: int, workspace,
+                            workspace_bytes=None, stream=None) -> None:
+    ws_bytes = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    check(lib().kvs_decode_step_e4m3_paired(ctypes.byref(shp), _p(q), _p(kv_pool), pool_blocks,
+                                            _p(block_table), max_blocks, _p(seq_lens),
+                                            _p(pair_role), _p(meta_offsets), batch, total_blocks,
+                                            layer_begin, layer_end, scale, _p(out),
+                                            _p(block_mass), accumulate, split_blocks,
+                                            _p(workspace), ws_bytes, _s(stream)))
+
+
 def decode_step_kivi(shp: Shape, q, kv_pool, pool_blocks: int, kivi_pool, kivi_blocks: int,
                      block_table, max_blocks: int, seq_lens, quant_lens, meta_offsets, batch: int,
                      total_blocks: int, layer_begin: int, layer_end: int, scale: float, out,

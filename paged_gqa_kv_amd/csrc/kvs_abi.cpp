@@ -59,6 +59,10 @@ constexpr int32_t kMaxAutoSplit = 1024;
 constexpr int32_t kMaxAutoSplitE4M3 = 512;
 constexpr int32_t kMaxAutoSplitKivi = 128;
 constexpr uint64_t kChipSimds = 1024;   // gfx950: 256 compute units x 4 SIMDs
+// Automatic split of an E4M3 paired decode: at 512 blocks the paired LDS
+// leaves 4 waves per CU, too few for that decode's instruction stream (14.0
+// against 11.7 ms at 256 on the 32-sequence shared-prefix batch); 256 leaves 7.
+constexpr int32_t kMaxAutoPairSplitE4M3 = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -363,15 +367,16 @@ int decode_step(int32_t kv_format, const kvs_shape* shape, const void* q, const 
     return fail(KVS_E_ALIGN, "int32 / fp32 arrays must be 4-byte aligned");
   if (!aligned(workspace, kAlign)) return fail(KVS_E_ALIGN, "workspace must be 256-byte aligned");
   if (pair_role) {
-    if (kv_format != KVS_KV_FP16)
-      return fail(KVS_E_RANGE, "paired decode runs over fp16 pools only");
+    if (kv_format != KVS_KV_FP16 && kv_format != KVS_KV_E4M3)
+      return fail(KVS_E_RANGE, "paired decode runs over fp16 or E4M3 pools only");
     if (!aligned(pair_role, 4)) return fail(KVS_E_ALIGN, "pair_role must be 4-byte aligned");
     if (split_blocks > kvs::kMaxPairSplit)
       return fail(KVS_E_RANGE, "split_blocks %d above %d for a paired decode", split_blocks,
                   kvs::kMaxPairSplit);
     if (split_blocks == 0) {
+      const int32_t cap = kv_format == KVS_KV_E4M3 ? kMaxAutoPairSplitE4M3 : kvs::kMaxPairSplit;
       split_blocks = choose_split(batch, max_blocks_per_seq, layer_end - layer_begin, kv_format);
-      if (split_blocks > kvs::kMaxPairSplit) split_blocks = kvs::kMaxPairSplit;
+      if (split_blocks > cap) split_blocks = cap;
     }
   }
   DecodeLayout L;
@@ -502,6 +507,21 @@ int kvs_decode_step_paired(const kvs_shape* shape, const void* q, const void* kv
                            void* stream) {
   if (!pair_role) return fail(KVS_E_NULL, "pair_role is NULL");
   return decode_step(KVS_KV_FP16, shape, q, kv_pool, pool_blocks, nullptr, 0, block_table,
+                     max_blocks_per_seq, seq_lens, nullptr, pair_role, meta_offsets, batch,
+                     total_blocks, layer_begin, layer_end, scale, out, block_mass, accumulate,
+                     split_blocks, workspace, workspace_bytes, stream);
+}
+
+int kvs_decode_step_e4m3_paired(const kvs_shape* shape, const void* q, const void* kv_pool,
+                                int64_t pool_blocks, const int32_t* block_table,
+                                int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                const int32_t* pair_role, const int32_t* meta_offsets,
+                                int32_t batch, int64_t total_blocks, int32_t layer_begin,
+                                int32_t layer_end, float scale, void* out, float* block_mass,
+                                int accumulate, int32_t split_blocks, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!pair_role) return fail(KVS_E_NULL, "pair_role is NULL");
+  return decode_step(KVS_KV_E4M3, shape, q, kv_pool, pool_blocks, nullptr, 0, block_table,
                      max_blocks_per_seq, seq_lens, nullptr, pair_role, meta_offsets, batch,
                      total_blocks, layer_begin, layer_end, scale, out, block_mass, accumulate,
                      split_blocks, workspace, workspace_bytes, stream);

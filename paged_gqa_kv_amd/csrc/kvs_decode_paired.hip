@@ -55,10 +55,11 @@ __device__ __forceinline__ bool joint_split(const DecodeArgs& a, int sa, int sb_
   return a.table[(size_t)sa * a.max_nb + b0] == a.table[(size_t)sb_ * a.max_nb + b0];
 }
 
-// One step of the pair's walk: the block to load, which column groups are
-// live (bit 0: A, bit 1: B) and the logical position.
+// One step of the pair's walk: the kPer blocks to load, which column groups
+// are live (bit 0: A, bit 1: B) and the first logical position.
+template <int kPer>
 struct PairStep {
-  int pid;
+  int pid[kPer];
   int mask;
   int b;
 };
@@ -66,9 +67,9 @@ struct PairStep {
 }  // namespace
 
 // The LDS of a paired split keeps at most 2 work-groups per SIMD; the launch
-// bound gives the kernel their VGPR budget (178, no spills).
+// bound gives the kernel their VGPR budget (fp16: 178, no spills).
+template <class F>
 __global__ void __launch_bounds__(64, 2) paged_decode_pair(DecodeArgs a) {
-  using F = KvF16;
   extern __shared__ __align__(16) uint8_t smem[];
   const int SB = a.split_blocks;
   // LDS layout (decode_pair_lds_bytes): block ids of A and B, mass partials of
@@ -139,45 +140,63 @@ __global__ void __launch_bounds__(64, 2) paged_decode_pair(DecodeArgs a) {
     for (int i = 0; i < 4; ++i) qb[i] = h8_t{0, 0, 0, 0, 0, 0, 0, 0};
   }
 
-  // ---- the walk: steps over positions [b0, bend)
-  auto shared_at = [&](int b) {
-    return b < b1A && b < b1B && tbl[b - b0] == tbl[SB + b - b0];
+  // ---- the walk: steps over groups of kPer positions from b0, the grouping of
+  // paged_decode_gqa.  A group is joint when no position of it holds
+  // different blocks in A and B (a position only one of them reaches is
+  // loaded for that one); a joint group is one step with both column groups
+  // live, any other group one step for A's blocks and one for B's.
+  constexpr int kPer = F::kPer;
+  const int cachedA = tbl[b1A - 1 - b0];                    // an in-split block of A
+  const int cachedB = paired ? tbl[SB + b1B - 1 - b0] : cachedA;
+  auto joint_group = [&](int b) {
+    bool joint = true;
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+      const int q = b + p;
+      joint &= !(q < b1A && q < b1B && tbl[q - b0] != tbl[SB + q - b0]);
+    }
+    return joint;
   };
+  const int ngroups = (bend - b0 + kPer - 1) / kPer;
   int nsteps = 0;
-  for (int i = lane; i < bend - b0; i += 64) {
-    const int b = b0 + i;
-    nsteps += shared_at(b) ? 1 : (int)(b < b1A) + (int)(b < b1B);
-  }
+  for (int i = lane; i < ngroups; i += 64) nsteps += joint_group(b0 + kPer * i) ? 1 : 2;
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) nsteps += __shfl_xor(nsteps, m, 64);
 
-  int cur_b = b0, cur_ph = 0;   // load cursor: position and, for an unshared position, A done
-  auto next_step = [&]() -> PairStep {
-    PairStep st;
-    if (cur_b >= bend) {          // past the end: a cached block of the split, nothing live
-      st.pid = tbl[b1A - 1 - b0];
-      st.mask = 0;
-      st.b = b0;
-      return st;
-    }
+  int cur_b = b0, cur_ph = 0;   // load cursor: first position of the group; A done
+  auto next_step = [&]() -> PairStep<kPer> {
+    PairStep<kPer> st;
     const int b = cur_b;
-    const bool hasA = b < b1A, hasB = b < b1B;
-    st.b = b;
-    if (shared_at(b)) {
-      st.pid = tbl[b - b0];
+    st.b = b0;
+    st.mask = 0;
+    if (b >= bend) {              // past the end: cached blocks of the split, nothing live
+#pragma unroll
+      for (int p = 0; p < kPer; ++p) st.pid[p] = cachedA;
+    } else if (joint_group(b)) {
+      st.b = b;
       st.mask = 3;
-      ++cur_b;
-    } else if (cur_ph == 0 && hasA) {
-      st.pid = tbl[b - b0];
+#pragma unroll
+      for (int p = 0; p < kPer; ++p) {
+        const int q = b + p;
+        st.pid[p] = q < b1A ? tbl[q - b0] : q < b1B ? tbl[SB + q - b0] : cachedA;
+      }
+      cur_b += kPer;
+    } else if (cur_ph == 0) {     // both reach the group: A's blocks, then B's
+      st.b = b;
       st.mask = 1;
-      if (hasB) cur_ph = 1; else ++cur_b;
+#pragma unroll
+      for (int p = 0; p < kPer; ++p) st.pid[p] = b + p < b1A ? tbl[b + p - b0] : cachedA;
+      cur_ph = 1;
     } else {
-      st.pid = tbl[SB + b - b0];
+      st.b = b;
       st.mask = 2;
+#pragma unroll
+      for (int p = 0; p < kPer; ++p) st.pid[p] = b + p < b1B ? tbl[SB + b + p - b0] : cachedB;
       cur_ph = 0;
-      ++cur_b;
+      cur_b += kPer;
     }
-    st.pid = __builtin_amdgcn_readfirstlane(st.pid);
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) st.pid[p] = __builtin_amdgcn_readfirstlane(st.pid[p]);
     st.mask = __builtin_amdgcn_readfirstlane(st.mask);
     st.b = __builtin_amdgcn_readfirstlane(st.b);
     return st;
@@ -199,16 +218,19 @@ __global__ void __launch_bounds__(64, 2) paged_decode_pair(DecodeArgs a) {
   for (int k = 0; k < 8; ++k) acc[k] = f4_t{0.f, 0.f, 0.f, 0.f};
 
   constexpr int kRing = F::kRing;
-  BlockRegs<F> ring[kRing];
+  StepRegs<F> ring[kRing];
   int ring_mask[kRing], ring_b[kRing];
-  bool ring_ok[kRing];
-#pragma unroll
-  for (int k = 0; k < kRing; ++k) {
-    const PairStep st = next_step();
+  bool ring_ok[kRing][kPer];
+  auto load_next = [&](int k) {
+    const PairStep<kPer> st = next_step();
     ring_mask[k] = st.mask;
     ring_b[k] = st.b;
-    load_block(ring[k], step_base(st.pid, &ring_ok[k]), lane, c, j);
-  }
+#pragma unroll
+    for (int p = 0; p < kPer; ++p)
+      load_block(ring[k].blk[p], step_base(st.pid[p], &ring_ok[k][p]), lane, c, j);
+  };
+#pragma unroll
+  for (int k = 0; k < kRing; ++k) load_next(k);
 
   bool saw_bad = false;
   for (int sbase = 0; sbase < nsteps; sbase += kRing) {
@@ -216,52 +238,73 @@ __global__ void __launch_bounds__(64, 2) paged_decode_pair(DecodeArgs a) {
     for (int k = 0; k < kRing; ++k) {
       const int mask = sbase + k < nsteps ? ring_mask[k] : 0;
       const int b = ring_b[k];
-      const bool ok = ring_ok[k];
-      saw_bad |= mask != 0 && !ok;
-      const int vA = (mask & 1) && ok ? min(16, nA - 16 * b) : 0;
-      const int vB = (mask & 2) && ok ? min(16, nB - 16 * b) : 0;
-      const int vown = hi ? vB : vA;
-      const int vrows = max(vA, vB);
+      int vown[kPer], vrows[kPer];
+      bool own_active[kPer];
+#pragma unroll
+      for (int p = 0; p < kPer; ++p) {
+        const int q = b + p;
+        const bool ok = ring_ok[k][p];
+        const bool liveA = (mask & 1) && q < b1A;
+        const bool liveB = (mask & 2) && q < b1B;
+        saw_bad |= (liveA || liveB) && !ok;
+        const int vA = liveA && ok ? min(16, nA - 16 * q) : 0;
+        const int vB = liveB && ok ? min(16, nB - 16 * q) : 0;
+        vown[p] = hi ? vB : vA;
+        vrows[p] = max(vA, vB);
+        own_active[p] = hi ? liveB : liveA;
+      }
 
-      // ---- value tile to LDS (the slot's value registers are free after this)
-      stage_values<F>(ring[k], vstage, lane, 0);
+      // ---- value tiles to LDS (the slot's value registers are free after this)
+#pragma unroll
+      for (int p = 0; p < kPer; ++p) stage_values<F>(ring[k].blk[p], vstage, lane, p);
 
-      // ---- logits of 16 tokens x 16 columns
-      f4_t sacc = f4_t{0.f, 0.f, 0.f, 0.f};
+      // ---- logits of 16 tokens x 16 columns per block
+      f4_t sacc[kPer];
+#pragma unroll
+      for (int p = 0; p < kPer; ++p) sacc[p] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_operand<F>(ring[k], i), qb[i], sacc,
-                                                      0, 0, 0);
+#pragma unroll
+        for (int p = 0; p < kPer; ++p)
+          sacc[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_operand<F>(ring[k].blk[p], i),
+                                                           qb[i], sacc[p], 0, 0, 0);
 
       // ---- refill this slot with the step kRing ahead
-      {
-        const PairStep st = next_step();
-        ring_mask[k] = st.mask;
-        ring_b[k] = st.b;
-        load_block(ring[k], step_base(st.pid, &ring_ok[k]), lane, c, j);
+      load_next(k);
+
+      float sv[kPer][4];
+#pragma unroll
+      for (int p = 0; p < kPer; ++p) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[p][i] = sacc[p][i] * a.scale_log2;
+        if (vown[p] < 16) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (4 * j + i >= vown[p]) sv[p][i] = -INFINITY;
+        }
       }
 
-      float sv[4];
+      // ---- online softmax over the step (per column; the 4 lanes j share a column)
+      float bm = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sv[i] = sacc[i] * a.scale_log2;
-      if (vown < 16) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (4 * j + i >= vown) sv[i] = -INFINITY;
-      }
-
-      // ---- online softmax (per column; the 4 lanes j share a column)
-      float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      for (int p = 0; p < kPer; ++p)
+        bm = fmaxf(bm, fmaxf(fmaxf(sv[p][0], sv[p][1]), fmaxf(sv[p][2], sv[p][3])));
       bm = head_max4(bm);
       const float m_new = fmaxf(m_run, bm);
       const bool live = m_new != -INFINITY;
       const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-      float pv[4];
+      float pv[kPer][4];
+      float bsum[kPer];
+      float ps_all = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pv[i] = live ? __builtin_amdgcn_exp2f(sv[i] - m_new) : 0.f;
-      const float ps = (pv[0] + pv[1]) + (pv[2] + pv[3]);
-      l_run = l_run * alpha + ps;
-      const float bsum = head_sum4(ps);
+      for (int p = 0; p < kPer; ++p) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pv[p][i] = live ? __builtin_amdgcn_exp2f(sv[p][i] - m_new) : 0.f;
+        const float ps = (pv[p][0] + pv[p][1]) + (pv[p][2] + pv[p][3]);
+        ps_all = p == 0 ? ps : ps_all + ps;
+        bsum[p] = head_sum4(ps);
+      }
+      l_run = l_run * alpha + ps_all;
 
       if (__ballot((!hi || paired) && alpha != 1.f) != 0ull) {
 #pragma unroll
@@ -269,28 +312,34 @@ __global__ void __launch_bounds__(64, 2) paged_decode_pair(DecodeArgs a) {
         if (!hi || paired)
           for (int idx = j; idx < b - b0; idx += 4) pi_lds[c * SB + idx] *= alpha;
       }
-      if (j == 0 && (hi ? (mask & 2) : (mask & 1))) pi_lds[c * SB + (b - b0)] = bsum;
+#pragma unroll
+      for (int p = 0; p < kPer; ++p)
+        if (own_active[p] && j == 0) pi_lds[c * SB + (b + p - b0)] = bsum[p];
       m_run = m_new;
 
       // ---- PV: transposed value rows from LDS
-      u4_t R[4];
-      value_rows<F>(vstage, 0, j, c, R);
-      if (vrows < 16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (4 * j + i >= vrows) R[i] = u4_t{0u, 0u, 0u, 0u};
-      }
-      const h4_t pb = h4_t{(_Float16)pv[0], (_Float16)pv[1], (_Float16)pv[2], (_Float16)pv[3]};
+      for (int p = 0; p < kPer; ++p) {
+        u4_t R[4];
+        value_rows<F>(vstage, p, j, c, R);
+        if (vrows[p] < 16) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t lo01 = __builtin_amdgcn_perm(R[1][q], R[0][q], 0x05040100u);
-        const uint32_t lo23 = __builtin_amdgcn_perm(R[3][q], R[2][q], 0x05040100u);
-        const uint32_t hi01 = __builtin_amdgcn_perm(R[1][q], R[0][q], 0x07060302u);
-        const uint32_t hi23 = __builtin_amdgcn_perm(R[3][q], R[2][q], 0x07060302u);
-        acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-            __builtin_bit_cast(h4_t, u2_t{lo01, lo23}), pb, acc[2 * q], 0, 0, 0);
-        acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-            __builtin_bit_cast(h4_t, u2_t{hi01, hi23}), pb, acc[2 * q + 1], 0, 0, 0);
+          for (int i = 0; i < 4; ++i)
+            if (4 * j + i >= vrows[p]) R[i] = u4_t{0u, 0u, 0u, 0u};
+        }
+        const h4_t pb = h4_t{(_Float16)pv[p][0], (_Float16)pv[p][1], (_Float16)pv[p][2],
+                             (_Float16)pv[p][3]};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t lo01 = __builtin_amdgcn_perm(R[1][q], R[0][q], 0x05040100u);
+          const uint32_t lo23 = __builtin_amdgcn_perm(R[3][q], R[2][q], 0x05040100u);
+          const uint32_t hi01 = __builtin_amdgcn_perm(R[1][q], R[0][q], 0x07060302u);
+          const uint32_t hi23 = __builtin_amdgcn_perm(R[3][q], R[2][q], 0x07060302u);
+          acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+              __builtin_bit_cast(h4_t, u2_t{lo01, lo23}), pb, acc[2 * q], 0, 0, 0);
+          acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+              __builtin_bit_cast(h4_t, u2_t{hi01, hi23}), pb, acc[2 * q + 1], 0, 0, 0);
+        }
       }
     }
   }
@@ -324,8 +373,13 @@ __global__ void __launch_bounds__(64, 2) paged_decode_pair(DecodeArgs a) {
 hipError_t launch_decode_pair(const DecodeArgs& a, int batch, hipStream_t stream) {
   const uint64_t wgs = (uint64_t)batch * a.n_splits * a.n_layers * 8u;
   const size_t lds = decode_pair_lds_bytes(a.split_blocks);
-  if (a.kv_format != KVS_KV_FP16 || lds > kMaxDecodeLds) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(paged_decode_pair, dim3((uint32_t)wgs), dim3(64), lds, stream, a);
+  if (lds > kMaxDecodeLds) return hipErrorInvalidValue;
+  if (a.kv_format == KVS_KV_FP16)
+    hipLaunchKernelGGL(paged_decode_pair<KvF16>, dim3((uint32_t)wgs), dim3(64), lds, stream, a);
+  else if (a.kv_format == KVS_KV_E4M3)
+    hipLaunchKernelGGL(paged_decode_pair<KvE4M3>, dim3((uint32_t)wgs), dim3(64), lds, stream, a);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -32,15 +32,17 @@ def pair_plan(table_host, blocks) -> np.ndarray:
     return role
 
 
-def pair_loaded_tokens(table_host, lens, role, split_blocks: int) -> int:
-    """Tokens whose keys and values kvs_decode_step_paired loads per (layer,
-    KV head).  A split is joint when its two sequences are linked both ways,
-    both reach the split's first position and hold the same block there; in a
-    joint split a position where both hold the same block is loaded once, for
-    the larger of the two token counts.  Every other split loads its own
-    sequence's tokens, as the unpaired decode does."""
+def pair_loaded_tokens(table_host, lens, role, split_blocks: int, blocks_per_step: int = 1) -> int:
+    """Tokens whose keys and values the paired decode loads per (layer, KV
+    head).  A split is joint when its two sequences are linked both ways, both
+    reach the split's first position and hold the same block there.  A joint
+    split walks groups of blocks_per_step positions from its first block (1
+    for fp16, 2 for E4M3); a group in which no position holds different blocks
+    in the two sequences is loaded once, each position for the larger of the
+    two token counts, any other group once per sequence.  Every other split
+    loads its own sequence's tokens, as the unpaired decode does."""
     role = np.asarray(role)
-    B, SB = len(lens), int(split_blocks)
+    B, SB, per = len(lens), int(split_blocks), int(blocks_per_step)
     lens = np.asarray(lens, dtype=np.int64)
     nb = (lens + 15) // 16
     tbl = table_host
@@ -56,6 +58,9 @@ def pair_loaded_tokens(table_host, lens, role, split_blocks: int) -> int:
             return other, s
         return None
 
+    def tokens_at(s, b, b1):
+        return int(min(16, lens[s] - 16 * b)) if b < b1 else 0
+
     tokens = 0
     for s in range(B):
         link = link_of(s)
@@ -70,13 +75,12 @@ def pair_loaded_tokens(table_host, lens, role, split_blocks: int) -> int:
                 continue   # loaded by the first sequence's work-groups
             p = link[1]
             b1p = min(int(nb[p]), b0 + SB)
-            for b in range(b0, max(b1, b1p)):
-                va = int(min(16, lens[s] - 16 * b)) if b < b1 else 0
-                vb = int(min(16, lens[p] - 16 * b)) if b < b1p else 0
-                if va and vb and tbl[s, b] == tbl[p, b]:
-                    tokens += max(va, vb)
-                else:
-                    tokens += va + vb
+            for g0 in range(b0, max(b1, b1p), per):
+                group = range(g0, g0 + per)
+                same = all(not (b < b1 and b < b1p and tbl[s, b] != tbl[p, b]) for b in group)
+                for b in group:
+                    va, vb = tokens_at(s, b, b1), tokens_at(p, b, b1p)
+                    tokens += max(va, vb) if same else va + vb
     return tokens
 
 
@@ -104,17 +108,18 @@ class DecodeSession:
                                                     self.layer_end, split_blocks, fmt)
         if self.split_blocks == 0:
             raise ValueError(f"invalid split_blocks {split_blocks}")
-        # paired decode (fp16): pair_role as kvs_decode_step_paired takes it, or
-        # "auto" for pair_plan's shared-prefix pairs; splits of at most 512 blocks
+        # paired decode (fp16, E4M3): pair_role as kvs_decode_step_paired takes
+        # it, or "auto" for pair_plan's shared-prefix pairs; automatic splits of
+        # at most 512 blocks (fp16) or 256 (E4M3)
         self.pair_role = None
         if pair_role is not None:
-            if fmt != "fp16":
-                raise ValueError("paired decode runs over fp16 pools only")
+            if fmt not in ("fp16", "e4m3"):
+                raise ValueError("paired decode runs over fp16 or E4M3 pools only")
             if isinstance(pair_role, str) and pair_role == "auto":
                 pair_role = pair_plan(m.table_host, m.blocks)
             self.pair_role = torch.as_tensor(np.asarray(pair_role, dtype=np.int32), device=dev)
-            if split_blocks == 0:
-                self.split_blocks = min(self.split_blocks, 512)
+            if split_blocks == 0:   # the library's automatic choice for pairs
+                self.split_blocks = min(self.split_blocks, 256 if fmt == "e4m3" else 512)
         self.out = torch.zeros((B, L, 64, 128), dtype=torch.float16, device=dev)
         self.mass = torch.zeros(max(m.total_blocks, 1), dtype=torch.float32, device=dev)
         ws_bytes = api.decode_workspace_bytes(self.shape, B, m.max_blocks, m.total_blocks,
@@ -194,7 +199,7 @@ class DecodeSession:
             return self.kv_bytes_per_step
         m = self.m
         tokens = pair_loaded_tokens(m.table_host, m.lens, self.pair_role.cpu().numpy(),
-                                    self.split_blocks)
+                                    self.split_blocks, 2 if self.kv_format == "e4m3" else 1)
         layers = self.layer_end - self.layer_begin
         return tokens * layers * 8 * 128 * 2 * self.kv_elem_bytes
 
@@ -216,10 +221,10 @@ class DecodeSession:
                                  stream=self.stream)
             return
         if self.pair_role is not None:
-            api.decode_step_paired(self.shape, q, m.pool, m.pool_blocks, m.block_table,
-                                   m.max_blocks, m.seq_lens, self.pair_role, m.meta_offsets,
-                                   m.batch, m.total_blocks, lb, le, sc, self.out, self.mass,
-                                   accumulate, self.split_blocks, self.ws, stream=self.stream)
+            fn = api.decode_step_e4m3_paired if self.kv_format == "e4m3" else api.decode_step_paired
+            fn(self.shape, q, m.pool, m.pool_blocks, m.block_table, m.max_blocks, m.seq_lens,
+               self.pair_role, m.meta_offsets, m.batch, m.total_blocks, lb, le, sc, self.out,
+               self.mass, accumulate, self.split_blocks, self.ws, stream=self.stream)
             return
         fn = api.decode_step_e4m3 if self.kv_format == "e4m3" else api.decode_step
         fn(self.shape, q, m.pool, m.pool_blocks, m.block_table, m.max_blocks, m.seq_lens,

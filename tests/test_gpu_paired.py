@@ -1,6 +1,7 @@
-"""GPU: the paired decode (kvs_decode_step_paired), where one wave serves two
-sequences that share blocks, gives the unpaired decode's bits and the
-oracle's values, whatever the pairing array holds."""
+"""GPU: the paired decode (kvs_decode_step_paired over fp16,
+kvs_decode_step_e4m3_paired over E4M3), where one wave serves two sequences
+that share blocks, gives the unpaired decode's bits and the oracle's values,
+whatever the pairing array holds."""
 import numpy as np
 import pytest
 import torch
@@ -24,18 +25,26 @@ def _bits(t):
     return t.contiguous().view(torch.int16 if t.dtype == torch.float16 else torch.int32)
 
 
-def _shared_workload(seed=9, layers=2):
+FORMATS = ["fp16", "e4m3"]
+
+
+def _fmt(wl, fmt):
+    return W.as_e4m3(wl) if fmt == "e4m3" else wl
+
+
+def _shared_workload(seed=9, layers=2, fmt="fp16"):
     # an 18-block (288-token) shared prefix; 100 and 40 tokens are shorter than
     # it, so their last shared block is partial for them and full for others
     lens = [700, 100, 333, 288, 1000, 40, 517]
-    return W.materialise(W.custom("pair", layers, lens, seed=seed, spare_blocks=6,
-                                  shared_prefix_tokens=288), DEV)
+    return W.materialise(_fmt(W.custom("pair", layers, lens, seed=seed, spare_blocks=6,
+                                       shared_prefix_tokens=288), fmt), DEV)
 
 
-@pytest.mark.parametrize("split_blocks", [4, 8, 0])
-def test_paired_decode_bits_and_oracle(split_blocks):
-    _case(f"paired vs unpaired decode, shared 288-token prefix, split_blocks={split_blocks}")
-    m = _shared_workload()
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("split_blocks", [4, 5, 8, 0])
+def test_paired_decode_bits_and_oracle(split_blocks, fmt):
+    _case(f"{fmt} paired vs unpaired decode, shared 288-token prefix, split_blocks={split_blocks}")
+    m = _shared_workload(fmt=fmt)
     role = pair_plan(m.table_host, m.blocks)
     assert (role >= 0).sum() == 3 and (role <= -2).sum() == 3
     par = DecodeSession(m, split_blocks=split_blocks, pair_role=role)
@@ -71,10 +80,11 @@ def _check_pairing(m, role, split_blocks, step=0):
     assert par.status() == 0 and ref.status() == 0
 
 
+@pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("split_blocks", [4, 16])
-def test_paired_decode_first_sequence_shorter(split_blocks):
-    _case(f"pairs whose first sequence is the shorter one, split_blocks={split_blocks}")
-    m = _shared_workload(seed=4)
+def test_paired_decode_first_sequence_shorter(split_blocks, fmt):
+    _case(f"{fmt} pairs whose first sequence is the shorter one, split_blocks={split_blocks}")
+    m = _shared_workload(seed=4, fmt=fmt)
     # reverse every link of the shared-prefix plan: the second sequence of each
     # pair becomes the first, so joint splits run past the first one's end
     plan = pair_plan(m.table_host, m.blocks)
@@ -85,9 +95,11 @@ def test_paired_decode_first_sequence_shorter(split_blocks):
     _check_pairing(m, role, split_blocks)
 
 
-def test_paired_decode_shared_blocks_between_private_ones():
-    _case("pairs sharing blocks at some positions only (shared, private, shared again)")
-    m = W.materialise(W.custom("mix", 2, [300, 250, 180, 400], seed=21, spare_blocks=4), DEV)
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_paired_decode_shared_blocks_between_private_ones(fmt):
+    _case(f"{fmt} pairs sharing blocks at some positions only (shared, private, shared again)")
+    m = W.materialise(_fmt(W.custom("mix", 2, [300, 250, 180, 400], seed=21, spare_blocks=4),
+                           fmt), DEV)
     # make sequence 1 share sequence 0's blocks at positions 0-3 and 8-11 (4-7
     # stay its own), and sequence 3 share sequence 2's blocks at positions 4-7
     # and 9 (not at 0-3 or 8); the tables on both sides of the boundary change
@@ -100,13 +112,14 @@ def test_paired_decode_shared_blocks_between_private_ones():
         t[3, b] = t[2, b]
     m.block_table.copy_(torch.from_numpy(t).to(DEV))
     role = [1, -2, 3, -4]
-    for sb in (4, 8, 16):
+    for sb in (4, 5, 8, 16):
         _check_pairing(m, role, sb)
 
 
-def test_inconsistent_pair_roles_change_nothing():
-    _case("pair_role arrays with broken, one-sided, self and out-of-range links")
-    m = _shared_workload(seed=3)
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_inconsistent_pair_roles_change_nothing(fmt):
+    _case(f"{fmt} pair_role arrays with broken, one-sided, self and out-of-range links")
+    m = _shared_workload(seed=3, fmt=fmt)
     B = m.batch
     ref = DecodeSession(m, split_blocks=8)
     q = W.make_query(m, 0)
@@ -131,9 +144,11 @@ def test_inconsistent_pair_roles_change_nothing():
         assert par.status() == 0, name
 
 
-def test_pairs_without_shared_blocks():
-    _case("pairs whose sequences share no block: every split decoded separately")
-    m = W.materialise(W.custom("nopair", 2, [300, 517, 64, 1], seed=12, spare_blocks=4), DEV)
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_pairs_without_shared_blocks(fmt):
+    _case(f"{fmt} pairs whose sequences share no block: every split decoded separately")
+    m = W.materialise(_fmt(W.custom("nopair", 2, [300, 517, 64, 1], seed=12, spare_blocks=4),
+                           fmt), DEV)
     ref = DecodeSession(m, split_blocks=4)
     par = DecodeSession(m, split_blocks=4, pair_role=np.asarray([1, -2, 3, -4], dtype=np.int32))
     q = W.make_query(m, 1)
@@ -145,7 +160,7 @@ def test_pairs_without_shared_blocks():
 
 
 def test_paired_decode_rejects_before_launch():
-    _case("paired entry point: NULL pair_role, split above 512, non-fp16 session")
+    _case("paired entry point: NULL pair_role, split above 512, KIVI session")
     m = _shared_workload(seed=5)
     sess = DecodeSession(m, split_blocks=8, pair_role="auto")
     with pytest.raises(api.KvsError):
@@ -159,5 +174,13 @@ def test_paired_decode_rejects_before_launch():
                                m.meta_offsets, m.batch, m.total_blocks, 0, m.num_layers,
                                api.DEFAULT_SCALE, sess.out, sess.mass, 0, 1024, sess.ws)
     with pytest.raises(ValueError):
-        DecodeSession(W.materialise(W.as_e4m3(W.WORKLOADS["decode-1L-1K"]), DEV),
+        DecodeSession(W.materialise(W.as_kivi2(W.WORKLOADS["decode-1L-1K"]), DEV),
                       pair_role="auto")
+    e4 = _shared_workload(seed=5, fmt="e4m3")
+    sess = DecodeSession(e4, split_blocks=8, pair_role="auto")
+    with pytest.raises(api.KvsError):
+        api.decode_step_e4m3_paired(sess.shape, W.make_query(e4, 0), e4.pool, e4.pool_blocks,
+                                    e4.block_table, e4.max_blocks, e4.seq_lens, None,
+                                    e4.meta_offsets, e4.batch, e4.total_blocks, 0,
+                                    e4.num_layers, api.DEFAULT_SCALE, sess.out, sess.mass, 0, 8,
+                                    sess.ws)

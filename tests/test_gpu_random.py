@@ -36,7 +36,7 @@ def _params(k):
     sb = int(rng.choice([0, 4, 6, 8, 12, 32]))
     lb = int(rng.integers(0, L))
     le = int(rng.integers(lb + 1, L + 1))
-    pair = fmt == "fp16" and shared > 0 and bool(rng.random() < 0.75)
+    pair = fmt != "kivi2" and shared > 0 and bool(rng.random() < 0.75)
     seed = int(rng.integers(1, 1 << 30))
     return fmt, L, lens, shared, sb, lb, le, pair, seed
 

@@ -71,3 +71,32 @@ def test_loaded_tokens_split_joint_only_at_equal_first_block():
     table = np.array([[0, 1, 2, 3], [0, 1, 2, 7]], dtype=np.int32)
     assert pair_loaded_tokens(table, [64, 40], role, 4) == 64
     assert pair_loaded_tokens(table, [64, 40], role, 1) == 64
+
+
+@pytest.mark.parametrize("split_blocks", [4, 8, 128, 512])
+def test_loaded_tokens_two_blocks_per_step_closed_form(split_blocks):
+    # a 128-block prefix and even splits: every two-block group is wholly shared
+    # or wholly private, so the saving is the one-block-per-step closed form
+    rng = np.random.default_rng(5)
+    prefix = 2048
+    lens = rng.integers(1, 5000, size=14).tolist() + [prefix, 2047, 2049, 17]
+    _, blocks, table = _tables(lens, prefix)
+    role = pair_plan(table, blocks)
+    saved = sum(min(lens[a], lens[b], prefix) for a in range(len(lens))
+                for b in [int(role[a])] if b >= 0)
+    assert pair_loaded_tokens(table, lens, role, split_blocks, 2) == sum(lens) - saved
+
+
+def test_loaded_tokens_two_blocks_per_step_group_rule():
+    # sequence 1 differs from sequence 0 at position 1 only: one block per step
+    # shares positions 0, 2 and 3; two per step shares only the group (2, 3)
+    table = np.array([[0, 1, 2, 3], [0, 9, 2, 3]], dtype=np.int32)
+    role = np.array([1, -2])
+    assert pair_loaded_tokens(table, [64, 64], role, 4, 1) == 16 + 32 + 16 + 16
+    assert pair_loaded_tokens(table, [64, 64], role, 4, 2) == 64 + 32
+    # an odd split size: groups start at each split's first block.  Splits
+    # [0, 3) and [3, 6), both joint; position 4 differs.  Two per step: groups
+    # (0, 1) and (2) shared, (3, 4) loaded for both, (5) shared.
+    table = np.array([[0, 1, 2, 3, 4, 5], [0, 1, 2, 3, 7, 5]], dtype=np.int32)
+    assert pair_loaded_tokens(table, [96, 96], role, 3, 1) == 16 * 3 + (16 + 32 + 16)
+    assert pair_loaded_tokens(table, [96, 96], role, 3, 2) == 16 * 3 + (64 + 16)
