@@ -15,6 +15,9 @@ Prints one JSON line:
                  --pair-sharers its bytes are those the paired kernel loads
                  (a block two paired sequences share counted once)
   cpu_baseline   the fp64 oracle on a bounded sample of the same workload
+  copy_probe     a 4 GiB device copy (read + write) and the library's
+                 streaming read probe over the same buffer;
+                 frac_of_read_probe = roofline.achieved / that read rate
 """
 from __future__ import annotations
 
@@ -118,28 +121,39 @@ def _traffic(kernel: str, workload: str, split_blocks: int):
 def _copy_probe(gib: float, reps: int):
     """Achievable streaming bandwidth: device-to-device copy of gib-GiB buffers,
     median of reps, counting bytes read plus bytes written (the method the
-    Visual Reference's measurement box describes for its 87 %-of-spec figure)."""
+    Visual Reference's measurement box describes for its 87 %-of-spec figure).
+    Beside it, the library's streaming read probe (kvs_stream_probe, mode 0)
+    over the same buffer: the read-only rate a decode could at best reach."""
     import torch
+
+    from paged_gqa_kv_amd import api
 
     n = int(gib * 2**30) // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-    dst.copy_(src)
-    times = []
-    for _ in range(reps):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        dst.copy_(src)
-        b.record()
-        b.synchronize()
-        times.append(a.elapsed_time(b) / 1e3)
-    times.sort()
-    med = times[len(times) // 2]
-    del src, dst
+    sink = torch.empty(1 << 20, dtype=torch.int32, device="cuda")
+
+    def median_s(fn):
+        fn()
+        times = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            times.append(a.elapsed_time(b) / 1e3)
+        times.sort()
+        return times[len(times) // 2]
+
+    med = median_s(lambda: dst.copy_(src))
+    med_read = median_s(lambda: api.stream_probe(src, sink, n * 4, 0))
+    del src, dst, sink
     torch.cuda.empty_cache()
     return {"bytes_per_copy": 2 * n * 4, "median_s": med, "gbps": 2 * n * 4 / med / 1e9,
-            "reps": reps}
+            "reps": reps, "read_probe_bytes": n * 4, "read_probe_median_s": med_read,
+            "read_probe_gbps": n * 4 / med_read / 1e9}
 
 
 def _cpu_baseline(m, alpha, budget_s):
@@ -433,6 +447,7 @@ def main():
         "host_wall_s": round(wall, 4),
         "copy_probe": probe,
         "frac_of_copy_probe": round(value / probe["gbps"], 4) if probe else None,
+        "frac_of_read_probe": round(achieved / probe["read_probe_gbps"], 4) if probe else None,
         "roofline": {
             "bound": "hbm",
             "kernel": kernel,
