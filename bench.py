@@ -16,7 +16,7 @@ Prints one JSON line:
                  (a block two paired sequences share counted once)
   cpu_baseline   the fp64 oracle on a bounded sample of the same workload
   copy_probe     a 4 GiB device copy (read + write) and the library's
-                 streaming read probe over the same buffer;
+                 streaming read probe over a 16 GiB buffer;
                  frac_of_read_probe = roofline.achieved / that read rate
 """
 from __future__ import annotations
@@ -69,11 +69,16 @@ def _parse():
                     help="fp16 / E4M3: pair sequences that share their first block "
                          "(kvs_decode_step_paired, kvs_decode_step_e4m3_paired), so a shared "
                          "block is loaded once per pair")
+    ap.add_argument("--scrub-mib", type=int, default=0,
+                    help="write a buffer of this many MiB before each timed step, outside the "
+                         "step's timing, so a small workload cannot be served from the caches")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="approximate CPU time budget of the oracle baseline (0 = skip)")
     ap.add_argument("--copy-probe-gib", type=float, default=4.0,
                     help="buffer size of the device copy probe (0 = skip)")
     ap.add_argument("--copy-probe-reps", type=int, default=20)
+    ap.add_argument("--read-probe-gib", type=float, default=16.0,
+                    help="buffer size of the streaming read probe run beside the copy probe")
     return ap.parse_args()
 
 
@@ -118,12 +123,12 @@ def _traffic(kernel: str, workload: str, split_blocks: int):
     return rec.get("hbm_bytes_per_launch")
 
 
-def _copy_probe(gib: float, reps: int):
+def _copy_probe(gib: float, reps: int, read_gib: float):
     """Achievable streaming bandwidth: device-to-device copy of gib-GiB buffers,
     median of reps, counting bytes read plus bytes written (the method the
     Visual Reference's measurement box describes for its 87 %-of-spec figure).
     Beside it, the library's streaming read probe (kvs_stream_probe, mode 0)
-    over the same buffer: the read-only rate a decode could at best reach."""
+    over a read_gib-GiB buffer: the read-only rate a decode could at best reach."""
     import torch
 
     from paged_gqa_kv_amd import api
@@ -148,12 +153,15 @@ def _copy_probe(gib: float, reps: int):
         return times[len(times) // 2]
 
     med = median_s(lambda: dst.copy_(src))
-    med_read = median_s(lambda: api.stream_probe(src, sink, n * 4, 0))
-    del src, dst, sink
+    del src, dst
+    nr = int(read_gib * 2**30) // 16 * 16
+    rsrc = torch.empty(nr, dtype=torch.uint8, device="cuda")   # contents do not matter
+    med_read = median_s(lambda: api.stream_probe(rsrc, sink, nr, 0))
+    del rsrc, sink
     torch.cuda.empty_cache()
     return {"bytes_per_copy": 2 * n * 4, "median_s": med, "gbps": 2 * n * 4 / med / 1e9,
-            "reps": reps, "read_probe_bytes": n * 4, "read_probe_median_s": med_read,
-            "read_probe_gbps": n * 4 / med_read / 1e9}
+            "reps": reps, "read_probe_bytes": nr, "read_probe_median_s": med_read,
+            "read_probe_gbps": nr / med_read / 1e9}
 
 
 def _cpu_baseline(m, alpha, budget_s):
@@ -301,22 +309,34 @@ def main():
     lens_at_start = m.seq_lens.cpu().numpy().copy()
     bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    scrub = None
+    if args.scrub_mib > 0:   # written between steps, outside each step's events
+        scrub = torch.empty(args.scrub_mib << 18, dtype=torch.float32, device="cuda")
     start.record(stream)
     for k in range(args.steps):
-        if k:
+        if scrub is not None:
+            scrub.fill_(float(k))
+        if k or scrub is not None:
             bounds[k].record(stream)
         api.set_decode_events(*pairs[k])
         run_step(k, args.warmup + k, mids[k])
+        ends[k].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     api.set_decode_events(None, None)
-    total_ms = start.elapsed_time(end)
     decode_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
-    step_start = [start] + bounds[1:]
-    step_end = bounds[1:] + [end]
+    step_start = [start] + bounds[1:] if scrub is None else bounds
+    if scrub is None:
+        total_ms = start.elapsed_time(end)
+        step_end = bounds[1:] + [end]
+    else:   # the steps alone: each from its first launch to its last
+        step_end = ends
+        total_ms = sum(a.elapsed_time(b) for a, b in zip(step_start, step_end))
     step_ms = sorted(a.elapsed_time(b) for a, b in zip(step_start, step_end))
     score_ms = sorted(a.elapsed_time(b) for a, b in zip(mids, step_end))
+    del scrub
     for a, b in pairs:
         ev.destroy(a)
         ev.destroy(b)
@@ -395,7 +415,7 @@ def main():
     probe = None
     if args.copy_probe_gib > 0:
         print("[bench] copy probe", file=sys.stderr, flush=True)
-        probe = _copy_probe(args.copy_probe_gib, args.copy_probe_reps)
+        probe = _copy_probe(args.copy_probe_gib, args.copy_probe_reps, args.read_probe_gib)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -429,6 +449,7 @@ def main():
             "kv_bytes_per_step": kv_bytes,
             "unique_kv_bytes_per_step": unique_bytes,
             "pair_sharers": bool(args.pair_sharers),
+            "scrub_mib_between_steps": args.scrub_mib,
             "kv_bytes_loaded_per_step": loaded_bytes,
             "parallelism": "single GPU",
         },

@@ -183,9 +183,10 @@ int kvs_set_decode_events(void* before, void* after);
  * compared with (the pages measure achievable streaming bandwidth with a plain
  * copy of large buffers, median of several runs: Visual Reference Sec. 4 and 9,
  * measurement notes).  Not part of the decode path.
- *  mode 0 (read):  reads `bytes` from src with 16-byte loads, every lane folding
- *                  what it read into one 32-bit word written to dst (dst holds
- *                  grid x 256 words).
+ *  mode 0 (read):  reads `bytes` from src, each wave 8 KiB chunks of 1 KiB
+ *                  non-temporal loads with the grid sweeping the buffer front
+ *                  to back; every lane folds what it read into one 32-bit word
+ *                  written to dst (dst holds grid x 256 words).
  *  mode 1 (copy):  copies `bytes` from src to dst.
  * bytes must be a non-zero multiple of 16; src and dst 16-byte aligned;
  * grid = number of 256-lane work-groups (0 = library choice). */

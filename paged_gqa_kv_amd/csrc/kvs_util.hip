@@ -20,22 +20,28 @@ __global__ void __launch_bounds__(64) clear_words(uint32_t* p, int n) {
 }
 
 // ---------------------------------------------------------------------------
-// stream probe: grid-stride 16-byte loads, 8 in flight per lane.
+// stream probe.  Read: each wave takes 8 KiB chunks (chunk w, w + waves, ...),
+// eight 1 KiB non-temporal loads per chunk, so the whole grid sweeps the
+// buffer front to back the way a decode wave reads a tile.  Copy: grid-stride
+// 16-byte loads and stores.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) stream_read(const u4_t* __restrict__ src, size_t n16,
                                                   uint32_t* __restrict__ sink) {
-  const size_t tid = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const size_t stride = (size_t)gridDim.x * 256;
+  const int lane = threadIdx.x & 63;
+  const size_t waves = (size_t)gridDim.x * 4;
+  const size_t w = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const size_t nchunks = n16 / 512;
   uint32_t acc = 0;
-  size_t i = tid;
-  for (; i + 7 * stride < n16; i += 8 * stride) {
+  for (size_t ch = w; ch < nchunks; ch += waves) {
+    const u4_t* p = src + ch * 512 + lane;
     u4_t v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(p + 64 * u);
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
-  for (; i < n16; i += stride) {
+  const size_t tid = (size_t)blockIdx.x * 256 + threadIdx.x;
+  for (size_t i = nchunks * 512 + tid; i < n16; i += waves * 64) {
     const u4_t v = src[i];
     acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
   }
