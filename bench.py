@@ -70,7 +70,7 @@ def _parse():
                          "(kvs_decode_step_paired, kvs_decode_step_e4m3_paired), so a shared "
                          "block is loaded once per pair")
     ap.add_argument("--scrub-mib", type=int, default=0,
-                    help="write a buffer of this many MiB before each timed step, outside the "
+                    help="read a buffer of this many MiB before each timed step, outside the "
                          "step's timing, so a small workload cannot be served from the caches")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="approximate CPU time budget of the oracle baseline (0 = skip)")
@@ -311,12 +311,12 @@ def main():
     mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     scrub = None
-    if args.scrub_mib > 0:   # written between steps, outside each step's events
-        scrub = torch.empty(args.scrub_mib << 18, dtype=torch.float32, device="cuda")
+    if args.scrub_mib > 0:   # read between steps, outside each step's events
+        scrub = torch.ones(args.scrub_mib << 18, dtype=torch.float32, device="cuda")
     start.record(stream)
     for k in range(args.steps):
-        if scrub is not None:
-            scrub.fill_(float(k))
+        if scrub is not None:   # plain loads: evicts L2 and the Infinity Cache, leaves no dirty lines
+            scrub.sum()
         if k or scrub is not None:
             bounds[k].record(stream)
         api.set_decode_events(*pairs[k])
