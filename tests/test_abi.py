@@ -281,3 +281,29 @@ def test_binding_rejects_non_contiguous_tensors():
         api._p(x.t())
     assert api._p(x).value == x.data_ptr()
 
+
+
+def _decode_paired(e4m3=False, pair_role=0x40000, **over):
+    a = _decode_args(**over)
+    fn = api.decode_step_e4m3_paired if e4m3 else api.decode_step_paired
+    return fn(a["shp"], a["q"], a["kv_pool"], a["pool_blocks"], a["block_table"],
+              a["max_blocks"], a["seq_lens"], pair_role, a["meta_offsets"], a["batch"],
+              a["total_blocks"], a["layer_begin"], a["layer_end"], a["scale"], a["out"],
+              a["block_mass"], a["accumulate"], a["split_blocks"], a["workspace"],
+              a["workspace_bytes"], stream=0)
+
+
+@pytest.mark.parametrize("e4m3", [False, True])
+@pytest.mark.parametrize("over,code", [
+    (dict(pair_role=0), KVS_E_NULL),
+    (dict(q=0), KVS_E_NULL),
+    (dict(pair_role=0x40002), KVS_E_ALIGN),
+    (dict(split_blocks=1024), KVS_E_RANGE),       # a paired split holds at most 512 blocks
+    (dict(batch=0), KVS_E_RANGE),
+    (dict(), KVS_E_WORKSPACE),
+])
+def test_paired_decode_rejects_before_launch(e4m3, over, code):
+    with pytest.raises(KvsError) as e:
+        _decode_paired(e4m3=e4m3, **over)
+    assert e.value.code == code
+    assert api.last_error()
