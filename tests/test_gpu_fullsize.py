@@ -154,6 +154,11 @@ def test_fullsize_shared_prefix_batch_paired():
          seqs_for_layer_mass=[0, 1, 30], pair=True)
 
 
+def test_fullsize_shared_prefix_batch_e4m3_paired():
+    _run("decode-80L-32xMixed-shared2K", 0.15, steps=2, rows=6, oracle_layers=1,
+         seqs_for_layer_mass=[2, 3], kv_format="e4m3", pair=True)
+
+
 def test_fullsize_1m_context():
     _run("decode-32L-1M", 0.01, steps=2, rows=6, oracle_layers=1)
 
