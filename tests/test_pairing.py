@@ -100,3 +100,67 @@ def test_loaded_tokens_two_blocks_per_step_group_rule():
     table = np.array([[0, 1, 2, 3, 4, 5], [0, 1, 2, 3, 7, 5]], dtype=np.int32)
     assert pair_loaded_tokens(table, [96, 96], role, 3, 1) == 16 * 3 + (16 + 32 + 16)
     assert pair_loaded_tokens(table, [96, 96], role, 3, 2) == 16 * 3 + (64 + 16)
+
+
+def _walk_tokens(table, lens, role, SB, per):
+    """The paired kernel's walk, step by step (joint splits decoded by the first
+    sequence of a pair; within one, groups of `per` positions; a joint group is
+    one load per position, any other group one load per sequence), summing
+    each loaded block's tokens for the sequences it is live for."""
+    B = len(lens)
+    nb = [(int(n) + 15) // 16 for n in lens]
+    total = 0
+    for s in range(B):
+        o = int(role[s])
+        other = o if o >= 0 else -2 - o
+        mutual = o != -1 and other != s and 0 <= other < B and (
+            (o >= 0 and int(role[other]) == -2 - s) or (o <= -2 and int(role[other]) == s))
+        for b0 in range(0, nb[s], SB):
+            first, second = (s, other) if o >= 0 else (other, s)
+            joint = (mutual and b0 < nb[first] and b0 < nb[second]
+                     and table[first][b0] == table[second][b0])
+            if joint and s != first:
+                continue
+            b1a = min(nb[s], b0 + SB)
+            if not joint:
+                total += sum(min(16, int(lens[s]) - 16 * b) for b in range(b0, b1a))
+                continue
+            p = second
+            b1b = min(nb[p], b0 + SB)
+            steps = []
+            cur = b0
+            while cur < max(b1a, b1b):
+                grp = range(cur, cur + per)
+                if all(not (q < b1a and q < b1b and table[s][q] != table[p][q]) for q in grp):
+                    steps.append((cur, 3))
+                else:
+                    steps += [(cur, 1), (cur, 2)]
+                cur += per
+            for start, mask in steps:
+                for q in range(start, start + per):
+                    va = min(16, int(lens[s]) - 16 * q) if (mask & 1) and q < b1a else 0
+                    vb = min(16, int(lens[p]) - 16 * q) if (mask & 2) and q < b1b else 0
+                    total += max(va, vb)
+    return total
+
+
+@pytest.mark.parametrize("per", [1, 2])
+@pytest.mark.parametrize("seed", range(6))
+def test_loaded_tokens_match_a_step_by_step_walk(per, seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(2, 9))
+    lens = [int(x) for x in rng.integers(0, 900, size=B)]
+    nbmax = max((n + 15) // 16 for n in lens) + 1
+    base = rng.permutation(10_000)[:nbmax]
+    table = np.empty((B, nbmax), dtype=np.int64)
+    for s in range(B):    # each row copies the base row at random positions
+        own = rng.permutation(10_000)[:nbmax] + 10_000 * (s + 1)
+        table[s] = np.where(rng.random(nbmax) < 0.6, base, own)
+    role = np.full(B, -1)
+    order = rng.permutation(B)
+    for a_, b_ in zip(order[0::2], order[1::2]):
+        if rng.random() < 0.8:
+            role[a_], role[b_] = b_, -2 - a_
+    for SB in (4, 5, 16):
+        assert pair_loaded_tokens(table, lens, role, SB, per) == _walk_tokens(table, lens, role,
+                                                                              SB, per)
