@@ -343,3 +343,39 @@ def test_uniform_attention_and_alpha_one_closed_forms():
         np.testing.assert_allclose(E, counts / counts.max(), rtol=0, atol=1e-6)
         assert np.all(E[counts == counts.max()] == 1.0)
     assert sess.status() == 0
+
+
+def test_large_batch_of_short_sequences():
+    """3,000 sequences of 0..80 tokens in one call: per-sequence grids far past
+    one work-group, decode of a sample against the oracle, scoring of every
+    record against the oracle fed the GPU's mass, and eviction candidates."""
+    _case("batch of 3,000 short sequences, 1 layer, 2 steps")
+    rng = np.random.default_rng(77)
+    lens = [int(x) for x in rng.integers(0, 81, size=3000)]
+    m = W.materialise(W.custom("many", 1, lens, seed=14, spare_blocks=16), DEV)
+    sess = DecodeSession(m)
+    h = P.host(m)
+    pol = OS.Policy(alpha=0.15)
+    gpol = api.policy(0.15)
+    offsets = m.meta_offsets.cpu().numpy()
+    state = OS.init_state(m.blocks, m.seq_ids.cpu().numpy())
+    sample = sorted(set(int(x) for x in rng.choice(3000, size=60, replace=False)) | {0, 2999})
+    sample = [s for s in sample if lens[s] > 0]
+    live_rows = np.concatenate([offsets[s] + np.arange(nb) for s, nb in enumerate(m.blocks)])
+    for step in range(2):
+        q = W.make_query(m, step)
+        sess.step(q, step, gpol)
+        torch.cuda.synchronize()
+        h_sub = dict(h, table=h["table"][sample], lens=[lens[s] for s in sample])
+        out_ref, mass_ref = P.oracle_decode(h_sub, q.cpu().numpy()[sample])
+        P.check_out(sess.out[sample], out_ref, range(1))
+        P.check_mass(sess.mass, mass_ref, offsets[sample])
+        gpu_mass = sess.mass.cpu().numpy().astype(np.float64)
+        masses = [gpu_mass[offsets[s]:offsets[s] + m.blocks[s]] for s in range(m.batch)]
+        state, stale = OS.score_update(state, masses, step, pol)
+        assert not stale.any()
+        P.check_records(sess.records()[live_rows], state, pol)
+    blk, _ = sess.evict_candidates(1, 0.15)
+    ref_blk, _ = OS.eviction_candidates(state, 1, 0.15, nseq=m.batch)
+    assert blk.cpu().tolist() == ref_blk.tolist()
+    assert sess.status() == 0
