@@ -379,3 +379,24 @@ def test_large_batch_of_short_sequences():
     ref_blk, _ = OS.eviction_candidates(state, 1, 0.15, nseq=m.batch)
     assert blk.cpu().tolist() == ref_blk.tolist()
     assert sess.status() == 0
+
+
+@pytest.mark.parametrize("fmt,split_blocks,paired", [("fp16", 1024, False), ("e4m3", 1024, False),
+                                                     ("fp16", 512, True), ("e4m3", 512, True)])
+def test_longest_splits_with_a_one_block_tail(fmt, split_blocks, paired):
+    """The largest split sizes the entry points take, over sequences whose last
+    split holds one block (and a partial one), against the oracle."""
+    _case(f"{fmt}, split {split_blocks}, paired {paired}: 2,049- and 1,025-block sequences")
+    lens = [16 * 2048 + 5, 16 * 1024 + 16, 300, 16 * 1024 + 1]
+    wl = W.custom("long", 1, lens, seed=23, spare_blocks=8, shared_prefix_tokens=4096)
+    if fmt == "e4m3":
+        wl = W.as_e4m3(wl)
+    m = W.materialise(wl, DEV)
+    sess = DecodeSession(m, split_blocks=split_blocks, pair_role="auto" if paired else None)
+    q = W.make_query(m, 3)
+    sess.decode(q)
+    torch.cuda.synchronize()
+    assert sess.status() == 0
+    out_ref, mass_ref = P.oracle_decode(P.host(m), q)
+    P.check_out(sess.out, out_ref, range(1))
+    P.check_mass(sess.mass, mass_ref, m.meta_offsets.cpu().numpy())
