@@ -58,7 +58,7 @@ extern "C" {
 typedef enum {
     KVS_OK = 0,
     KVS_E_NULL = -1,       /* a required pointer is NULL */
-    KVS_E_SHAPE = -2,      /* head shape other than 64 / 8 / 128 / 16, or num_layers < 1 */
+    KVS_E_SHAPE = -2,      /* head shape other than 64 / 8 / 128 / 16, or num_layers outside [1, 65535] */
     KVS_E_RANGE = -3,      /* a count or index argument is out of range */
     KVS_E_ALIGN = -4,      /* a tensor is not 16-byte aligned */
     KVS_E_WORKSPACE = -5,  /* workspace smaller than the matching *_workspace_bytes() */
@@ -77,7 +77,7 @@ typedef enum {
                                         the fp16 free stack): boundary not moved */
 
 /* Model head shape.  The kernels support num_q_heads 64, num_kv_heads 8,
- * head_dim 128, block_tokens 16 and any num_layers >= 1 (Visual Reference
+ * head_dim 128, block_tokens 16 and 1 <= num_layers <= 65535 (Visual Reference
  * Sec. 1, Architecture Parameters). */
 typedef struct {
     int32_t num_layers;

@@ -68,13 +68,17 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Layers are a grid dimension factor and a size factor of the workspace; the
+// cap keeps every size computation far from 64-bit overflow.
+constexpr int32_t kMaxLayers = 65535;
+
 int check_shape(const kvs_shape* s) {
   if (!s) return fail(KVS_E_NULL, "shape is NULL");
-  if (s->num_layers < 1 || s->num_q_heads != 64 || s->num_kv_heads != 8 || s->head_dim != 128 ||
-      s->block_tokens != 16)
+  if (s->num_layers < 1 || s->num_layers > kMaxLayers || s->num_q_heads != 64 ||
+      s->num_kv_heads != 8 || s->head_dim != 128 || s->block_tokens != 16)
     return fail(KVS_E_SHAPE,
                 "unsupported shape {layers=%d, q_heads=%d, kv_heads=%d, head_dim=%d, block=%d}; "
-                "kernels support 64/8/128/16 with layers >= 1",
+                "kernels support 64/8/128/16 with 1 <= layers <= 65535",
                 s->num_layers, s->num_q_heads, s->num_kv_heads, s->head_dim, s->block_tokens);
   return KVS_OK;
 }
@@ -176,15 +180,19 @@ bool decode_layout(const kvs_shape* shape, int32_t kv_format, int32_t batch, int
                    DecodeLayout* L) {
   if (!shape || !format_valid(kv_format) || batch < 1 || batch > kMaxBatch || max_nb < 1 ||
       max_nb > kMaxBlocksPerSeq || total_blocks < 0 || total_blocks > INT32_MAX || lb < 0 ||
-      le <= lb || le > shape->num_layers)
+      le <= lb || le > shape->num_layers || shape->num_layers > kMaxLayers)
     return false;
   const int32_t nl = le - lb;
   const int32_t sb =
       split_blocks == 0 ? choose_split(batch, max_nb, nl, kv_format) : split_blocks;
   if (!split_valid(sb)) return false;
   if (kv_format == KVS_KV_KIVI2 && (sb & 1)) return false;
+  // batch < 2^16, layers < 2^16, splits < 2^24 and total_blocks < 2^31 keep
+  // every term below 2^63: stats < 2^62 and stats * 512 would not be, so the
+  // partial-output term is checked before it is formed.
   const uint64_t nsplit = (uint64_t)(max_nb + sb - 1) / sb;
   const uint64_t stats = (uint64_t)batch * nl * 64u * nsplit;
+  if (stats > (1ull << 50)) return false;
   size_t off = kHeader;
   L->ml = off;
   off = align_up(off + stats * 8u);

@@ -307,3 +307,14 @@ def test_paired_decode_rejects_before_launch(e4m3, over, code):
         _decode_paired(e4m3=e4m3, **over)
     assert e.value.code == code
     assert api.last_error()
+
+
+def test_layer_count_is_bounded_before_any_size_is_formed():
+    # 65,536 layers would take the workspace sizes towards 64-bit overflow
+    big = api.Shape(65536, 64, 8, 128, 16)
+    assert api.decode_workspace_bytes(big, 1, 16, 16, 0, 65536, 0, "fp16") == 0
+    with pytest.raises(KvsError) as e:
+        _decode(shp=big, layer_end=1)
+    assert e.value.code == KVS_E_SHAPE
+    ok = api.Shape(65535, 64, 8, 128, 16)
+    assert api.decode_workspace_bytes(ok, 1, 16, 16, 0, 1, 0, "fp16") > 0
