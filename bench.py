@@ -91,6 +91,7 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self):
         ev = ctypes.c_void_p()
@@ -98,6 +99,11 @@ class HipEvents:
         if rc != 0:
             raise RuntimeError(f"hipEventCreate failed ({rc})")
         return ev.value
+
+    def record(self, ev, stream_handle: int):
+        rc = self.hip.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream_handle))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
 
     def elapsed_ms(self, a, b) -> float:
         ms = ctypes.c_float()
@@ -279,14 +285,11 @@ def main():
     queries = [W.make_query(m, k) for k in range(n_q)]
     new_kv = [W.new_token_kv(m, k) for k in range(n_q)] if args.append else None
 
-    def run_step(k, idx, mid=None):
-        """One step: [append], decode, score.  `mid` (an event) is recorded
-        between decode and scoring so the scoring kernels can be timed alone."""
+    def run_step(k, idx):
+        """One step: [append], decode, score."""
         if new_kv is not None:
             sess.append(*new_kv[idx])
         sess.decode(queries[idx])
-        if mid is not None:
-            mid.record(torch.cuda.current_stream())
         sess.score(k, pol)
     torch.cuda.synchronize()
 
@@ -307,35 +310,41 @@ def main():
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     lens_at_start = m.seq_lens.cpu().numpy().copy()
-    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # Inside the timed region the only markers are the two HIP events around
+    # each decode kernel (the roofline's timing); on the 8 x 8K x 4-layer batch
+    # two more per step cost 5 us of a 180 us step.  Per-step times come from
+    # those events, the scoring kernels are timed apart afterwards.
     scrub = None
+    bounds = ends = None
     if args.scrub_mib > 0:   # read between steps, outside each step's events
         scrub = torch.ones(args.scrub_mib << 18, dtype=torch.float32, device="cuda")
+        bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    end_hip = ev.create()
     start.record(stream)
     for k in range(args.steps):
         if scrub is not None:   # plain loads: evicts L2 and the Infinity Cache, leaves no dirty lines
             scrub.sum()
-        if k or scrub is not None:
             bounds[k].record(stream)
         api.set_decode_events(*pairs[k])
-        run_step(k, args.warmup + k, mids[k])
-        ends[k].record(stream)
+        run_step(k, args.warmup + k)
+        if scrub is not None:
+            ends[k].record(stream)
+    ev.record(end_hip, stream.cuda_stream)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     api.set_decode_events(None, None)
     decode_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
-    step_start = [start] + bounds[1:] if scrub is None else bounds
     if scrub is None:
         total_ms = start.elapsed_time(end)
-        step_end = bounds[1:] + [end]
+        # step k: from its decode kernel's start to the next one's (the last to the end)
+        marks = [a for a, _ in pairs] + [end_hip]
+        step_ms = sorted(ev.elapsed_ms(marks[k], marks[k + 1]) for k in range(args.steps))
     else:   # the steps alone: each from its first launch to its last
-        step_end = ends
-        total_ms = sum(a.elapsed_time(b) for a, b in zip(step_start, step_end))
-    step_ms = sorted(a.elapsed_time(b) for a, b in zip(step_start, step_end))
-    score_ms = sorted(a.elapsed_time(b) for a, b in zip(mids, step_end))
+        step_ms = sorted(a.elapsed_time(b) for a, b in zip(bounds, ends))
+        total_ms = sum(step_ms)
+    ev.destroy(end_hip)
     del scrub
     for a, b in pairs:
         ev.destroy(a)
@@ -377,6 +386,24 @@ def main():
         e1.synchronize()
         ev_ms.append(e0.elapsed_time(e1))
     ev_ms.sort()
+
+    # the scoring kernels alone, timed apart on the same mass; the records the
+    # run produced are put back afterwards
+    saved_meta = sess.meta.clone()
+    score_ms = []
+    for rep in range(3):   # 8 back-to-back updates per sample, as they follow each other in a run
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(8):
+            sess.score(args.steps + 8 * rep + i, pol)
+        e1.record(stream)
+        e1.synchronize()
+        score_ms.append(e0.elapsed_time(e1) / 8)
+    sess.meta.copy_(saved_meta)
+    torch.cuda.synchronize()
+    del saved_meta
+    score_ms.sort()
     if int(blk.min().item()) < 0:
         raise RuntimeError("a sequence got no eviction candidate")
 
