@@ -98,7 +98,6 @@ __global__ void __launch_bounds__(64, F::kWavesPerSimd) paged_decode_gqa(DecodeA
   const size_t block_stride = (size_t)a.num_layers * kLayerBytes;
   const size_t tile_off = (size_t)layer * kLayerBytes + (size_t)g * tile_bytes<F>();
   float m_run = -INFINITY;
-  float l_run = 0.f;
   f4_t acc[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = f4_t{0.f, 0.f, 0.f, 0.f};
@@ -176,21 +175,17 @@ __global__ void __launch_bounds__(64, F::kWavesPerSimd) paged_decode_gqa(DecodeA
       for (int p = 0; p < kPer; ++p)
         bm = fmaxf(bm, fmaxf(fmaxf(sv[p][0], sv[p][1]), fmaxf(sv[p][2], sv[p][3])));
       bm = head_max4(bm);
-      const float m_new = fmaxf(m_run, bm);
+      const float m_new = fmaxf(m_run, bm - kProbShift);   // reference below the maximum
       const bool live = m_new != -INFINITY;
       const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
       float pv[kPer][4];
       float bsum[kPer];
-      float ps_all = 0.f;
 #pragma unroll
       for (int p = 0; p < kPer; ++p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) pv[p][i] = live ? __builtin_amdgcn_exp2f(sv[p][i] - m_new) : 0.f;
-        const float ps = (pv[p][0] + pv[p][1]) + (pv[p][2] + pv[p][3]);
-        ps_all = p == 0 ? ps : ps_all + ps;
-        bsum[p] = head_sum4(ps);
+        bsum[p] = head_sum4((pv[p][0] + pv[p][1]) + (pv[p][2] + pv[p][3]));
       }
-      l_run = l_run * alpha + ps_all;
 
       if (__ballot(c < kGroup && alpha != 1.f) != 0ull) {
 #pragma unroll
@@ -232,10 +227,8 @@ __global__ void __launch_bounds__(64, F::kWavesPerSimd) paged_decode_gqa(DecodeA
   if (saw_bad && lane == 0) flag(a.status, KVS_DEV_BAD_BLOCK_ID);
 
   // ---- split epilogue: statistics, partial output, mass partials
-  const float lt = head_sum4(l_run);
   const size_t st = (((size_t)s * a.n_layers + lr) * kQHeads + kGroup * g + c) * a.n_splits + split;
   if (c < kGroup) {
-    if (j == 0) a.ml[st] = make_float2(m_run, lt);
     float* op = a.opart + st * kHeadDim + 32 * j;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -245,6 +238,8 @@ __global__ void __launch_bounds__(64, F::kWavesPerSimd) paged_decode_gqa(DecodeA
   }
   __syncthreads();
   const int cnt = b1 - b0;
+  const float lt = split_norm<kGroup>(pi_lds, SB, lane, cnt, 0);
+  if (c < kGroup && j == 0) a.ml[st] = make_float2(m_run, lt);
   for (int hh = 0; hh < kGroup; ++hh) {
     float* dst = a.pi + ((size_t)lr * kQHeads + kGroup * g + hh) * a.total_blocks + r0 + b0;
     for (int bb = lane; bb < cnt; bb += 64) dst[bb] = pi_lds[hh * SB + bb];

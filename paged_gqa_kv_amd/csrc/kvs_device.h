@@ -45,6 +45,18 @@ __device__ __forceinline__ uint32_t xcd_item(uint32_t w, uint32_t grid) {
   return w / span * span + (w % kXcds) * kXcdRun + (w / kXcds) % kXcdRun;
 }
 
+// Softmax weights enter the PV products as fp16.  A split takes its weights
+// relative to a reference 2^kProbShift below its running maximum (base 2), so
+// they lie in (0, 2^15] instead of (0, 1]: fp16 then rounds a weight w (as a
+// fraction of the split's maximum) with relative error 2^-11 down to
+// w = 2^-29 and absolute error at most 2^-41 below that, where weights in
+// (0, 1] would lose every w < 2^-25.  Over a 16,384-token split the weight
+// lost to that floor is at most 16,384 x 2^-41 < 2^-27 of the maximum.  The
+// split's sum, partial output and mass partials carry the same factor 2^15,
+// and so does the reference it stores with them, so the split combine
+// (weights 2^(m_k - M) / Lambda) cancels it exactly.
+constexpr float kProbShift = 15.f;
+
 __device__ __forceinline__ float xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 
 // Maximum / sum of v over the 4 lanes l, l ^ 16, l ^ 32, l ^ 48 (the 4 lanes j
@@ -74,6 +86,27 @@ __device__ __forceinline__ float head_sum4(float v) {
   v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
   p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// Softmax normaliser of each row (head) of a split: the sum of the row's
+// block-mass partials in LDS, row r holding its cnt blocks at
+// pi_lds[r * SB + b] (cnt_lo for rows 0..7, cnt_hi for rows 8..15), all taken
+// relative to the split's final reference.  It is summed in fp64 in a fixed
+// order: a running fp32 sum would take a dominant block's weight plus
+// thousands of increments near its rounding unit and drift (a 17-nat peak over
+// 16,384 tokens moved an fp32 sum by 3e-5).  The 64 / kRows lanes of a row
+// share its blocks; every lane returns its row's sum.
+template <int kRows>
+__device__ __forceinline__ float split_norm(const float* pi_lds, int SB, int lane, int cnt_lo,
+                                            int cnt_hi) {
+  constexpr int kParts = 64 / kRows;
+  const int r = lane % kRows;
+  const int cnt = r < 8 ? cnt_lo : cnt_hi;
+  double acc = 0.0;
+  for (int b = lane / kRows; b < cnt; b += kParts) acc += (double)pi_lds[r * SB + b];
+#pragma unroll
+  for (int m = kRows; m < 64; m <<= 1) acc += __shfl_xor(acc, m, 64);
+  return (float)acc;
 }
 
 __device__ __forceinline__ void flag(uint32_t* status, uint32_t bit) {

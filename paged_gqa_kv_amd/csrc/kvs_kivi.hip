@@ -39,6 +39,13 @@ namespace kvs {
 //       scales fold into the fp16 probability operand; the zero-point term is
 //       accumulated per group and added at the end.  Lane (j, c) ends with
 //       channels 16 k + 4 j + i of head c.
+//       The two terms nearly cancel when values sit around zero (each is about
+//       the group minimum times the weight sum, their difference the output),
+//       so both must see the same weights: the folded operand p s enters as its
+//       fp16 product plus the product's fp16 remainder (two MFMAs), not rounded
+//       once.  Rounded once, weights that all round to the same fp16 value (a
+//       nearly flat softmax) bias every product the same way: -1e-4 of the code
+//       term, 1e-2 of an output 100 times smaller than the group minima.
 //  fp16 residual blocks (from quant_lens[s] on) run one by one with the same
 //  operand layouts (value tile transposed through LDS).
 // ---------------------------------------------------------------------------
@@ -47,6 +54,8 @@ namespace kvs {
 // pair's arithmetic; two slots measured 4 % slower (more registers, larger
 // loop body) in this issue-bound kernel.
 constexpr int kKiviRing = 1;
+// Launch bound: 4 waves per SIMD (at most 128 VGPRs).
+constexpr int kKiviWavesPerSimd = 4;
 
 // The 8 codes of one set (code m at bits 4 m, 4 m + 1 of w, other bits 0) as
 // fp16 0..3: E2M1 reads a nibble 0..3 as 0, 0.5, 1, 1.5; the scale 2 makes
@@ -68,7 +77,7 @@ __device__ __forceinline__ float dot2(h2_t x, h2_t y, float acc) {
   return __builtin_amdgcn_fdot2(x, y, acc, false);
 }
 
-__global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(DecodeArgs a) {
+__global__ void __launch_bounds__(64, kKiviWavesPerSimd) paged_decode_kivi(DecodeArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int SB = a.split_blocks;
   int32_t* tbl = reinterpret_cast<int32_t*>(smem);                          // [SB] block ids
@@ -135,12 +144,20 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
     for (int i = 0; i < 4; ++i) qb[i] = *reinterpret_cast<const h8_t*>(qp + 32 * i + 8 * j);
   }
 
+  // Weights relative to a reference 2^kshift below the running maximum (see
+  // kProbShift).  Here they also form the fp16 PV operand p s with the value
+  // scales, so the shift is chosen per split from its first pair's largest
+  // value scale s1: kshift = clamp(7 - floor(log2 s1), 0, 15) keeps
+  // 2^kshift s1 below 2^8.  A product p s 2^kshift then overflows fp16 only
+  // for a scale above about 128 s1 in the same split, and that split is run
+  // again with kshift = 0 (weights <= 1, scales < 2^16: no overflow).  Products
+  // below 2^-25 of the reference round to zero, so the code term of a split
+  // loses at most 3 x tokens x 2^-(25 + kshift) against a largest weight of
+  // 2^kshift: under 2^-32 s1 per token.
+  float kshift = kProbShift;
   float m_run = -INFINITY;
-  float l_run = 0.f;
   f4_t acc[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) acc[k] = f4_t{0.f, 0.f, 0.f, 0.f};
-  float zacc[4] = {0.f, 0.f, 0.f, 0.f};
+  float zacc[4];
   bool saw_bad = false;
 
   // Online softmax of one block's 16 x 16 logits (base 2); returns p relative
@@ -149,14 +166,12 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
     float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     bm = head_max4(bm);
     bm = fmaxf(bm, swap8(bm));   // both halves keep the same running maximum
-    const float m_new = fmaxf(m_run, bm);
+    const float m_new = fmaxf(m_run, bm - kshift);
     const bool live = m_new != -INFINITY;
     const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) pv[i] = live ? __builtin_amdgcn_exp2f(sv[i] - m_new) : 0.f;
-    const float ps = (pv[0] + pv[1]) + (pv[2] + pv[3]);
-    l_run = l_run * alpha + ps;
-    const float bs = head_sum4(ps);
+    const float bs = head_sum4((pv[0] + pv[1]) + (pv[2] + pv[3]));
     if (__ballot(c < kGroup && alpha != 1.f) != 0ull) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc[k] *= alpha;
@@ -177,13 +192,11 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
     float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     bm = head_max4(bm);
     bm = fmaxf(bm, swap8(bm));
-    const float m_new = fmaxf(m_run, bm);
+    const float m_new = fmaxf(m_run, bm - kshift);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
     for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_new);
-    const float ps = (pv[0] + pv[1]) + (pv[2] + pv[3]);
-    l_run = l_run * alpha + ps;
-    const float bs = head_sum4(ps);
+    const float bs = head_sum4((pv[0] + pv[1]) + (pv[2] + pv[3]));
     if (__ballot(alpha != 1.f) != 0ull) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc[k] *= alpha;
@@ -198,6 +211,15 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
 
   // ---- quantised blocks [b0, bq1), in pairs (b0 and nq / 16 are even)
   const int bq1 = min(b1, nq >> 4);
+  // One pass over the split.  Called once, and a second time (inlined again,
+  // not a loop, so the first pass keeps its own register allocation) only
+  // when the first pass overflowed.
+  auto run_split = [&](bool first) __attribute__((always_inline)) {
+  m_run = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) zacc[k] = 0.f;
   if (bq1 > b0) {
     const size_t kblock = (size_t)a.num_layers * 16 * kKiviTileBytes;
     const size_t ktile = ((size_t)(layer * 2) * 8 + g) * kKiviTileBytes;
@@ -232,6 +254,22 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
     bool ring_ok[kKiviRing];
 #pragma unroll
     for (int k = 0; k < kKiviRing; ++k) load_pair(ring[k], b0 + 2 * k, &ring_ok[k]);
+    if (first) {
+      // largest value scale of the split's first pair: bytes 512..639 of its two
+      // value tiles, held by lanes 32..39 (scales are >= 0, so their fp16 bit
+      // patterns order like their values)
+      uint32_t sbits = 0u;
+      if (lane >= 32 && lane < 40)
+#pragma unroll
+        for (int t = 2; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sbits = max(sbits, max(ring[0][t][i] & 0x7FFFu, (ring[0][t][i] >> 16) & 0x7FFFu));
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) sbits = max(sbits, (uint32_t)__shfl_xor((int)sbits, m, 64));
+      const int e5 = (int)(__builtin_amdgcn_readfirstlane(sbits) >> 10);   // fp16 exponent field
+      kshift = (float)min(15, max(0, 22 - e5));
+    }
 
     for (int pb = b0; pb < bq1; pb += 2 * kKiviRing) {
 #pragma unroll
@@ -314,12 +352,18 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
 #pragma unroll
           for (int grp = 0; grp < 4; ++grp) {
             const h4_t s4 = *reinterpret_cast<const h4_t*>(vt + 512 + 2 * (16 * grp + 4 * j));
+            // p s as bp + br: the fp16 product and its remainder (exact in fp16
+            // unless it falls below 2^-24), so that the code term weighs each
+            // token by the same fp16 weight as the zero-point term
             const h4_t bp = pbm * s4;
+            const h4_t br = __builtin_elementwise_fma(pbm, s4, -bp);
             const h8_t vc = codes_to_h8(code_set(vent, grp));
-            acc[2 * grp] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-                h4_t{vc[0], vc[1], vc[2], vc[3]}, bp, acc[2 * grp], 0, 0, 0);
-            acc[2 * grp + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-                h4_t{vc[4], vc[5], vc[6], vc[7]}, bp, acc[2 * grp + 1], 0, 0, 0);
+            const h4_t va = h4_t{vc[0], vc[1], vc[2], vc[3]};
+            const h4_t vb = h4_t{vc[4], vc[5], vc[6], vc[7]};
+            acc[2 * grp] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, bp, acc[2 * grp], 0, 0, 0);
+            acc[2 * grp + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(vb, bp, acc[2 * grp + 1], 0, 0, 0);
+            acc[2 * grp] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, br, acc[2 * grp], 0, 0, 0);
+            acc[2 * grp + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(vb, br, acc[2 * grp + 1], 0, 0, 0);
           }
         }
       }
@@ -368,12 +412,23 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
       }
     }
   }
+  };
+  run_split(true);
+  if (kshift != 0.f) {
+    bool finite = true;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) finite = finite && __builtin_isfinite(acc[k][i]);
+    if (__ballot(!finite) != 0ull) {
+      kshift = 0.f;   // an fp16 product overflowed: run the split again unshifted
+      run_split(false);
+    }
+  }
   if (saw_bad && lane == 0) flag(a.status, KVS_DEV_BAD_BLOCK_ID);
 
   // ---- split epilogue: statistics, partial output (+ value zero-point terms), mass partials
   // The upper half's columns (second blocks of the pairs) join the lower half's.
-  float lt = head_sum4(l_run);
-  lt += swap8(lt);
   float zt[4];
 #pragma unroll
   for (int grp = 0; grp < 4; ++grp) {
@@ -385,7 +440,6 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[k][i] += swap8(acc[k][i]);
   if (c < kGroup) {
-    if (j == 0) a.ml[st] = make_float2(m_run, lt);
     float* op = a.opart + st * kHeadDim + 4 * j;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -396,6 +450,8 @@ __global__ void __launch_bounds__(64, kDecodeWavesPerSimd) paged_decode_kivi(Dec
   }
   __syncthreads();
   const int cnt = b1 - b0;
+  const float lt = split_norm<kGroup>(pi_lds, SB, lane, cnt, 0);
+  if (c < kGroup && j == 0) a.ml[st] = make_float2(m_run, lt);
   for (int hh = 0; hh < kGroup; ++hh) {
     float* dst = a.pi + ((size_t)lr * kQHeads + kGroup * g + hh) * a.total_blocks + r0 + b0;
     for (int bb = lane; bb < cnt; bb += 64) dst[bb] = pi_lds[hh * SB + bb];
