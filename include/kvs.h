@@ -242,6 +242,41 @@ int kvs_decode_step(const kvs_shape* shape,
                     void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* Bytes of the library-owned scratch kvs_decode_step_noalloc uses (32 MiB). */
+#define KVS_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* kvs_decode_step without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  It allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine).  The split statistics, partial outputs and mass partials
+ * live in a file-scope device array of KVS_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends; its address is
+ * looked up once per device on the first call there (make that first call
+ * outside graph capture).  Arguments, results and rules are those of
+ * kvs_decode_step, except:
+ *  status  uint32, device, 4-B aligned, caller-owned: the sticky device-data
+ *          bits kvs_device_status() would report for a workspace are OR-ed in
+ *          here; the caller clears it.
+ * A call whose sizes need more than KVS_NOALLOC_SCRATCH_BYTES (see
+ * kvs_decode_workspace_bytes with KVS_KV_FP16) returns KVS_E_WORKSPACE before
+ * anything is enqueued: split such a step into layer ranges (accumulate = 1).
+ * Every call on one GPU shares that GPU's scratch, which keeps the last call's
+ * contents (each call writes every part it later reads): calls that overlap
+ * on one GPU -- on different streams or from different host threads without
+ * ordering -- race and give wrong results. */
+int kvs_decode_step_noalloc(const kvs_shape* shape,
+                            const void* q,
+                            const void* kv_pool, int64_t pool_blocks,
+                            const int32_t* block_table, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, const int32_t* meta_offsets,
+                            int32_t batch, int64_t total_blocks,
+                            int32_t layer_begin, int32_t layer_end,
+                            float scale,
+                            void* out, float* block_mass, int accumulate,
+                            int32_t split_blocks,
+                            uint32_t* status,
+                            void* stream);
+
 /* The same step over a pool of FP8 E4M3 codes: kv_pool is uint8
  * [pool_blocks][num_layers][2][8][16][128] holding OCP E4M3 codes with no scale
  * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 encodes

@@ -43,8 +43,10 @@ EXPORTS = (
     "kvs_decode_step_e4m3", "kvs_append_workspace_bytes", "kvs_append_kv",
     "kvs_kivi_block_bytes", "kvs_kivi_quantize", "kvs_decode_step_kivi",
     "kvs_kivi_advance_workspace_bytes", "kvs_kivi_advance", "kvs_decode_step_paired",
-    "kvs_decode_step_e4m3_paired",
+    "kvs_decode_step_e4m3_paired", "kvs_decode_step_noalloc",
 )
+
+KVS_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class Shape(ctypes.Structure):
@@ -88,6 +90,9 @@ _SIGS = {
     "kvs_decode_step": (ctypes.c_int, [
         ctypes.POINTER(Shape), _vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _i64, _i32, _i32,
         ctypes.c_float, _vp, _vp, ctypes.c_int, _i32, _vp, _sz, _vp]),
+    "kvs_decode_step_noalloc": (ctypes.c_int, [
+        ctypes.POINTER(Shape), _vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _i64, _i32, _i32,
+        ctypes.c_float, _vp, _vp, ctypes.c_int, _i32, _vp, _vp]),
     "kvs_decode_step_e4m3": (ctypes.c_int, [
         ctypes.POINTER(Shape), _vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _i64, _i32, _i32,
         ctypes.c_float, _vp, _vp, ctypes.c_int, _i32, _vp, _sz, _vp]),

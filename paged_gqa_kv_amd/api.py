@@ -136,6 +136,19 @@ def decode_step(shp: Shape, q, kv_pool, pool_blocks: int, block_table, max_block
                                 ws_bytes, _s(stream)))
 
 
+def decode_step_noalloc(shp: Shape, q, kv_pool, pool_blocks: int, block_table, max_blocks: int,
+                        seq_lens, meta_offsets, batch: int, total_blocks: int, layer_begin: int,
+                        layer_end: int, scale: float, out, block_mass, accumulate: int,
+                        split_blocks: int, status, stream=None) -> None:
+    """kvs_decode_step_noalloc: the decode step with the library's own scratch;
+    `status` is a caller-owned device uint32 word for the sticky status bits."""
+    check(lib().kvs_decode_step_noalloc(ctypes.byref(shp), _p(q), _p(kv_pool), pool_blocks,
+                                        _p(block_table), max_blocks, _p(seq_lens),
+                                        _p(meta_offsets), batch, total_blocks, layer_begin,
+                                        layer_end, scale, _p(out), _p(block_mass), accumulate,
+                                        split_blocks, _p(status), _s(stream)))
+
+
 def decode_step_e4m3(shp: Shape, q, kv_pool, pool_blocks: int, block_table, max_blocks: int,
                      seq_lens, meta_offsets, batch: int, total_blocks: int, layer_begin: int,
                      layer_end: int, scale: float, out, block_mass, accumulate: int,

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvs.so")
 SOURCES = ["kvs_decode.hip", "kvs_decode_paired.hip", "kvs_combine.hip", "kvs_kivi.hip", "kvs_score.hip", "kvs_append.hip", "kvs_util.hip",
-           "kvs_abi.cpp"]
+           "kvs_noalloc.hip", "kvs_abi.cpp"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled for all device code.

@@ -340,11 +340,16 @@ int decode_step(int32_t kv_format, const kvs_shape* shape, const void* q, const 
                 const int32_t* meta_offsets, int32_t batch,
                 int64_t total_blocks, int32_t layer_begin, int32_t layer_end, float scale,
                 void* out, float* block_mass, int accumulate, int32_t split_blocks,
-                void* workspace, size_t workspace_bytes, void* stream) {
+                void* workspace, size_t workspace_bytes, void* stream,
+                uint32_t* status_word = nullptr) {
+  // status_word != NULL: the library's own scratch (kvs_decode_step_noalloc)
+  // stands in for the workspace, and the status bits go to status_word.
+  const bool library_scratch = status_word != nullptr;
+  if (library_scratch) workspace_bytes = KVS_NOALLOC_SCRATCH_BYTES;
   int rc = check_shape(shape);
   if (rc) return rc;
   if (!q || !kv_pool || !block_table || !seq_lens || !meta_offsets || !out || !block_mass ||
-      !workspace)
+      (!workspace && !library_scratch))
     return fail(KVS_E_NULL, "a required pointer is NULL");
   rc = check_counts(batch, max_blocks_per_seq);
   if (rc) return rc;
@@ -373,7 +378,8 @@ int decode_step(int32_t kv_format, const kvs_shape* shape, const void* q, const 
   if (!aligned(block_mass, 4) || !aligned(block_table, 4) || !aligned(seq_lens, 4) ||
       !aligned(meta_offsets, 4))
     return fail(KVS_E_ALIGN, "int32 / fp32 arrays must be 4-byte aligned");
-  if (!aligned(workspace, kAlign)) return fail(KVS_E_ALIGN, "workspace must be 256-byte aligned");
+  if (!library_scratch && !aligned(workspace, kAlign))
+    return fail(KVS_E_ALIGN, "workspace must be 256-byte aligned");
   if (pair_role) {
     if (kv_format != KVS_KV_FP16 && kv_format != KVS_KV_E4M3)
       return fail(KVS_E_RANGE, "paired decode runs over fp16 or E4M3 pools only");
@@ -391,8 +397,15 @@ int decode_step(int32_t kv_format, const kvs_shape* shape, const void* q, const 
   if (!decode_layout(shape, kv_format, batch, max_blocks_per_seq, total_blocks, layer_begin,
                      layer_end, split_blocks, &L))
     return fail(KVS_E_RANGE, "inconsistent sizes");
-  if (workspace_bytes < L.total)
+  if (workspace_bytes < L.total) {
+    if (library_scratch)
+      return fail(KVS_E_WORKSPACE,
+                  "this call needs %zu bytes of scratch, above the %zu bytes "
+                  "kvs_decode_step_noalloc holds: split the layer range into several calls "
+                  "(accumulate = 1)",
+                  L.total, workspace_bytes);
     return fail(KVS_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
+  }
   const int32_t nl = layer_end - layer_begin;
   const uint64_t wgs = (uint64_t)batch * (uint64_t)L.n_splits * (uint64_t)nl * 8u;
   if (wgs * 64u >= (1ull << 32))
@@ -400,9 +413,15 @@ int decode_step(int32_t kv_format, const kvs_shape* shape, const void* q, const 
                 (unsigned long long)wgs);
   if ((uint64_t)batch * nl * 64u >= (1ull << 32))
     return fail(KVS_E_RANGE, "batch x layers too large for one launch");
+  if (library_scratch) {   // every host check passed: the per-device address
+    hipError_t e = hipSuccess;
+    workspace = kvs::noalloc_scratch(&e);
+    if (!workspace) return hip_fail(e, "looking up the library's scratch array");
+  }
 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  uint32_t* status = reinterpret_cast<uint32_t*>(ws);
+  // sticky status bits: the workspace header, or a caller-owned word
+  uint32_t* status = status_word ? status_word : reinterpret_cast<uint32_t*>(ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
 
   kvs::DecodeArgs d{};
@@ -490,6 +509,21 @@ int kvs_decode_step(const kvs_shape* shape, const void* q, const void* kv_pool, 
                      max_blocks_per_seq, seq_lens, nullptr, nullptr, meta_offsets, batch,
                      total_blocks, layer_begin, layer_end, scale, out, block_mass, accumulate,
                      split_blocks, workspace, workspace_bytes, stream);
+}
+
+int kvs_decode_step_noalloc(const kvs_shape* shape, const void* q, const void* kv_pool,
+                            int64_t pool_blocks, const int32_t* block_table,
+                            int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                            const int32_t* meta_offsets, int32_t batch, int64_t total_blocks,
+                            int32_t layer_begin, int32_t layer_end, float scale, void* out,
+                            float* block_mass, int accumulate, int32_t split_blocks,
+                            uint32_t* status, void* stream) {
+  if (!status) return fail(KVS_E_NULL, "status is NULL");
+  if (!aligned(status, 4)) return fail(KVS_E_ALIGN, "status must be 4-byte aligned");
+  return decode_step(KVS_KV_FP16, shape, q, kv_pool, pool_blocks, nullptr, 0, block_table,
+                     max_blocks_per_seq, seq_lens, nullptr, nullptr, meta_offsets, batch,
+                     total_blocks, layer_begin, layer_end, scale, out, block_mass, accumulate,
+                     split_blocks, nullptr, 0, stream, status);
 }
 
 int kvs_decode_step_e4m3(const kvs_shape* shape, const void* q, const void* kv_pool,

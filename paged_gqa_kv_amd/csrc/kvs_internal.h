@@ -29,6 +29,11 @@ constexpr size_t decode_pair_lds_bytes(int32_t split_blocks) {
 }
 constexpr int32_t kMaxPairSplit = 512;   // paired splits: LDS and 4 work-groups per CU
 
+// Device address of the library-owned scratch array used by
+// kvs_decode_step_noalloc, for the current device (looked up once per device);
+// nullptr with *err set when the lookup fails.
+void* noalloc_scratch(hipError_t* err);
+
 struct DecodeArgs {
   const uint16_t* q;        // fp16 bits [B][num_layers][64][128]
   const uint8_t* pool;      // [P][num_layers][2][8][16][128] fp16 values or E4M3 codes

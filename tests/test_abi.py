@@ -318,3 +318,44 @@ def test_layer_count_is_bounded_before_any_size_is_formed():
     assert e.value.code == KVS_E_SHAPE
     ok = api.Shape(65535, 64, 8, 128, 16)
     assert api.decode_workspace_bytes(ok, 1, 16, 16, 0, 1, 0, "fp16") > 0
+
+
+def _decode_noalloc(status=0x8000, **over):
+    a = _decode_args(**over)
+    return api.decode_step_noalloc(a["shp"], a["q"], a["kv_pool"], a["pool_blocks"],
+                                   a["block_table"], a["max_blocks"], a["seq_lens"],
+                                   a["meta_offsets"], a["batch"], a["total_blocks"],
+                                   a["layer_begin"], a["layer_end"], a["scale"], a["out"],
+                                   a["block_mass"], a["accumulate"], a["split_blocks"], status,
+                                   stream=0)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(status=0), KVS_E_NULL),
+    (dict(status=0x8002), KVS_E_ALIGN),
+    (dict(q=0), KVS_E_NULL),
+    (dict(block_mass=0), KVS_E_NULL),
+    (dict(batch=0), KVS_E_RANGE),
+    (dict(layer_end=3), KVS_E_RANGE),
+    (dict(split_blocks=2048), KVS_E_RANGE),
+    (dict(q=0x1008), KVS_E_ALIGN),
+    # 128K tokens x 80 layers in one call needs ~165 MiB of split partials
+    (dict(shp=api.shape(80), layer_end=80, max_blocks=8192, total_blocks=8192, batch=1),
+     KVS_E_WORKSPACE),
+])
+def test_noalloc_decode_rejects_before_launch(over, code):
+    """Every host check of kvs_decode_step_noalloc returns before the library
+    looks up its scratch or launches anything (no GPU here)."""
+    with pytest.raises(KvsError) as e:
+        _decode_noalloc(**over)
+    assert e.value.code == code
+    if code == KVS_E_WORKSPACE:
+        assert "layer range" in e.value.message
+
+
+def test_noalloc_scratch_holds_a_layer_range_of_the_128k_step():
+    """The 32 MiB scratch takes the 128K-token step in ranges of 8 layers."""
+    shp = api.shape(80)
+    assert _abi.KVS_NOALLOC_SCRATCH_BYTES == 32 << 20
+    assert api.decode_workspace_bytes(shp, 1, 8192, 8192, 0, 8, 0, "fp16") <= 32 << 20
+    assert api.decode_workspace_bytes(shp, 1, 8192, 8192, 0, 80, 0, "fp16") > 32 << 20
