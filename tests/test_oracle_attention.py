@@ -217,3 +217,32 @@ def test_empty_sequence_gives_zero_rows_and_no_blocks():
                                  [m.lens[1], m.lens[3]], 0.088)
     assert np.array_equal(out[[1, 3]], out2)
     assert all(np.array_equal(a, b) for a, b in zip([mass[1], mass[3]], mass2))
+
+
+def test_threaded_runner_equals_decode_step_bit_for_bit():
+    """oracle/runner.py only schedules attention.decode_layer / kivi.decode_layer
+    over (sequence, layer) pieces: its outputs and masses are those of
+    decode_step, bit for bit, for any thread count."""
+    from oracle import kivi as KV
+    from oracle import runner as OR
+    rng = np.random.default_rng(11)
+    B, L, nb_max = 3, 3, 12
+    lens = [130, 16 * nb_max, 1]
+    pool = rng.standard_normal((40, L, 2, 8, 16, 128)).astype(np.float16)
+    table = np.stack([rng.permutation(40)[:nb_max] for _ in range(B)]).astype(np.int32)
+    q = rng.standard_normal((B, L, 64, 128)).astype(np.float16)
+
+    def host_layer(s, layer):
+        nb = -(-lens[s] // 16)
+        return pool[table[s, :nb], layer][:, None]
+
+    for fmt, ref_fn in (("fp16", lambda: OA.decode_step(q, pool, table, lens, 0.1)),
+                        ("kivi2", lambda: KV.decode_step(q, pool, table, lens, 0.1))):
+        out_ref, mass_ref = ref_fn()
+        for threads in (1, 3):
+            out, mass, info = OR.decode_layers(q, host_layer, lens, range(L), 0.1, fmt,
+                                               threads=threads, blas_threads=1)
+            assert np.array_equal(out, out_ref)
+            for a, b in zip(mass, mass_ref):
+                assert np.array_equal(a, b)
+            assert info["workers"] == threads
