@@ -14,7 +14,8 @@ Prints one JSON line:
                  the library around its launch on the bench's stream; with
                  --pair-sharers its bytes are those the paired kernel loads
                  (a block two paired sequences share counted once)
-  cpu_baseline   the fp64 oracle on a bounded sample of the same workload
+  cpu_baseline   the fp64 oracle over one whole step of the same workload on
+                 the host's cores (measured, with its thread counts)
   copy_probe     a 4 GiB device copy (read + write) and the library's
                  streaming read probe over a 16 GiB buffer;
                  frac_of_read_probe = roofline.achieved / that read rate
@@ -27,7 +28,6 @@ import hashlib
 import json
 import math
 import os
-import resource
 import sys
 import time
 
@@ -72,8 +72,10 @@ def _parse():
     ap.add_argument("--scrub-mib", type=int, default=0,
                     help="read a buffer of this many MiB before each timed step, outside the "
                          "step's timing, so a small workload cannot be served from the caches")
-    ap.add_argument("--cpu-seconds", type=float, default=20.0,
-                    help="approximate CPU time budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=150.0,
+                    help="cap on the oracle baseline's time: it stops after the layer chunk "
+                         "that passes it (a whole 128K-token step takes well under it; "
+                         "0 = skip)")
     ap.add_argument("--copy-probe-gib", type=float, default=4.0,
                     help="buffer size of the device copy probe (0 = skip)")
     ap.add_argument("--copy-probe-reps", type=int, default=20)
@@ -171,70 +173,90 @@ def _copy_probe(gib: float, reps: int, read_gib: float):
 
 
 def _cpu_baseline(m, alpha, budget_s):
-    """The fp64 oracle (as it stands) on the first layers of step 0 of the same
-    workload, until about budget_s seconds of work; scaled to KV GB/s."""
+    """The fp64 oracle (as it stands) over one whole decode step of the same
+    workload (step 0's query, every layer and sequence), then the scoring of
+    every record.  The oracle runs per (sequence, layer) on the host's cores
+    (oracle/runner.py, up to 16 threads); layers are copied to host memory a
+    chunk at a time before the chunk is timed, so the device-to-host copy is
+    reported apart.  Stops after the chunk that passes budget_s of oracle time
+    (a 128K-token step takes well under it)."""
     import numpy as np
     import torch
 
     import workload as W
-    from oracle import attention as OA
-    from oracle import kivi as KV
+    from oracle import runner as OR
     from oracle import scoring as OS
 
     q = W.make_query(m, 0).cpu().numpy()
     scale = 1.0 / math.sqrt(128.0)
     L = m.num_layers
-    r0 = resource.getrusage(resource.RUSAGE_SELF)
-    t0 = time.perf_counter()
+    fmt = m.workload.kv_format
+    threads = OR.host_threads(16)
+    # one sequence: split each layer's BLAS over 2 threads; many: 1 thread per piece
+    blas = 2 if m.batch == 1 else 1
+    # pieces of 1M tokens hold 17 GB of fp64 keys and values each: fewer at a time
+    if max(m.lens) > 262144:
+        blas = 4
+    chunk = max(1, threads // blas)
     copy_s = 0.0
+    oracle_s = 0.0
     layers_done = 0
-    kv_bytes = 0
     masses = [np.zeros(nb) for nb in m.blocks]
-    for layer in range(L):
+    info = {}
+    for l0 in range(0, L, chunk):
+        layers = range(l0, min(L, l0 + chunk))
         tc = time.perf_counter()
-        pool_l = {}
-        # device -> host copy of this layer's blocks (reported apart from the oracle time)
-        for s in range(m.batch):
-            pids = torch.from_numpy(m.table_host[s, :m.blocks[s]].astype(np.int64)).to(m.pool.device)
-            pool_l[s] = m.pool[pids, layer].cpu().numpy()[:, None]   # [nb][1][2][8][16][128]
+        host = {}
+        for layer in layers:   # device -> host copy of this chunk's blocks
+            for s in range(m.batch):
+                pids = torch.from_numpy(m.table_host[s, :m.blocks[s]].astype(np.int64)).to(
+                    m.pool.device)
+                host[s, layer] = m.pool[pids, layer].cpu().numpy()[:, None]
         copy_s += time.perf_counter() - tc
+        _, ms, info = OR.decode_layers(q, lambda s, layer: host[s, layer], m.lens, layers, scale,
+                                       kv_format=fmt, threads=threads, blas_threads=blas)
+        oracle_s += info["wall_s"]
         for s in range(m.batch):
-            tbl = np.arange(m.blocks[s])
-            fmt = m.workload.kv_format
-            if fmt == "kivi2":
-                _, ms = KV.decode_layer(q[s, layer], pool_l[s], tbl, m.lens[s], 0, scale)
-                nq = KV.quant_boundary(m.lens[s])
-                kv_bytes += 8 * (nq // 16 * 2 * KV.TILE_BYTES + (m.lens[s] - nq) * 128 * 2 * 2)
-            else:
-                _, ms = OA.decode_layer(q[s, layer], pool_l[s], tbl, m.lens[s], 0, scale, fmt)
-                kv_bytes += m.lens[s] * 8 * 128 * 2 * (1 if fmt == "e4m3" else 2)
-            masses[s] += ms
-        layers_done += 1
-        if time.perf_counter() - t0 - copy_s >= budget_s:
+            masses[s] += ms[s]
+        layers_done += len(layers)
+        del host
+        if oracle_s >= budget_s:
             break
+    t = time.perf_counter()
     st = OS.init_state(m.blocks, list(range(m.batch)))
     OS.score_update(st, masses, 0, OS.Policy(alpha=alpha))
-    wall = time.perf_counter() - t0 - copy_s
-    r1 = resource.getrusage(resource.RUSAGE_SELF)
-    cpu = (r1.ru_utime - r0.ru_utime) + (r1.ru_stime - r0.ru_stime)
-    cores = max(1, round(cpu / max(wall + copy_s, 1e-9)))
+    oracle_s += time.perf_counter() - t
+    if fmt == "kivi2":
+        from oracle import kivi as KV
+        per_layer = sum(8 * (KV.quant_boundary(n) // 16 * 2 * KV.TILE_BYTES +
+                             (n - KV.quant_boundary(n)) * 128 * 2 * 2) for n in m.lens)
+    else:
+        per_layer = sum(m.lens) * 8 * 128 * 2 * (1 if fmt == "e4m3" else 2)
+    kv_bytes = per_layer * layers_done
     try:
         from threadpoolctl import threadpool_info
-        blas = ", ".join(f"{d.get('internal_api')} x{d.get('num_threads')}" for d in threadpool_info())
+        blas_lib = ", ".join(sorted({str(d.get("internal_api")) for d in threadpool_info()}))
     except Exception:  # reporting only
-        blas = "unknown"
+        blas_lib = "unknown"
+    whole = layers_done == L
     return {
-        "value": kv_bytes / wall / 1e9,
+        "value": kv_bytes / oracle_s / 1e9,
         "unit": "GB/s",
-        "cores": cores,
-        "threadpools": blas,
+        "cores": info.get("threads", threads),
+        "threads": {"pieces_in_parallel": info.get("workers"), "blas_per_piece":
+                    info.get("blas_threads"), "blas_library": blas_lib},
+        "host_cpus": {"os_cpu_count": os.cpu_count(),
+                      "affinity": len(os.sched_getaffinity(0))},
         "kind": "oracle",
-        "sample": (f"fp64 oracle decode of layers 0..{layers_done - 1} of {L} for all "
-                   f"{m.batch} sequence(s) of step 0, plus scoring of all {m.total_blocks} "
-                   f"records; {wall:.1f} s of oracle time excluding {copy_s:.1f} s of "
-                   f"device-to-host copy; host has {os.cpu_count()} logical CPUs"),
-        "seconds": wall,
-        "step_seconds_extrapolated": wall * L / layers_done,
+        "blocks_scored_per_s": (m.total_blocks / oracle_s) if whole else None,
+        "sample": (f"fp64 oracle decode of {'all' if whole else layers_done} of {L} layers "
+                   f"for all {m.batch} sequence(s) of step 0 (measured, not extrapolated), "
+                   f"plus scoring of all {m.total_blocks} records: {oracle_s:.1f} s of oracle "
+                   f"time on {info.get('threads', threads)} threads, excluding {copy_s:.1f} s "
+                   f"of device-to-host copy"),
+        "seconds": oracle_s,
+        "copy_seconds": copy_s,
+        "whole_step": whole,
     }
 
 
@@ -504,6 +526,11 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
+            "traffic_source": (f"lookup of profiles/{kernel}_{wl.name}_traffic.json: "
+                               "rocprofv3 FETCH_SIZE + WRITE_SIZE per launch, calibrated on a "
+                               "copy kernel, keyed by the kernel's source digest and split"
+                               if traffic is not None else
+                               "no counter summary for the current kernel source and split"),
         },
         "cpu_baseline": cpu,
     }
