@@ -436,11 +436,10 @@ def main():
         kv_bytes = int(mean_tokens * m.num_layers * 8 * 128 * 2 * sess.kv_elem_bytes)
         fp16_bytes = int(mean_tokens * m.num_layers * 8 * 128 * 2 * 2)
         if args.kv_format == "kivi2":   # stored bytes of each timed step's lengths
-            from paged_gqa_kv_amd.session import kivi_quant_len
             per_step = []
             for k in range(args.steps):
                 lens_k = lens_at_start + k + 1
-                nq = np.array([kivi_quant_len(n) for n in lens_k])
+                nq = np.array([api.kivi_quant_len(n) for n in lens_k])
                 per_step.append(int((nq // 16 * 2 * 768 + (lens_k - nq) * 128 * 2 * 2).sum()))
             kv_bytes = int(sum(per_step) / len(per_step)) * m.num_layers * 8
     unique_bytes = m.unique_blocks * 16 * m.num_layers * 8 * 128 * 2 * sess.kv_elem_bytes

@@ -305,8 +305,8 @@ int kvs_decode_step_e4m3(const kvs_shape* shape,
  * z + code * s.  Keys are grouped per channel over 32 consecutive tokens (two
  * 16-token blocks), values per token over 32 consecutive channels.  The newest
  * tokens stay fp16: tokens [0, quant_len) of a sequence are quantised, with
- * quant_len a multiple of 32 (the pages' residual window of ~128 tokens gives
- * quant_len = max(0, floor((n - 128) / 32) * 32); the caller chooses).
+ * quant_len a multiple of 32 given by kvs_kivi_quant_len (the pages' residual
+ * window of ~128 tokens: residual_tokens = 128).
  *
  * Quantised block format, uint8 [kivi_blocks][num_layers][2][8][768]: per
  * layer 8 key tiles then 8 value tiles of 768 bytes, one per KV head.  Bytes
@@ -323,6 +323,14 @@ int kvs_decode_step_e4m3(const kvs_shape* shape,
  *   value tile: token t, channel group g at index 16 g + t.
  * A 32-token pair is two blocks with logical indices 2 p and 2 p + 1; the
  * two may be any physical blocks of the quantised pool. */
+
+/* The window rule: quantised tokens of a seq_len-token sequence whose newest
+ * residual_tokens tokens stay fp16, i.e. the largest multiple of 32 that
+ * leaves at least residual_tokens tokens (0 below residual_tokens + 32):
+ * max(0, floor((seq_len - residual_tokens) / 32) * 32).  kvs_kivi_advance
+ * applies the same rule on the device.  Host only; -1 if an argument is
+ * negative. */
+int32_t kvs_kivi_quant_len(int32_t seq_len, int32_t residual_tokens);
 
 /* Quantise 32-token pairs of fp16 blocks into quantised blocks.
  *  kv_pool     fp16 pool as for kvs_decode_step (read only).
@@ -348,7 +356,7 @@ size_t kvs_kivi_advance_workspace_bytes(int32_t batch);
 /* Move KIVI quantisation boundaries forward after appends: the fp16 residual
  * window is where keys wait until 32 tokens form a whole group (Fitting a
  * Million Tokens, Sec. 02).  For each sequence s, in batch order, with
- * seq_lens[s] - quant_lens[s] >= residual_tokens + 32: the fp16 blocks of
+ * kvs_kivi_quant_len(seq_lens[s], residual_tokens) > quant_lens[s]: the fp16 blocks of
  * logical blocks quant_lens[s] / 16 and + 1 (ids in kv_pool) are quantised
  * into two blocks taken from the top of the KIVI free stack (the first such
  * sequence takes kivi_free[top - 1] for its even block and kivi_free[top - 2]
@@ -359,7 +367,10 @@ size_t kvs_kivi_advance_workspace_bytes(int32_t batch);
  * quant_lens[s] == max(0, floor((seq_lens[s] - residual_tokens) / 32) * 32).
  * With too few KIVI ids, later sequences are left unchanged and
  * KVS_DEV_POOL_EXHAUSTED is raised; bad lengths raise KVS_DEV_BAD_SEQ_LEN, ids
- * outside the pools KVS_DEV_BAD_BLOCK_ID.  Tops and stacks are device int32.
+ * outside the pools KVS_DEV_BAD_BLOCK_ID.  Tops and stacks are device int32;
+ * a top outside [0, capacity] is clamped into it (KVS_DEV_BAD_OFFSETS).  The
+ * fp16 blocks of a sequence's residual window must be its own (not shared with
+ * another sequence's table): they are pushed onto fp16_free once quantised.
  * Calls that overlap on one stream order race. */
 int kvs_kivi_advance(const kvs_shape* shape,
                      const void* kv_pool, int64_t pool_blocks,
@@ -538,7 +549,11 @@ size_t kvs_append_workspace_bytes(int32_t batch);
  *                 clamped into it (KVS_DEV_BAD_OFFSETS).
  *  seq_lens       int32 [batch], device, in / out.
  * A sequence that needs a block when none is left, whose table row or record
- * capacity is full, is left unchanged (KVS_DEV_POOL_EXHAUSTED).
+ * capacity is full, is left unchanged (KVS_DEV_POOL_EXHAUSTED).  The partial
+ * tail block a token is written into must belong to that sequence alone: the
+ * library keeps no reference counts, so a tail block shared with another
+ * table (a shared prefix that ends inside a block) would change under it.
+ * Shared prefixes therefore cover whole blocks.
  * workspace: kvs_append_workspace_bytes() bytes. */
 int kvs_append_kv(const kvs_shape* shape, int kv_elem_bytes,
                   const void* k_new, const void* v_new,

@@ -43,7 +43,7 @@ EXPORTS = (
     "kvs_decode_step_e4m3", "kvs_append_workspace_bytes", "kvs_append_kv",
     "kvs_kivi_block_bytes", "kvs_kivi_quantize", "kvs_decode_step_kivi",
     "kvs_kivi_advance_workspace_bytes", "kvs_kivi_advance", "kvs_decode_step_paired",
-    "kvs_decode_step_e4m3_paired", "kvs_decode_step_noalloc",
+    "kvs_decode_step_e4m3_paired", "kvs_decode_step_noalloc", "kvs_kivi_quant_len",
 )
 
 KVS_NOALLOC_SCRATCH_BYTES = 32 << 20
@@ -106,6 +106,7 @@ _SIGS = {
         ctypes.POINTER(Shape), _vp, _vp, _i64, _vp, _i64, _vp, _i32, _vp, _vp, _vp, _i32, _i64,
         _i32, _i32, ctypes.c_float, _vp, _vp, ctypes.c_int, _i32, _vp, _sz, _vp]),
     "kvs_kivi_block_bytes": (_sz, [ctypes.POINTER(Shape)]),
+    "kvs_kivi_quant_len": (_i32, [_i32, _i32]),
     "kvs_kivi_advance_workspace_bytes": (_sz, [_i32]),
     "kvs_kivi_advance": (ctypes.c_int, [ctypes.POINTER(Shape), _vp, _i64, _vp, _i64, _vp, _i32,
                                         _vp, _vp, _i32, _i32, _vp, _i32, _vp, _vp, _i32, _vp,

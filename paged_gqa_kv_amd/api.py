@@ -86,6 +86,18 @@ def decode_workspace_bytes(shp: Shape, batch: int, max_blocks: int, total_blocks
                                             split_blocks)
 
 
+KIVI_RESIDUAL_TOKENS = 128   # the fp16 window of the newest ~128 tokens
+
+
+def kivi_quant_len(seq_len: int, residual_tokens: int = KIVI_RESIDUAL_TOKENS) -> int:
+    """The library's window rule (kvs_kivi_quant_len): quantised tokens of a
+    seq_len-token sequence."""
+    v = lib().kvs_kivi_quant_len(int(seq_len), int(residual_tokens))
+    if v < 0:
+        raise ValueError(f"invalid seq_len {seq_len} or residual_tokens {residual_tokens}")
+    return v
+
+
 def kivi_block_bytes(shp: Shape) -> int:
     return lib().kvs_kivi_block_bytes(ctypes.byref(shp))
 

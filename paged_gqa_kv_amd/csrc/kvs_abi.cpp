@@ -583,6 +583,11 @@ int kvs_decode_step_kivi(const kvs_shape* shape, const void* q, const void* kv_p
                      accumulate, split_blocks, workspace, workspace_bytes, stream);
 }
 
+int32_t kvs_kivi_quant_len(int32_t seq_len, int32_t residual_tokens) {
+  if (seq_len < 0 || residual_tokens < 0) return -1;
+  return kvs::kivi_quant_len(seq_len, residual_tokens);
+}
+
 size_t kvs_kivi_advance_workspace_bytes(int32_t batch) {
   if (batch < 1) return 0;
   return align_up(kHeader + 16u + (size_t)batch * 20u);

@@ -29,6 +29,19 @@ constexpr size_t decode_pair_lds_bytes(int32_t split_blocks) {
 }
 constexpr int32_t kMaxPairSplit = 512;   // paired splits: LDS and 4 work-groups per CU
 
+// The KIVI window rule (Fitting a Million Tokens, Sec. 02: the newest ~128
+// tokens stay fp16, quantisation works in whole 32-token key groups): tokens
+// [0, quant_len) of an n-token sequence are quantised, quant_len being the
+// largest multiple of 32 that leaves at least `residual` tokens in fp16 (0 when
+// fewer than residual + 32 tokens).  The one implementation of the rule, used
+// by kvs_kivi_quant_len on the host and by the boundary advance on the device.
+__host__ __device__ constexpr int32_t kivi_quant_len(int32_t n, int32_t residual) {
+  return n - residual < 32 ? 0 : (n - residual) / 32 * 32;
+}
+static_assert(kivi_quant_len(159, 128) == 0 && kivi_quant_len(160, 128) == 32 &&
+              kivi_quant_len(191, 128) == 32 && kivi_quant_len(192, 128) == 64 &&
+              kivi_quant_len(0, 128) == 0, "window rule");
+
 // Device address of the library-owned scratch array used by
 // kvs_decode_step_noalloc, for the current device (looked up once per device);
 // nullptr with *err set when the lookup fails.

@@ -595,7 +595,7 @@ __global__ void __launch_bounds__(kAdvanceThreads) kivi_advance_alloc(KiviAdvanc
       const bool valid = n >= 0 && nq >= 0 && (nq & 31) == 0 && nq <= n && n <= 16 * a.max_nb;
       if (!valid) {
         flag(a.status, KVS_DEV_BAD_SEQ_LEN);
-      } else if (n - nq >= a.residual + 32) {
+      } else if (kivi_quant_len(n, a.residual) > nq) {   // the next pair has left the window
         const int b = nq >> 4;
         src_e = a.table[(size_t)s * a.max_nb + b];
         src_o = a.table[(size_t)s * a.max_nb + b + 1];
@@ -646,6 +646,10 @@ __global__ void __launch_bounds__(256) kivi_advance_commit(KiviAdvanceArgs a) {
   const int count = *a.count;
   int ftop = *a.fp16_free_top;
   const int tid = threadIdx.x;
+  if (ftop < 0 || ftop > a.fp16_free_capacity) {   // a top outside the stack: clamped
+    if (tid == 0) flag(a.status, KVS_DEV_BAD_OFFSETS);
+    ftop = ftop < 0 ? 0 : a.fp16_free_capacity;
+  }
   // exclusive count of committed jobs before each job, in job order
   __shared__ int done[256];
   int pushed = 0;

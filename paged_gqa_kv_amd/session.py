@@ -2,8 +2,8 @@
 
 Allocates (with torch) the output, block-mass, record and workspace buffers a
 decode + scoring step needs, and calls the library.  No arithmetic here; for
-a KIVI cache it also decides which tokens are quantised (the residual-window
-rule) and which quantised blocks hold them.
+a KIVI cache it asks the library which tokens are quantised (its window rule,
+kvs_kivi_quant_len) and places the quantised blocks.
 """
 from __future__ import annotations
 
@@ -84,13 +84,6 @@ def pair_loaded_tokens(table_host, lens, role, split_blocks: int, blocks_per_ste
     return tokens
 
 
-def kivi_quant_len(n: int) -> int:
-    """Quantised tokens of an n-token sequence under a KIVI cache: the newest
-    ~128 tokens stay fp16 and the boundary is snapped down to a whole 32-token
-    group (Fitting a Million Tokens, Sec. 02)."""
-    return max(0, (int(n) - 128) // 32 * 32)
-
-
 class DecodeSession:
     def __init__(self, m, layer_begin: int = 0, layer_end=None, split_blocks: int = 0,
                  anchor_blocks: int = 1, stream=None, kivi_spare_blocks=None, pair_role=None):
@@ -144,7 +137,7 @@ class DecodeSession:
         m = self.m
         dev = m.pool.device
         table = m.table_host
-        self.quant_lens_host = np.array([kivi_quant_len(n) for n in m.lens], dtype=np.int32)
+        self.quant_lens_host = np.array([api.kivi_quant_len(n) for n in m.lens], dtype=np.int32)
         pairs, where = [], {}
         kivi_table = table.astype(np.int32).copy()
         for s_ in range(m.batch):
@@ -273,7 +266,8 @@ class DecodeSession:
         if kivi:
             # quantise the pair that left the fp16 window, if any, and free its fp16 blocks
             api.kivi_advance(self.shape, m.pool, m.pool_blocks, self.kivi_pool, self.kivi_blocks,
-                             table, m.max_blocks, m.seq_lens, self.quant_lens, m.batch, 128,
+                             table, m.max_blocks, m.seq_lens, self.quant_lens, m.batch,
+                             api.KIVI_RESIDUAL_TOKENS,
                              self.kivi_free, int(self.kivi_free.numel()), self.kivi_free_top,
                              self.free_stack, int(self.free_stack.numel()), self.free_top,
                              self.advance_ws, stream=self.stream)

@@ -268,10 +268,17 @@ def test_kivi_quantize_validation_and_sizes():
 
 
 def test_kivi_quant_len_rule_matches_the_oracle():
+    """The library's window rule (kvs_kivi_quant_len, also applied on the device
+    by kvs_kivi_advance) against the oracle's boundary, for several windows."""
     from oracle import kivi as KV
-    from paged_gqa_kv_amd.session import kivi_quant_len
-    for n in list(range(0, 400)) + [131072, 1048576]:
-        assert kivi_quant_len(n) == KV.quant_boundary(n)
+    for residual in (0, 1, 31, 32, 100, 128, 200):
+        for n in list(range(0, 420)) + [131072, 1048576, 1048576 + 17]:
+            assert api.kivi_quant_len(n, residual) == KV.quant_boundary(n, residual), (n, residual)
+    assert api.kivi_quant_len(5000) == KV.quant_boundary(5000)     # the default window is 128
+    with pytest.raises(ValueError):
+        api.kivi_quant_len(-1)
+    with pytest.raises(ValueError):
+        api.kivi_quant_len(10, -3)
 
 
 def test_binding_rejects_non_contiguous_tensors():

@@ -10,7 +10,7 @@ import workload as W
 from oracle import kivi as KV
 from oracle import scoring as OS
 from paged_gqa_kv_amd import api
-from paged_gqa_kv_amd.session import DecodeSession, kivi_quant_len
+from paged_gqa_kv_amd.session import DecodeSession
 
 from . import parity as P
 
@@ -30,7 +30,7 @@ def _kivi_session(lens, layers=2, split_blocks=0, seed=21, shared=0):
     m = W.materialise(wl, DEV)
     sess = DecodeSession(m, split_blocks=split_blocks)
     torch.cuda.synchronize()
-    assert [kivi_quant_len(n) for n in m.lens] == [KV.quant_boundary(n) for n in m.lens]
+    assert [api.kivi_quant_len(n) for n in m.lens] == [KV.quant_boundary(n) for n in m.lens]
     return m, sess
 
 
@@ -297,3 +297,36 @@ def test_mixed_precision_by_layer():
     P.check_out(sess.out, out12, [1, 2])
     P.check_mass(sess.mass, [a + b for a, b in zip(mass0, mass12)], m.meta_offsets.cpu().numpy())
     assert sess.status() == 0 and fp16.status() == 0
+
+
+@pytest.mark.parametrize("bad_top", [-7, 1 << 20])
+def test_kivi_advance_clamps_an_out_of_range_fp16_free_top(bad_top):
+    """kivi_advance_commit clamps a top outside [0, capacity] (here -7 and far
+    above the capacity) into the stack before pushing, and reports
+    KVS_DEV_BAD_OFFSETS: the pushes land inside the stack."""
+    _case(f"kvs_kivi_advance with fp16_free_top = {bad_top}")
+    wl = W.as_kivi2(W.custom("kclamp", 1, [159, 100], seed=3, spare_blocks=8))
+    m = W.materialise(wl, DEV, extra_blocks=2)
+    sess = DecodeSession(m, kivi_spare_blocks=4)
+    assert sess.quant_lens.cpu().tolist() == [0, 0]
+    m.seq_lens[0] = 160      # token 159 sits in slot 15 of its block: the window is full
+    cap = 6
+    fp16_free = torch.full((cap,), -1, dtype=torch.int32, device=DEV)
+    fp16_top = torch.tensor([bad_top], dtype=torch.int32, device=DEV)
+    kivi_free = torch.from_numpy(sess.kivi_free_host.astype(np.int32)).to(DEV)
+    kivi_top = torch.tensor([int(sess.kivi_free_host.size)], dtype=torch.int32, device=DEV)
+    ws = torch.empty(api.kivi_advance_workspace_bytes(m.batch), dtype=torch.uint8, device=DEV)
+    api.workspace_init(ws)
+    api.kivi_advance(sess.shape, m.pool, m.pool_blocks, sess.kivi_pool, sess.kivi_blocks,
+                     sess.kivi_table, m.max_blocks, m.seq_lens, sess.quant_lens, m.batch,
+                     api.KIVI_RESIDUAL_TOKENS, kivi_free, int(kivi_free.numel()), kivi_top,
+                     fp16_free, cap, fp16_top, ws)
+    torch.cuda.synchronize()
+    assert api.device_status(ws) & api._abi.KVS_DEV_BAD_OFFSETS
+    assert sess.quant_lens.cpu().tolist() == [32, 0]
+    start = 0 if bad_top < 0 else cap
+    pushed = fp16_free.cpu().tolist()
+    if start + 2 <= cap:
+        assert pushed[:2] == m.table_host[0, :2].tolist() and int(fp16_top.item()) == 2
+    else:   # clamped to a full stack: nothing fits, the ids are not pushed
+        assert pushed == [-1] * cap and int(fp16_top.item()) == cap
