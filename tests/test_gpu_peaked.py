@@ -167,3 +167,25 @@ def test_peaked_longest_split(fmt, sigma, v_offset, gap):
     sess = DecodeSession(m, split_blocks=1024)
     h = P.host(m)
     _check(m, sess, q, lambda: P.oracle_decode(h, q))
+
+
+@pytest.mark.parametrize("late_scale", [10.0, 300.0], ids=lambda x: f"late{x:g}")
+def test_kivi_split_whose_product_overflows_runs_again(late_scale):
+    """The first 32-token pair of each split has values ~ N(0, 0.01^2), so the
+    split takes a large shift for p * s; the rest of the split has values
+    ~ N(0, late_scale^2), whose products with near-maximal weights overflow fp16
+    under that shift.  The split must be decoded again unshifted and still match
+    the oracle (keys ~ N(0, 1e-3^2): nearly flat weights near the maximum)."""
+    _case(f"KIVI decode, first pair of each split at 0.01, later values at {late_scale:g}: "
+          "overflow and second pass")
+    lens = [4160, 2336]
+    m, q = _peaked_workload("kov", lens, 1e-3, 0.0, 0.0, [], fmt="kivi2")
+    for s, n in enumerate(lens):
+        for b in range(m.blocks[s]):
+            pid = int(m.table_host[s, b])
+            f = 0.01 if b % 128 < 2 else late_scale      # blocks 0-1 of each 128-block split
+            m.pool[pid, :, 1] = (m.pool[pid, :, 1].float() * (f / 1e-3)).to(torch.float16)
+    torch.cuda.synchronize()
+    sess = DecodeSession(m, split_blocks=128)
+    pool = m.pool.cpu().numpy()
+    _check(m, sess, q, lambda: KV.decode_step(q.cpu().numpy(), pool, m.table_host, m.lens, SCALE))
