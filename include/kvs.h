@@ -284,7 +284,11 @@ int kvs_decode_step_noalloc(const kvs_shape* shape,
  * Million Tokens, Sec. 02: FP8 E4M3 KV, no calibration).  Every code is
  * dequantised exactly to fp16 inside the kernel; q, out, the block mass and all
  * other arguments, sizes and rules are those of kvs_decode_step (the workspace
- * of kvs_decode_workspace_bytes serves both). */
+ * of kvs_decode_workspace_bytes serves both).  One wave serves KV heads 2 i
+ * and 2 i + 1 together; each query head's arithmetic is that of a decode with
+ * one head per wave, except that a NaN code among the values a sequence reads
+ * from one of the two heads also makes the other head's output rows NaN (its
+ * product with that head's zero weights). */
 int kvs_decode_step_e4m3(const kvs_shape* shape,
                          const void* q,
                          const void* kv_pool, int64_t pool_blocks,
@@ -504,11 +508,9 @@ int kvs_decode_step_paired(const kvs_shape* shape,
 
 /* kvs_decode_step_paired over an FP8 E4M3 pool: the decode of
  * kvs_decode_step_e4m3 with pairs of sequences that share blocks decoded by one
- * wave.  That decode takes blocks two at a time from the split's first block;
- * a pair shares a step when no position of its two blocks holds different
- * physical blocks in the two sequences (a position only one of them reaches is
- * loaded for that one), and decodes the two positions separately otherwise.
- * The results are bit-identical to kvs_decode_step_e4m3 whatever the pairing.
+ * wave, one block per step as in kvs_decode_step_paired.  The results are
+ * bit-identical to kvs_decode_step_e4m3 whatever the pairing (for finite
+ * codes: see the NaN note there).
  * pair_role, split_blocks (at most 512; 0 chooses as kvs_decode_split_blocks
  * does for KVS_KV_E4M3, capped at 256) and every other argument as in
  * kvs_decode_step_paired; the workspace must fit

@@ -116,8 +116,8 @@ int check_counts(int32_t batch, int32_t max_blocks) {
 // The largest power-of-two split in [16, the format's cap] whose launch keeps
 // enough bytes in flight on the whole chip (wave count) and per compute unit
 // (waves that fit the LDS a split needs, at most the kernel's waves per SIMD).
-// Reads one decode wave keeps in flight: two fp16 blocks or two two-block E4M3
-// steps (K and V tiles of its KV head).  For KIVI the figure is a sizing
+// Reads one decode wave keeps in flight: two fp16 blocks (K and V tiles of its
+// KV head) or two E4M3 blocks of its two KV heads.  For KIVI the figure is a sizing
 // constant of two 32-token pairs (4 tiles of 768 bytes each): the kernel has
 // one pair's loads in flight while it works on the previous pair from LDS.
 uint64_t wave_inflight_bytes(int32_t kv_format) {
@@ -128,16 +128,21 @@ uint64_t wave_inflight_bytes(int32_t kv_format) {
   }
 }
 
+// KV heads one decode wave serves.
+uint32_t heads_per_wave(int32_t kv_format) {
+  return kv_format == KVS_KV_E4M3 ? (uint32_t)kvs::kE4M3HeadsPerWave : 1u;
+}
+
 uint64_t waves_per_simd(int32_t kv_format) {
   return kv_format == KVS_KV_E4M3 ? kvs::kDecodeWavesPerSimdE4M3 : kvs::kDecodeWavesPerSimd;
 }
 
-// Waves the grid must provide per SIMD (1,024 SIMDs on gfx950).  The E4M3
-// decode needs two: with one wave per SIMD its conversions and softmax are not
-// hidden behind the loads (8 sequences x 8K x 4 layers: 4.5 TB/s at split 128,
-// 1,024 waves, against 5.0 TB/s at split 64, 2,048 waves).
+// Waves the grid must provide (1,024 SIMDs on gfx950).  The E4M3 decode needs
+// one per SIMD: each wave's conversions and softmax must have loads of other
+// waves to hide behind (8 sequences x 8K x 4 layers: 6.1 TB/s at split 64 with
+// 1,024 waves, 5.8 TB/s at split 32 with 2,048, 5.4 TB/s at split 16).
 uint64_t min_grid_waves(int32_t kv_format) {
-  return kv_format == KVS_KV_E4M3 ? 2u * kChipSimds : 0u;
+  return kv_format == KVS_KV_E4M3 ? kChipSimds : 0u;
 }
 
 int32_t max_auto_split(int32_t kv_format) {
@@ -151,12 +156,13 @@ int32_t max_auto_split(int32_t kv_format) {
 bool format_valid(int32_t f) { return f == KVS_KV_FP16 || f == KVS_KV_E4M3 || f == KVS_KV_KIVI2; }
 
 int32_t choose_split(int32_t batch, int32_t max_nb, int32_t n_layers, int32_t kv_format) {
-  const uint64_t streams = (uint64_t)batch * (uint64_t)n_layers * 8u;
+  const uint32_t heads = heads_per_wave(kv_format);
+  const uint64_t streams = (uint64_t)batch * (uint64_t)n_layers * (8u / heads);
   const uint64_t wave_inflight = wave_inflight_bytes(kv_format);
   const uint64_t cu_waves = 4u * waves_per_simd(kv_format);
   for (int32_t cand = max_auto_split(kv_format); cand >= 16; cand >>= 1) {
     const uint64_t waves = streams * (uint64_t)((max_nb + cand - 1) / cand);
-    uint64_t per_cu = kvs::kLdsPerCu / kvs::decode_lds_bytes(cand);
+    uint64_t per_cu = kvs::kLdsPerCu / kvs::decode_lds_bytes(cand, (int)heads);
     if (per_cu > cu_waves) per_cu = cu_waves;
     if (waves * wave_inflight >= kChipInflightBytes && per_cu * wave_inflight >= kCuInflightBytes &&
         waves >= min_grid_waves(kv_format))
@@ -165,8 +171,8 @@ int32_t choose_split(int32_t batch, int32_t max_nb, int32_t n_layers, int32_t kv
   return 16;
 }
 
-// Upper bound keeps the decode work-group's LDS (36 B per block + 4 KiB) far
-// below the 64 KiB a work-group may request.
+// Upper bound keeps the decode work-group's LDS (36 B per block + 4 KiB, 68 B
+// per block for the E4M3 decode's two KV heads) within the 96 KiB it may request.
 bool split_valid(int32_t sb) { return sb >= 4 && sb <= 1024; }
 
 struct DecodeLayout {

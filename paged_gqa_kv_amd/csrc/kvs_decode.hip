@@ -24,47 +24,62 @@ namespace kvs {
 // ---------------------------------------------------------------------------
 // paged_decode_gqa
 //
-// One 64-lane wave owns (s, layer, g, split).  Lane l = 16 j + c.
-//  QK:  S^T[token][head] = K[token][:] . q[head][:] on v_mfma_f32_16x16x32_f16,
-//       A = the 16x128 key tile (lane reads 64 contiguous bytes of row c), B =
-//       the 8 queries of the group padded to 16 columns.  The result gives
-//       lane (j, c) the logits of head c for tokens 4j..4j+3.
-//  PV:  O^T[d][head] += V^T[d][token] P^T[token][head] on
+// One 64-lane wave owns (s, layer, split) and F::kHeads adjacent KV heads from
+// g: one for fp16, two for E4M3.  Lane l = 16 j + c.
+//  QK:  S^T[token][col] = K[token][:] . q[col][:] on v_mfma_f32_16x16x32_f16,
+//       A = a 16x128 key tile (lane reads 64 contiguous bytes of row c), B =
+//       the queries: column c holds query head 8 g + c for c < 8 F::kHeads, the
+//       rest are zero.  With two KV heads, column c belongs to head g + c / 8
+//       and takes its logits from that head's MFMA chain.  Lane (j, c) gets
+//       the logits of column c for tokens 4j..4j+3.
+//  PV:  O^T[d][col] += V^T[d][token] P^T[token][col] on
 //       v_mfma_f32_16x16x16_f16.  P^T is exactly the QK result layout (after
 //       rounding to fp16).  V^T needs the value tile transposed: it is staged
 //       through 4 KiB of LDS, each lane reads 4 rows x 16 bytes, and byte
 //       permutes build the operand of each of the 8 output tiles.  Output tile
 //       k holds d = 8 m + k, so lane (j, c) ends with the 32 contiguous values
-//       d in [32 j, 32 j + 32) of head c.
+//       d in [32 j, 32 j + 32) of column c.  With two KV heads each head's
+//       value tile is multiplied by P^T with the other head's columns zeroed,
+//       so every column accumulates only its own head's values.
 //  Online softmax in base 2: logits are scaled by scale * log2(e); a running
-//  maximum per head; the per-block mass of head c is kept in LDS relative to
-//  the current maximum and rescaled whenever that maximum grows.
+//  maximum per column; the per-block mass of each column is kept in LDS
+//  relative to the current maximum and rescaled whenever that maximum grows.
+//  Per column the arithmetic does not depend on F::kHeads (the other head's
+//  PV product adds exact zeros), as long as the stored values are finite.
 // ---------------------------------------------------------------------------
 // Blocks whose loads are in flight per wave: the ring slot being processed
 // plus kRing - 1 ahead (32 VGPRs per slot).  Deeper rings at lower occupancy
-// measured no faster on gfx950.  One wave per work-group, one KV head each:
-// work-groups of 4 or 8 waves reading neighbouring heads measured no faster.
+// measured no faster on gfx950.  One wave per work-group: work-groups of 4 or
+// 8 waves reading neighbouring heads measured no faster for fp16.
 template <class F>
 __global__ void __launch_bounds__(64, F::kWavesPerSimd) paged_decode_gqa(DecodeArgs a) {
+  static_assert(F::kPer == 1, "one block per step");
+  constexpr int kHeads = F::kHeads;
+  constexpr int kCols = kGroup * kHeads;              // MFMA columns holding query heads
+  constexpr uint32_t kWaveGroups = 8u / kHeads;       // waves per (layer, split)
+  constexpr int kGroupShift = kHeads == 1 ? 3 : 2;    // log2(kWaveGroups)
+  static_assert((1u << kGroupShift) == kWaveGroups, "power-of-two head groups");
   extern __shared__ __align__(16) uint8_t smem[];
   const int SB = a.split_blocks;
   // LDS layout (decode_lds_bytes): block ids, mass partials, value stage.
+  const int SP = decode_pi_stride(SB, kHeads);        // row stride of the mass partials
+  const int ids = kHeads == 1 ? SB : (SB + 3) & ~3;
   int32_t* tbl = reinterpret_cast<int32_t*>(smem);                          // [SB] block ids
-  float* pi_lds = reinterpret_cast<float*>(smem + (size_t)4 * SB);          // [8][SB]
-  u4_t* vstage = reinterpret_cast<u4_t*>(smem + (size_t)36 * SB);           // 16 x 16 chunks of 16 B
+  float* pi_lds = reinterpret_cast<float*>(smem + (size_t)4 * ids);         // [kCols][SP]
+  u4_t* vstage = reinterpret_cast<u4_t*>(smem + (size_t)4 * ids + (size_t)4 * kCols * SP);
 
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;
   const int j = lane >> 4;
 
   uint32_t w = xcd_item(blockIdx.x, gridDim.x);
-  const uint32_t lgg_count = (uint32_t)a.n_layers * 8u;
+  const uint32_t lgg_count = (uint32_t)a.n_layers * kWaveGroups;
   const int lgg = (int)(w % lgg_count);
   w /= lgg_count;
   const int split = (int)(w % (uint32_t)a.n_splits);
   const int s = (int)(w / (uint32_t)a.n_splits);
-  const int lr = lgg >> 3;
-  const int g = lgg & 7;
+  const int lr = lgg >> kGroupShift;
+  const int g = (lgg & (int)(kWaveGroups - 1)) * kHeads;   // first KV head of the wave
   const int layer = a.layer_begin + lr;
 
   int r0 = 0;
@@ -82,9 +97,9 @@ __global__ void __launch_bounds__(64, F::kWavesPerSimd) paged_decode_gqa(DecodeA
     tbl[i] = a.table[(size_t)s * a.max_nb + b0 + i];
   __syncthreads();
 
-  // B operand of QK: queries of the group, rows 8..15 zero.
+  // B operand of QK: query heads 8 g .. 8 g + kCols - 1, other columns zero.
   h8_t qb[4];
-  if (c < kGroup) {
+  if (c < kCols) {
     const uint16_t* qp =
         a.q + ((((size_t)s * a.num_layers + layer) * kQHeads + kGroup * g + c) * kHeadDim);
 #pragma unroll
@@ -114,102 +129,100 @@ __global__ void __launch_bounds__(64, F::kWavesPerSimd) paged_decode_gqa(DecodeA
   };
 
   constexpr int kRing = F::kRing;
-  constexpr int kPer = F::kPer;
   StepRegs<F> ring[kRing];
-  bool ring_ok[kRing][kPer];
-  auto load_step = [&](StepRegs<F>& r, bool (&ok)[kPer], int bfirst) {
+  bool ring_ok[kRing];
+  // the wave's heads' tiles of block bidx (adjacent: the key tiles form one
+  // run, the value tiles another)
+  auto load_step = [&](StepRegs<F>& r, bool& ok, int bidx) {
+    const uint8_t* base = slot_block(bidx, &ok);
 #pragma unroll
-    for (int p = 0; p < kPer; ++p)
-      load_block(r.blk[p], slot_block(bfirst + p, &ok[p]), lane, c, j);
+    for (int h = 0; h < kHeads; ++h)
+      load_block(r.blk[h], base + (size_t)h * tile_bytes<F>(), lane, c, j);
   };
 #pragma unroll
-  for (int k = 0; k < kRing; ++k) load_step(ring[k], ring_ok[k], b0 + k * kPer);
+  for (int k = 0; k < kRing; ++k) load_step(ring[k], ring_ok[k], b0 + k);
 
   bool saw_bad = false;
-  for (int bbase = b0; bbase < b1; bbase += kRing * kPer) {
+  for (int bbase = b0; bbase < b1; bbase += kRing) {
 #pragma unroll
     for (int k = 0; k < kRing; ++k) {
-      const int bs = bbase + k * kPer;        // first block of this step
-      bool active[kPer];
-      int valid[kPer];
-#pragma unroll
-      for (int p = 0; p < kPer; ++p) {
-        active[p] = bs + p < b1;
-        saw_bad |= active[p] && !ring_ok[k][p];
-        valid[p] = ring_ok[k][p] ? min(16, n - 16 * (bs + p)) : 0;
-      }
+      const int bs = bbase + k;        // this step's block
+      const bool active = bs < b1;
+      saw_bad |= active && !ring_ok[k];
+      const int valid = ring_ok[k] ? min(16, n - 16 * bs) : 0;
 
       // ---- value tiles to LDS (the slot's value registers are free after this)
 #pragma unroll
-      for (int p = 0; p < kPer; ++p) stage_values<F>(ring[k].blk[p], vstage, lane, p);
+      for (int h = 0; h < kHeads; ++h) stage_values<F>(ring[k].blk[h], vstage, lane, h);
 
-      // ---- logits of 16 tokens x 16 (8 real) heads per block
-      f4_t sacc[kPer];
+      // ---- logits of 16 tokens x 16 columns per head
+      f4_t sacc[kHeads];
 #pragma unroll
-      for (int p = 0; p < kPer; ++p) sacc[p] = f4_t{0.f, 0.f, 0.f, 0.f};
+      for (int h = 0; h < kHeads; ++h) sacc[h] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int p = 0; p < kPer; ++p)
-          sacc[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_operand<F>(ring[k].blk[p], i),
-                                                           qb[i], sacc[p], 0, 0, 0);
+        for (int h = 0; h < kHeads; ++h)
+          sacc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_operand<F>(ring[k].blk[h], i),
+                                                           qb[i], sacc[h], 0, 0, 0);
 
       // ---- refill this slot with the step kRing ahead
-      load_step(ring[k], ring_ok[k], bs + kRing * kPer);
+      load_step(ring[k], ring_ok[k], bs + kRing);
 
-      float sv[kPer][4];
+      // the lane's column belongs to head g + c / 8
+      float sv[4];
 #pragma unroll
-      for (int p = 0; p < kPer; ++p) {
+      for (int i = 0; i < 4; ++i) {
+        float x = sacc[0][i];
+        if constexpr (kHeads == 2) x = c < kGroup ? sacc[0][i] : sacc[1][i];
+        sv[i] = x * a.scale_log2;
+      }
+      if (valid < 16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sv[p][i] = sacc[p][i] * a.scale_log2;
-        if (valid[p] < 16) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (4 * j + i >= valid[p]) sv[p][i] = -INFINITY;
-        }
+        for (int i = 0; i < 4; ++i)
+          if (4 * j + i >= valid) sv[i] = -INFINITY;
       }
 
-      // ---- online softmax over the step (per head = per c; the 4 lanes j share a head)
+      // ---- online softmax over the block (per column; the 4 lanes j share one)
       float bm = -INFINITY;
-#pragma unroll
-      for (int p = 0; p < kPer; ++p)
-        bm = fmaxf(bm, fmaxf(fmaxf(sv[p][0], sv[p][1]), fmaxf(sv[p][2], sv[p][3])));
+      bm = fmaxf(bm, fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
       bm = head_max4(bm);
       const float m_new = fmaxf(m_run, bm - kProbShift);   // reference below the maximum
       const bool live = m_new != -INFINITY;
       const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-      float pv[kPer][4];
-      float bsum[kPer];
+      float pv[4];
 #pragma unroll
-      for (int p = 0; p < kPer; ++p) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pv[p][i] = live ? __builtin_amdgcn_exp2f(sv[p][i] - m_new) : 0.f;
-        bsum[p] = head_sum4((pv[p][0] + pv[p][1]) + (pv[p][2] + pv[p][3]));
-      }
+      for (int i = 0; i < 4; ++i) pv[i] = live ? __builtin_amdgcn_exp2f(sv[i] - m_new) : 0.f;
+      const float bsum = head_sum4((pv[0] + pv[1]) + (pv[2] + pv[3]));
 
-      if (__ballot(c < kGroup && alpha != 1.f) != 0ull) {
+      if (__ballot(c < kCols && alpha != 1.f) != 0ull) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[q] *= alpha;
-        if (c < kGroup)
-          for (int idx = j; idx < bs - b0; idx += 4) pi_lds[c * SB + idx] *= alpha;
+        if (c < kCols) {
+          if constexpr (kHeads == 2) {   // four partials per LDS access (rows 16-byte aligned)
+            f4_t* row = reinterpret_cast<f4_t*>(pi_lds + c * SP);
+            for (int v = j; 4 * v < bs - b0; v += 4) row[v] *= alpha;
+          } else {
+            for (int idx = j; idx < bs - b0; idx += 4) pi_lds[c * SP + idx] *= alpha;
+          }
+        }
       }
-#pragma unroll
-      for (int p = 0; p < kPer; ++p)
-        if (active[p] && c < kGroup && j == 0) pi_lds[c * SB + (bs + p - b0)] = bsum[p];
+      if (active && c < kCols && j == 0) pi_lds[c * SP + (bs - b0)] = bsum;
       m_run = m_new;
 
-      // ---- PV: transposed value rows from LDS
+      // ---- PV: transposed value rows from LDS, one head at a time
+      const h4_t pb = h4_t{(_Float16)pv[0], (_Float16)pv[1], (_Float16)pv[2], (_Float16)pv[3]};
 #pragma unroll
-      for (int p = 0; p < kPer; ++p) {
+      for (int h = 0; h < kHeads; ++h) {
         u4_t R[4];
-        value_rows<F>(vstage, p, j, c, R);
-        if (valid[p] < 16) {
+        value_rows<F>(vstage, h, j, c, R);
+        if (valid < 16) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (4 * j + i >= valid[p]) R[i] = u4_t{0u, 0u, 0u, 0u};
+            if (4 * j + i >= valid) R[i] = u4_t{0u, 0u, 0u, 0u};
         }
-        const h4_t pb = h4_t{(_Float16)pv[p][0], (_Float16)pv[p][1], (_Float16)pv[p][2],
-                             (_Float16)pv[p][3]};
+        // columns of the other head take no part in this head's product
+        const h4_t ph = (kHeads == 1 || (c >> 3) == h) ? pb : h4_t{0, 0, 0, 0};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t lo01 = __builtin_amdgcn_perm(R[1][q], R[0][q], 0x05040100u);
@@ -217,9 +230,9 @@ __global__ void __launch_bounds__(64, F::kWavesPerSimd) paged_decode_gqa(DecodeA
           const uint32_t hi01 = __builtin_amdgcn_perm(R[1][q], R[0][q], 0x07060302u);
           const uint32_t hi23 = __builtin_amdgcn_perm(R[3][q], R[2][q], 0x07060302u);
           acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-              __builtin_bit_cast(h4_t, u2_t{lo01, lo23}), pb, acc[2 * q], 0, 0, 0);
+              __builtin_bit_cast(h4_t, u2_t{lo01, lo23}), ph, acc[2 * q], 0, 0, 0);
           acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-              __builtin_bit_cast(h4_t, u2_t{hi01, hi23}), pb, acc[2 * q + 1], 0, 0, 0);
+              __builtin_bit_cast(h4_t, u2_t{hi01, hi23}), ph, acc[2 * q + 1], 0, 0, 0);
         }
       }
     }
@@ -228,7 +241,7 @@ __global__ void __launch_bounds__(64, F::kWavesPerSimd) paged_decode_gqa(DecodeA
 
   // ---- split epilogue: statistics, partial output, mass partials
   const size_t st = (((size_t)s * a.n_layers + lr) * kQHeads + kGroup * g + c) * a.n_splits + split;
-  if (c < kGroup) {
+  if (c < kCols) {
     float* op = a.opart + st * kHeadDim + 32 * j;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -238,24 +251,40 @@ __global__ void __launch_bounds__(64, F::kWavesPerSimd) paged_decode_gqa(DecodeA
   }
   __syncthreads();
   const int cnt = b1 - b0;
-  const float lt = split_norm<kGroup>(pi_lds, SB, lane, cnt, 0);
-  if (c < kGroup && j == 0) a.ml[st] = make_float2(m_run, lt);
-  for (int hh = 0; hh < kGroup; ++hh) {
+  const float lt = split_norm<kCols>(pi_lds, SP, lane, cnt, cnt);
+  if (c < kCols && j == 0) a.ml[st] = make_float2(m_run, lt);
+  // four rows at a time, so that four LDS reads are in flight per store round
+  for (int hh = 0; hh < kCols; hh += 4) {
     float* dst = a.pi + ((size_t)lr * kQHeads + kGroup * g + hh) * a.total_blocks + r0 + b0;
-    for (int bb = lane; bb < cnt; bb += 64) dst[bb] = pi_lds[hh * SB + bb];
+    for (int bb = lane; bb < cnt; bb += 64) {
+      float x[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) x[t] = pi_lds[(hh + t) * SP + bb];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) dst[(size_t)t * a.total_blocks + bb] = x[t];
+    }
   }
 }
 
+static_assert(decode_lds_bytes(1024, KvE4M3::kHeads) <= kMaxDecodeLds,
+              "largest E4M3 split must fit the LDS bound");
+
 hipError_t launch_decode(const DecodeArgs& a, int batch, hipStream_t stream) {
-  const uint64_t wgs = (uint64_t)batch * a.n_splits * a.n_layers * 8u;
-  const size_t lds = decode_lds_bytes(a.split_blocks);
-  if (lds > kMaxDecodeLds) return hipErrorInvalidValue;
   if (a.kv_format == KVS_KV_KIVI2) return launch_decode_kivi(a, batch, stream);
   if (a.pair_role) return launch_decode_pair(a, batch, stream);
-  if (a.kv_format == KVS_KV_E4M3)
+  // one wave per (sequence, split, layer, group of F::kHeads KV heads)
+  const uint64_t items = (uint64_t)batch * a.n_splits * a.n_layers;
+  if (a.kv_format == KVS_KV_E4M3) {
+    const size_t lds = decode_lds_bytes(a.split_blocks, KvE4M3::kHeads);
+    if (lds > kMaxDecodeLds) return hipErrorInvalidValue;
+    const uint64_t wgs = items * (8u / KvE4M3::kHeads);
     hipLaunchKernelGGL(paged_decode_gqa<KvE4M3>, dim3((uint32_t)wgs), dim3(64), lds, stream, a);
-  else
-    hipLaunchKernelGGL(paged_decode_gqa<KvF16>, dim3((uint32_t)wgs), dim3(64), lds, stream, a);
+  } else {
+    const size_t lds = decode_lds_bytes(a.split_blocks);
+    if (lds > kMaxDecodeLds) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(paged_decode_gqa<KvF16>, dim3((uint32_t)(items * 8u)), dim3(64), lds,
+                       stream, a);
+  }
   return hipGetLastError();
 }
 

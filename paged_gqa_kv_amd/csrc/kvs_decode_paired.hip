@@ -372,7 +372,8 @@ hipError_t launch_decode_pair(const DecodeArgs& a, int batch, hipStream_t stream
   if (a.kv_format == KVS_KV_FP16)
     hipLaunchKernelGGL(paged_decode_pair<KvF16>, dim3((uint32_t)wgs), dim3(64), lds, stream, a);
   else if (a.kv_format == KVS_KV_E4M3)
-    hipLaunchKernelGGL(paged_decode_pair<KvE4M3>, dim3((uint32_t)wgs), dim3(64), lds, stream, a);
+    hipLaunchKernelGGL(paged_decode_pair<KvE4M3Pair>, dim3((uint32_t)wgs), dim3(64), lds, stream,
+                       a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

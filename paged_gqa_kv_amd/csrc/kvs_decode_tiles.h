@@ -12,20 +12,35 @@
 namespace kvs {
 
 // Stored K/V element formats.  A (layer, K|V, KV head) tile is 16 rows of 128
-// elements; a block holds, per layer, 8 key tiles then 8 value tiles.
+// elements; a block holds, per layer, 8 key tiles then 8 value tiles.  A step
+// of a decode wave loads kPer blocks of kHeads adjacent KV heads.
 struct KvF16 {
   static constexpr int kElemBytes = 2;
   static constexpr int kLoads = 4;   // 16-byte loads per lane per tile
   static constexpr int kPer = 1;     // blocks per step
+  static constexpr int kHeads = 1;   // KV heads per wave
   static constexpr int kRing = 2;    // ring slots (32 VGPRs each)
   static constexpr int kWavesPerSimd = kDecodeWavesPerSimd;
 };
 struct KvE4M3 {                      // FP8 E4M3 codes, no scale
   static constexpr int kElemBytes = 1;
   static constexpr int kLoads = 2;
-  static constexpr int kPer = 2;     // two blocks per step: more independent work per wave
+  static constexpr int kPer = 1;
+  // Two adjacent KV heads per wave: a step reads one 4 KiB run of keys and one
+  // of values, as the fp16 decode does, and fills all 16 MFMA columns.
+  static constexpr int kHeads = kE4M3HeadsPerWave;
   static constexpr int kRing = 2;    // ring slots (32 VGPRs each); 3 measured no faster
   static constexpr int kWavesPerSimd = kDecodeWavesPerSimdE4M3;
+};
+// The paired decode over E4M3 codes: one KV head and one block per step, so
+// that each (sequence, head) sees the arithmetic of the E4M3 decode above.
+struct KvE4M3Pair {
+  static constexpr int kElemBytes = 1;
+  static constexpr int kLoads = 2;
+  static constexpr int kPer = 1;
+  static constexpr int kHeads = 1;
+  static constexpr int kRing = 2;
+  static constexpr int kWavesPerSimd = kDecodeWavesPerSimd;
 };
 
 template <class F>
@@ -34,10 +49,11 @@ struct BlockRegs {
   u4_t v[F::kLoads];
 };
 
-// One ring slot: the kPer blocks of one step.
+// One ring slot: the tiles of one step, tile t = kHeads * p + h for block p of
+// the step and head h of the wave.
 template <class F>
 struct StepRegs {
-  BlockRegs<F> blk[F::kPer];
+  BlockRegs<F> blk[F::kPer * F::kHeads];
 };
 
 template <class F>
@@ -79,8 +95,8 @@ __device__ __forceinline__ u2_t e4m3x4_to_f16(uint32_t w) {
   return u2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
-// Value tile of block p of a step to the 4 KiB LDS stage, as stored: fp16
-// [16][128] (one block per step), or E4M3 codes [16][128] at byte 2048 p.
+// Value tile t of a step to the 4 KiB LDS stage, as stored: fp16 [16][128]
+// (one tile per step), or E4M3 codes [16][128] at byte 2048 t.
 template <class F>
 __device__ __forceinline__ void stage_values(const BlockRegs<F>& r, u4_t* vstage, int lane,
                                              int p) {
@@ -88,7 +104,7 @@ __device__ __forceinline__ void stage_values(const BlockRegs<F>& r, u4_t* vstage
   for (int i = 0; i < F::kLoads; ++i) vstage[p * 128 + i * 64 + lane] = r.v[i];
 }
 
-// The PV operand rows of block p: R[i] = 8 fp16 values, elements [8 c, 8 c + 8)
+// The PV operand rows of tile p: R[i] = 8 fp16 values, elements [8 c, 8 c + 8)
 // of value row 4 j + i (E4M3 codes are converted here, after the LDS read).
 template <class F>
 __device__ __forceinline__ void value_rows(const u4_t* vstage, int p, int j, int c, u4_t (&R)[4]) {

@@ -96,14 +96,25 @@ __device__ __forceinline__ float head_sum4(float v) {
 // thousands of increments near its rounding unit and drift (a 17-nat peak over
 // 16,384 tokens moved an fp32 sum by 3e-5).  The 64 / kRows lanes of a row
 // share its blocks; every lane returns its row's sum.
+// Eight LDS reads are issued per round and added in the order of the blocks,
+// so the sum is the same as one read at a time without a wait per block.
 template <int kRows>
 __device__ __forceinline__ float split_norm(const float* pi_lds, int SB, int lane, int cnt_lo,
                                             int cnt_hi) {
   constexpr int kParts = 64 / kRows;
   const int r = lane % kRows;
   const int cnt = r < 8 ? cnt_lo : cnt_hi;
+  const float* row = pi_lds + r * SB;
   double acc = 0.0;
-  for (int b = lane / kRows; b < cnt; b += kParts) acc += (double)pi_lds[r * SB + b];
+  int b = lane / kRows;
+  for (; b + 7 * kParts < cnt; b += 8 * kParts) {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = row[b + u * kParts];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += (double)x[u];
+  }
+  for (; b < cnt; b += kParts) acc += (double)row[b];
 #pragma unroll
   for (int m = kRows; m < 64; m <<= 1) acc += __shfl_xor(acc, m, 64);
   return (float)acc;

@@ -11,15 +11,27 @@ namespace kvs {
 constexpr int kMassThreads = 1024;   // 16 waves share one 32-block column group
 constexpr int kMassCols = 32;
 constexpr int kScoreThreads = 256;   // records per scoring work-group
-constexpr size_t kMaxDecodeLds = 65536;  // dynamic LDS a decode work-group may request
+// Dynamic LDS a decode work-group may request (gfx950 allows up to 160 KiB
+// per work-group).
+constexpr size_t kMaxDecodeLds = 98304;
 constexpr size_t kLdsPerCu = 163840;     // gfx950: 160 KiB of LDS per compute unit
 constexpr int kDecodeWavesPerSimd = 3;   // decode kernel launch bound (VGPR budget)
-constexpr int kDecodeWavesPerSimdE4M3 = 2;   // E4M3 decode: two blocks per step need more VGPRs
+constexpr int kDecodeWavesPerSimdE4M3 = 2;   // E4M3 decode: two KV heads per step need more VGPRs
+constexpr int kE4M3HeadsPerWave = 2;     // KV heads one E4M3 decode wave serves
 
-// LDS of one decode work-group (one wave): the split's block ids (4 B each),
-// per-block mass partials of the 8 heads (32 B each) and the 4 KiB value stage.
-constexpr size_t decode_lds_bytes(int32_t split_blocks) {
-  return (size_t)36 * (size_t)split_blocks + 4096;
+// LDS of one decode work-group (one wave serving `kv_heads` KV heads): the
+// split's block ids (4 B each), per-block mass partials of the 8 query heads
+// of each KV head (4 B each per head) and the 4 KiB value stage.  With two KV
+// heads the id list is rounded up to 4 entries and each head's partial row to
+// decode_pi_stride() floats, so rows are 16-byte aligned and fall on
+// different LDS banks.
+constexpr int32_t decode_pi_stride(int32_t split_blocks, int kv_heads) {
+  return kv_heads == 1 ? split_blocks : ((split_blocks + 3) & ~3) + 4;
+}
+constexpr size_t decode_lds_bytes(int32_t split_blocks, int kv_heads = 1) {
+  const int32_t ids = kv_heads == 1 ? split_blocks : (split_blocks + 3) & ~3;
+  return (size_t)4 * (size_t)ids +
+         (size_t)4 * 8 * (size_t)kv_heads * (size_t)decode_pi_stride(split_blocks, kv_heads) + 4096;
 }
 
 // LDS of one paired decode work-group: block ids of both sequences, mass

@@ -32,17 +32,17 @@ def pair_plan(table_host, blocks) -> np.ndarray:
     return role
 
 
-def pair_loaded_tokens(table_host, lens, role, split_blocks: int, blocks_per_step: int = 1) -> int:
+def pair_loaded_tokens(table_host, lens, role, split_blocks: int) -> int:
     """Tokens whose keys and values the paired decode loads per (layer, KV
     head).  A split is joint when its two sequences are linked both ways, both
     reach the split's first position and hold the same block there.  A joint
-    split walks groups of blocks_per_step positions from its first block (1
-    for fp16, 2 for E4M3); a group in which no position holds different blocks
-    in the two sequences is loaded once, each position for the larger of the
-    two token counts, any other group once per sequence.  Every other split
-    loads its own sequence's tokens, as the unpaired decode does."""
+    split walks its positions one block at a time: a position where the two
+    sequences hold the same block (or only one of them reaches) is loaded
+    once, for the larger of the two token counts, any other position once per
+    sequence.  Every other split loads its own sequence's tokens, as the
+    unpaired decode does."""
     role = np.asarray(role)
-    B, SB, per = len(lens), int(split_blocks), int(blocks_per_step)
+    B, SB = len(lens), int(split_blocks)
     lens = np.asarray(lens, dtype=np.int64)
     nb = (lens + 15) // 16
     tbl = table_host
@@ -75,12 +75,10 @@ def pair_loaded_tokens(table_host, lens, role, split_blocks: int, blocks_per_ste
                 continue   # loaded by the first sequence's work-groups
             p = link[1]
             b1p = min(int(nb[p]), b0 + SB)
-            for g0 in range(b0, max(b1, b1p), per):
-                group = range(g0, g0 + per)
-                same = all(not (b < b1 and b < b1p and tbl[s, b] != tbl[p, b]) for b in group)
-                for b in group:
-                    va, vb = tokens_at(s, b, b1), tokens_at(p, b, b1p)
-                    tokens += max(va, vb) if same else va + vb
+            for b in range(b0, max(b1, b1p)):
+                same = not (b < b1 and b < b1p and tbl[s, b] != tbl[p, b])
+                va, vb = tokens_at(s, b, b1), tokens_at(p, b, b1p)
+                tokens += max(va, vb) if same else va + vb
     return tokens
 
 
@@ -192,7 +190,7 @@ class DecodeSession:
             return self.kv_bytes_per_step
         m = self.m
         tokens = pair_loaded_tokens(m.table_host, m.lens, self.pair_role.cpu().numpy(),
-                                    self.split_blocks, 2 if self.kv_format == "e4m3" else 1)
+                                    self.split_blocks)
         layers = self.layer_end - self.layer_begin
         return tokens * layers * 8 * 128 * 2 * self.kv_elem_bytes
 

@@ -73,39 +73,21 @@ def test_loaded_tokens_split_joint_only_at_equal_first_block():
     assert pair_loaded_tokens(table, [64, 40], role, 1) == 64
 
 
-@pytest.mark.parametrize("split_blocks", [4, 8, 128, 512])
-def test_loaded_tokens_two_blocks_per_step_closed_form(split_blocks):
-    # a 128-block prefix and even splits: every two-block group is wholly shared
-    # or wholly private, so the saving is the one-block-per-step closed form
-    rng = np.random.default_rng(5)
-    prefix = 2048
-    lens = rng.integers(1, 5000, size=14).tolist() + [prefix, 2047, 2049, 17]
-    _, blocks, table = _tables(lens, prefix)
-    role = pair_plan(table, blocks)
-    saved = sum(min(lens[a], lens[b], prefix) for a in range(len(lens))
-                for b in [int(role[a])] if b >= 0)
-    assert pair_loaded_tokens(table, lens, role, split_blocks, 2) == sum(lens) - saved
-
-
-def test_loaded_tokens_two_blocks_per_step_group_rule():
-    # sequence 1 differs from sequence 0 at position 1 only: one block per step
-    # shares positions 0, 2 and 3; two per step shares only the group (2, 3)
+def test_loaded_tokens_position_rule():
+    # sequence 1 differs from sequence 0 at position 1 only: positions 0, 2 and
+    # 3 are loaded once, position 1 once per sequence
     table = np.array([[0, 1, 2, 3], [0, 9, 2, 3]], dtype=np.int32)
     role = np.array([1, -2])
-    assert pair_loaded_tokens(table, [64, 64], role, 4, 1) == 16 + 32 + 16 + 16
-    assert pair_loaded_tokens(table, [64, 64], role, 4, 2) == 64 + 32
-    # an odd split size: groups start at each split's first block.  Splits
-    # [0, 3) and [3, 6), both joint; position 4 differs.  Two per step: groups
-    # (0, 1) and (2) shared, (3, 4) loaded for both, (5) shared.
+    assert pair_loaded_tokens(table, [64, 64], role, 4) == 16 + 32 + 16 + 16
+    # an odd split size: splits [0, 3) and [3, 6), both joint; position 4 differs
     table = np.array([[0, 1, 2, 3, 4, 5], [0, 1, 2, 3, 7, 5]], dtype=np.int32)
-    assert pair_loaded_tokens(table, [96, 96], role, 3, 1) == 16 * 3 + (16 + 32 + 16)
-    assert pair_loaded_tokens(table, [96, 96], role, 3, 2) == 16 * 3 + (64 + 16)
+    assert pair_loaded_tokens(table, [96, 96], role, 3) == 16 * 3 + (16 + 32 + 16)
 
 
-def _walk_tokens(table, lens, role, SB, per):
+def _walk_tokens(table, lens, role, SB):
     """The paired kernel's walk, step by step (joint splits decoded by the first
-    sequence of a pair; within one, groups of `per` positions; a joint group is
-    one load per position, any other group one load per sequence), summing
+    sequence of a pair; within one, a position holding the same block in both
+    sequences is one load, any other position one load per sequence), summing
     each loaded block's tokens for the sequences it is live for."""
     B = len(lens)
     nb = [(int(n) + 15) // 16 for n in lens]
@@ -130,23 +112,20 @@ def _walk_tokens(table, lens, role, SB, per):
             steps = []
             cur = b0
             while cur < max(b1a, b1b):
-                grp = range(cur, cur + per)
-                if all(not (q < b1a and q < b1b and table[s][q] != table[p][q]) for q in grp):
+                if not (cur < b1a and cur < b1b and table[s][cur] != table[p][cur]):
                     steps.append((cur, 3))
                 else:
                     steps += [(cur, 1), (cur, 2)]
-                cur += per
-            for start, mask in steps:
-                for q in range(start, start + per):
-                    va = min(16, int(lens[s]) - 16 * q) if (mask & 1) and q < b1a else 0
-                    vb = min(16, int(lens[p]) - 16 * q) if (mask & 2) and q < b1b else 0
-                    total += max(va, vb)
+                cur += 1
+            for q, mask in steps:
+                va = min(16, int(lens[s]) - 16 * q) if (mask & 1) and q < b1a else 0
+                vb = min(16, int(lens[p]) - 16 * q) if (mask & 2) and q < b1b else 0
+                total += max(va, vb)
     return total
 
 
-@pytest.mark.parametrize("per", [1, 2])
 @pytest.mark.parametrize("seed", range(6))
-def test_loaded_tokens_match_a_step_by_step_walk(per, seed):
+def test_loaded_tokens_match_a_step_by_step_walk(seed):
     rng = np.random.default_rng(seed)
     B = int(rng.integers(2, 9))
     lens = [int(x) for x in rng.integers(0, 900, size=B)]
@@ -162,5 +141,4 @@ def test_loaded_tokens_match_a_step_by_step_walk(per, seed):
         if rng.random() < 0.8:
             role[a_], role[b_] = b_, -2 - a_
     for SB in (4, 5, 16):
-        assert pair_loaded_tokens(table, lens, role, SB, per) == _walk_tokens(table, lens, role,
-                                                                              SB, per)
+        assert pair_loaded_tokens(table, lens, role, SB) == _walk_tokens(table, lens, role, SB)
