@@ -228,6 +228,12 @@ int kvs_device_status(void* workspace, void* stream, uint32_t* bits);
  *                the value given to kvs_decode_workspace_bytes.
  *  workspace     device scratch of kvs_decode_workspace_bytes() bytes, 256-B
  *                aligned, status header zeroed once by kvs_workspace_init().
+ * A wave of the decode serves one KV head, or two adjacent ones (2 i, 2 i + 1)
+ * when the records cover at least 3/4 of batch x splits x split_blocks (the
+ * sequences fill their splits).  The results are the same bit for bit either
+ * way, except that with two heads per wave a NaN among the values a sequence
+ * reads from one head also makes those channels NaN in the other head's output
+ * rows.
  */
 int kvs_decode_step(const kvs_shape* shape,
                     const void* q,

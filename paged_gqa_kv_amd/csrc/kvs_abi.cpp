@@ -128,7 +128,20 @@ uint64_t wave_inflight_bytes(int32_t kv_format) {
   }
 }
 
-// KV heads one decode wave serves.
+// KV heads per wave of the fp16 decode for these sizes.  Two adjacent heads
+// per wave read 8 KiB runs per step (+3.2 % at 128K x 80 layers, +1.7 % at
+// 1M x 32, +1 % on 8 x 8K x 4), but their LDS leaves 2-3 waves per CU, and
+// when the sequences fill their splits only in part (the 32-sequence batch of
+// mixed lengths: -3 % at its best split) one head per wave is faster.  So two
+// heads when the records cover at least 3/4 of the splits' blocks.
+int32_t fp16_heads_per_wave(int32_t batch, int64_t total_blocks, int32_t n_splits,
+                            int32_t split_blocks) {
+  const int64_t cover = (int64_t)batch * (int64_t)n_splits * (int64_t)split_blocks;
+  return 4 * total_blocks >= 3 * cover ? 2 : 1;
+}
+
+// KV heads one decode wave serves, as the split choice sizes it (the fp16
+// decode is sized for one head).
 uint32_t heads_per_wave(int32_t kv_format) {
   return kv_format == KVS_KV_E4M3 ? (uint32_t)kvs::kE4M3HeadsPerWave : 1u;
 }
@@ -450,6 +463,10 @@ int decode_step(int32_t kv_format, const kvs_shape* shape, const void* q, const 
   d.kivi_blocks = kivi ? kivi_blocks : 0;
   d.quant_lens = kivi ? quant_lens : nullptr;
   d.pair_role = pair_role;
+  d.kv_heads = kv_format == KVS_KV_E4M3   ? kvs::kE4M3HeadsPerWave
+               : kv_format == KVS_KV_FP16 ? fp16_heads_per_wave(batch, total_blocks, L.n_splits,
+                                                                L.split_blocks)
+                                          : 1;
   d.ml = reinterpret_cast<float2*>(ws + L.ml);
   d.opart = reinterpret_cast<float*>(ws + L.opart);
   d.pi = reinterpret_cast<float*>(ws + L.pi);

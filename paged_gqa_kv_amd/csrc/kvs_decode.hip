@@ -268,6 +268,8 @@ __global__ void __launch_bounds__(64, F::kWavesPerSimd) paged_decode_gqa(DecodeA
 
 static_assert(decode_lds_bytes(1024, KvE4M3::kHeads) <= kMaxDecodeLds,
               "largest E4M3 split must fit the LDS bound");
+static_assert(decode_lds_bytes(1024, 2, 2 * tile_bytes<KvF16x2>()) <= kMaxDecodeLds,
+              "largest two-head fp16 split must fit the LDS bound");
 
 hipError_t launch_decode(const DecodeArgs& a, int batch, hipStream_t stream) {
   if (a.kv_format == KVS_KV_KIVI2) return launch_decode_kivi(a, batch, stream);
@@ -279,6 +281,11 @@ hipError_t launch_decode(const DecodeArgs& a, int batch, hipStream_t stream) {
     if (lds > kMaxDecodeLds) return hipErrorInvalidValue;
     const uint64_t wgs = items * (8u / KvE4M3::kHeads);
     hipLaunchKernelGGL(paged_decode_gqa<KvE4M3>, dim3((uint32_t)wgs), dim3(64), lds, stream, a);
+  } else if (a.kv_heads == 2) {
+    const size_t lds = decode_lds_bytes(a.split_blocks, 2, 2 * tile_bytes<KvF16x2>());
+    if (lds > kMaxDecodeLds) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(paged_decode_gqa<KvF16x2>, dim3((uint32_t)(items * 4u)), dim3(64), lds,
+                       stream, a);
   } else {
     const size_t lds = decode_lds_bytes(a.split_blocks);
     if (lds > kMaxDecodeLds) return hipErrorInvalidValue;

@@ -22,6 +22,16 @@ struct KvF16 {
   static constexpr int kRing = 2;    // ring slots (32 VGPRs each)
   static constexpr int kWavesPerSimd = kDecodeWavesPerSimd;
 };
+// fp16 with two adjacent KV heads per wave: 8 KiB runs of keys and of values
+// per step.  The decode takes it when the sequences fill their splits.
+struct KvF16x2 {
+  static constexpr int kElemBytes = 2;
+  static constexpr int kLoads = 4;
+  static constexpr int kPer = 1;
+  static constexpr int kHeads = 2;
+  static constexpr int kRing = 2;    // ring slots (64 VGPRs each)
+  static constexpr int kWavesPerSimd = kDecodeWavesPerSimdF16x2;
+};
 struct KvE4M3 {                      // FP8 E4M3 codes, no scale
   static constexpr int kElemBytes = 1;
   static constexpr int kLoads = 2;
@@ -95,13 +105,13 @@ __device__ __forceinline__ u2_t e4m3x4_to_f16(uint32_t w) {
   return u2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
-// Value tile t of a step to the 4 KiB LDS stage, as stored: fp16 [16][128]
-// (one tile per step), or E4M3 codes [16][128] at byte 2048 t.
+// Value tile t of a step to the LDS stage, as stored ([16][128] fp16 values or
+// E4M3 codes), at byte t * tile_bytes.
 template <class F>
 __device__ __forceinline__ void stage_values(const BlockRegs<F>& r, u4_t* vstage, int lane,
                                              int p) {
 #pragma unroll
-  for (int i = 0; i < F::kLoads; ++i) vstage[p * 128 + i * 64 + lane] = r.v[i];
+  for (int i = 0; i < F::kLoads; ++i) vstage[p * (tile_bytes<F>() / 16) + i * 64 + lane] = r.v[i];
 }
 
 // The PV operand rows of tile p: R[i] = 8 fp16 values, elements [8 c, 8 c + 8)
@@ -110,7 +120,7 @@ template <class F>
 __device__ __forceinline__ void value_rows(const u4_t* vstage, int p, int j, int c, u4_t (&R)[4]) {
   if constexpr (F::kElemBytes == 2) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) R[i] = vstage[(4 * j + i) * 16 + c];
+    for (int i = 0; i < 4; ++i) R[i] = vstage[p * 256 + (4 * j + i) * 16 + c];
   } else {
     const uint8_t* tile = reinterpret_cast<const uint8_t*>(vstage) + 2048 * p;
 #pragma unroll

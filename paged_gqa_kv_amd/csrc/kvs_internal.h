@@ -17,21 +17,25 @@ constexpr size_t kMaxDecodeLds = 98304;
 constexpr size_t kLdsPerCu = 163840;     // gfx950: 160 KiB of LDS per compute unit
 constexpr int kDecodeWavesPerSimd = 3;   // decode kernel launch bound (VGPR budget)
 constexpr int kDecodeWavesPerSimdE4M3 = 2;   // E4M3 decode: two KV heads per step need more VGPRs
+constexpr int kDecodeWavesPerSimdF16x2 = 2;  // fp16 decode with two KV heads per wave
 constexpr int kE4M3HeadsPerWave = 2;     // KV heads one E4M3 decode wave serves
 
 // LDS of one decode work-group (one wave serving `kv_heads` KV heads): the
 // split's block ids (4 B each), per-block mass partials of the 8 query heads
-// of each KV head (4 B each per head) and the 4 KiB value stage.  With two KV
+// of each KV head (4 B each per head) and the value stage (`stage_bytes`: one
+// 4 KiB fp16 tile, two 2 KiB E4M3 tiles, or two fp16 tiles).  With two KV
 // heads the id list is rounded up to 4 entries and each head's partial row to
 // decode_pi_stride() floats, so rows are 16-byte aligned and fall on
 // different LDS banks.
 constexpr int32_t decode_pi_stride(int32_t split_blocks, int kv_heads) {
   return kv_heads == 1 ? split_blocks : ((split_blocks + 3) & ~3) + 4;
 }
-constexpr size_t decode_lds_bytes(int32_t split_blocks, int kv_heads = 1) {
+constexpr size_t decode_lds_bytes(int32_t split_blocks, int kv_heads = 1,
+                                  size_t stage_bytes = 4096) {
   const int32_t ids = kv_heads == 1 ? split_blocks : (split_blocks + 3) & ~3;
   return (size_t)4 * (size_t)ids +
-         (size_t)4 * 8 * (size_t)kv_heads * (size_t)decode_pi_stride(split_blocks, kv_heads) + 4096;
+         (size_t)4 * 8 * (size_t)kv_heads * (size_t)decode_pi_stride(split_blocks, kv_heads) +
+         stage_bytes;
 }
 
 // LDS of one paired decode work-group: block ids of both sequences, mass
@@ -79,6 +83,7 @@ struct DecodeArgs {
   int64_t kivi_blocks;
   const int32_t* quant_lens;  // KVS_KV_KIVI2: [B] quantised tokens per sequence
   const int32_t* pair_role;   // nullable: pairs of sequences decoded by one wave (fp16)
+  int32_t kv_heads;           // fp16 decode: KV heads per wave (1 or 2)
   float2* ml;               // [B][n_layers][64][n_splits]: (running max, sum), base 2
   float* opart;             // [B][n_layers][64][n_splits][128]
   float* pi;                // [n_layers][64][total_blocks]

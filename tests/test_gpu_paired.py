@@ -184,3 +184,29 @@ def test_paired_decode_rejects_before_launch():
                                     e4.meta_offsets, e4.batch, e4.total_blocks, 0,
                                     e4.num_layers, api.DEFAULT_SCALE, sess.out, sess.mass, 0, 8,
                                     sess.ws)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_two_heads_per_wave_decode_matches_one_head_per_wave_bit_for_bit(fmt):
+    """Sequences that fill their splits: the fp16 decode then serves two KV heads
+    per wave (records >= 3/4 of batch x splits x split blocks), as the E4M3
+    decode always does.  The paired decode with no pairs serves one head per
+    wave; per query head the arithmetic is the same, so every bit must match,
+    and both match the oracle."""
+    _case(f"{fmt}: 4 x 1,024 tokens at split 16 (two heads per wave) against the paired "
+          "decode with no pairs (one head per wave)")
+    m = W.materialise(_fmt(W.custom("full", 2, [1024, 1024, 1024, 1000], seed=31,
+                                    spare_blocks=3), fmt), DEV)
+    assert 4 * m.total_blocks >= 3 * m.batch * 4 * 16      # the two-heads rule holds
+    q = W.make_query(m, 0)
+    one = DecodeSession(m, split_blocks=16, pair_role=np.full(m.batch, -1, dtype=np.int32))
+    two = DecodeSession(m, split_blocks=16)
+    one.decode(q)
+    two.decode(q)
+    torch.cuda.synchronize()
+    assert one.status() == 0 and two.status() == 0
+    assert torch.equal(_bits(one.out), _bits(two.out))
+    assert torch.equal(_bits(one.mass), _bits(two.mass))
+    out_ref, mass_ref = P.oracle_decode(P.host(m), q)
+    P.check_out(two.out, out_ref, range(m.num_layers))
+    P.check_mass(two.mass, mass_ref, m.meta_offsets.cpu().numpy())
