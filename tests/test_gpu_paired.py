@@ -186,21 +186,24 @@ def test_paired_decode_rejects_before_launch():
                                     sess.ws)
 
 
+@pytest.mark.parametrize("split_blocks", [16, 5, 37])
 @pytest.mark.parametrize("fmt", FORMATS)
-def test_two_heads_per_wave_decode_matches_one_head_per_wave_bit_for_bit(fmt):
+def test_two_heads_per_wave_decode_matches_one_head_per_wave_bit_for_bit(fmt, split_blocks):
     """Sequences that fill their splits: the fp16 decode then serves two KV heads
     per wave (records >= 3/4 of batch x splits x split blocks), as the E4M3
     decode always does.  The paired decode with no pairs serves one head per
     wave; per query head the arithmetic is the same, so every bit must match,
     and both match the oracle."""
-    _case(f"{fmt}: 4 x 1,024 tokens at split 16 (two heads per wave) against the paired "
-          "decode with no pairs (one head per wave)")
+    _case(f"{fmt}: 4 x 1,024 tokens at split {split_blocks} (two heads per wave) against the "
+          "paired decode with no pairs (one head per wave)")
     m = W.materialise(_fmt(W.custom("full", 2, [1024, 1024, 1024, 1000], seed=31,
                                     spare_blocks=3), fmt), DEV)
-    assert 4 * m.total_blocks >= 3 * m.batch * 4 * 16      # the two-heads rule holds
+    n_splits = -(-64 // split_blocks)
+    assert 4 * m.total_blocks >= 3 * m.batch * n_splits * split_blocks   # the two-heads rule holds
     q = W.make_query(m, 0)
-    one = DecodeSession(m, split_blocks=16, pair_role=np.full(m.batch, -1, dtype=np.int32))
-    two = DecodeSession(m, split_blocks=16)
+    one = DecodeSession(m, split_blocks=split_blocks,
+                        pair_role=np.full(m.batch, -1, dtype=np.int32))
+    two = DecodeSession(m, split_blocks=split_blocks)
     one.decode(q)
     two.decode(q)
     torch.cuda.synchronize()
