@@ -25,7 +25,8 @@ namespace kvs {
 // paged_decode_gqa
 //
 // One 64-lane wave owns (s, layer, split) and F::kHeads adjacent KV heads from
-// g: one for fp16, two for E4M3.  Lane l = 16 j + c.
+// g: two for E4M3; for fp16 one, or two when the sequences fill their splits
+// (the host's choice, DecodeArgs::kv_heads).  Lane l = 16 j + c.
 //  QK:  S^T[token][col] = K[token][:] . q[col][:] on v_mfma_f32_16x16x32_f16,
 //       A = a 16x128 key tile (lane reads 64 contiguous bytes of row c), B =
 //       the queries: column c holds query head 8 g + c for c < 8 F::kHeads, the
