@@ -89,17 +89,22 @@ class HipEvents:
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so.7")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
+    # hipEventDisableSystemFence: these events only time the kernels and are read
+    # after a full device synchronisation, so they need no system-scope fence,
+    # which would add a cache write-back and invalidation at every record.
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
     def create(self):
         ev = ctypes.c_void_p()
-        rc = self.hip.hipEventCreate(ctypes.byref(ev))
+        rc = self.hip.hipEventCreateWithFlags(ctypes.byref(ev), self.DISABLE_SYSTEM_FENCE)
         if rc != 0:
-            raise RuntimeError(f"hipEventCreate failed ({rc})")
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
         return ev.value
 
     def record(self, ev, stream_handle: int):
@@ -333,9 +338,10 @@ def main():
     wall0 = time.perf_counter()
     lens_at_start = m.seq_lens.cpu().numpy().copy()
     # Inside the timed region the only markers are the two HIP events around
-    # each decode kernel (the roofline's timing); on the 8 x 8K x 4-layer batch
-    # two more per step cost 5 us of a 180 us step.  Per-step times come from
-    # those events, the scoring kernels are timed apart afterwards.
+    # each decode kernel (the roofline's timing).  Each idles the queue for about
+    # 4.5 us (8 x 8K tokens x 4 layers: a 173 us step without them, 182 us with
+    # them, kernel trace), so per-step times come from those events and the
+    # scoring kernels are timed apart afterwards.
     scrub = None
     bounds = ends = None
     if args.scrub_mib > 0:   # read between steps, outside each step's events
