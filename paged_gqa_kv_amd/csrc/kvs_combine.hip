@@ -169,6 +169,7 @@ __global__ void __launch_bounds__(kMassThreads) block_mass(MassArgs a) {
 // all its sequence's statistics, which is why it is kept for small problems.
 // ---------------------------------------------------------------------------
 constexpr int kFusedMaxWeights = 4096;   // (layer, head) rows x splits in LDS
+constexpr int kFusedRegSplits = 16;      // rows of up to this many splits load them at once
 
 __global__ void __launch_bounds__(kMassThreads) combine_mass(CombineArgs c, MassArgs a,
                                                              uint32_t comb_wgs,
@@ -193,6 +194,31 @@ __global__ void __launch_bounds__(kMassThreads) combine_mass(CombineArgs c, Mass
   const int rows = a.n_layers * kQHeads;
   for (int row = threadIdx.x; row < rows; row += kMassThreads) {
     const float2* st = c.ml + ((size_t)s * rows + row) * a.n_splits;
+    if (nsp <= kFusedRegSplits) {
+      // The row's statistics in registers, all loads issued at once (indices
+      // past nsp re-read the last split and are skipped): the loops below
+      // would otherwise wait for one load per split, three times over.
+      float2 v[kFusedRegSplits];
+#pragma unroll
+      for (int k = 0; k < kFusedRegSplits; ++k) v[k] = st[min(k, nsp - 1)];
+      float M = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < kFusedRegSplits; ++k)
+        if (k < nsp) M = fmaxf(M, v[k].x);
+      double L = 0.0;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int k = 0; k < kFusedRegSplits; ++k)
+          if (k < nsp) L += (double)v[k].y * (double)__builtin_amdgcn_exp2f(v[k].x - M);
+      }
+      const bool dead = !(L > 0.0);
+      const double invL = dead ? 0.0 : 1.0 / L;
+#pragma unroll
+      for (int k = 0; k < kFusedRegSplits; ++k)
+        if (k < nsp)
+          wl[row * nsp + k] = dead ? 0.f : (float)((double)__builtin_amdgcn_exp2f(v[k].x - M) * invL);
+      continue;
+    }
     float M = -INFINITY;
     for (int k = 0; k < nsp; ++k) M = fmaxf(M, st[k].x);
     double L = 0.0;

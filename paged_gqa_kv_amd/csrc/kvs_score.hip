@@ -99,6 +99,23 @@ __global__ void __launch_bounds__(kScoreThreads) score_update(ScoreArgs a) {
   const int nb = seq_records(a.meta_off, a.seq_lens, s, a.max_nb, a.total_blocks, a.status,
                              direct && threadIdx.x == 0 && chunk == 0, &r0);
   if (nb <= 0 || chunk * kScoreThreads >= nb) return;
+  // This thread's record and mass are loaded before the sequence maximum, so
+  // that their latency overlaps it; no other thread touches the record.
+  const int b = chunk * kScoreThreads + threadIdx.x;
+  const bool live = b < nb;
+  kvs_block_meta* rec = a.meta + r0 + (live ? b : 0);
+  uint64_t tt = 0;
+  double prev = 0.0;
+  uint32_t count = 0;
+  uint8_t flags = 0;
+  float mb = 0.f;
+  if (live) {
+    tt = rec->t_touch;
+    prev = rec->score;
+    count = rec->touch_count;
+    flags = rec->flags;
+    mb = a.mass[r0 + b];
+  }
   float M = 0.f;
   if (direct) {
     // indices past the end re-read the last record: harmless for a maximum
@@ -116,28 +133,24 @@ __global__ void __launch_bounds__(kScoreThreads) score_update(ScoreArgs a) {
   }
   M = block_reduce_max(M, red);
 
-  const int b = chunk * kScoreThreads + threadIdx.x;
   bool stale = false;
-  if (b < nb) {
-    kvs_block_meta* rec = a.meta + r0 + b;
-    const uint64_t tt = rec->t_touch;
+  if (live) {
     if (tt != KVS_NEVER_TOUCHED && tt >= a.step) {
       stale = true;
     } else {
-      const double mh = M > 0.f ? (double)a.mass[r0 + b] / (double)M : 0.0;
+      const double mh = M > 0.f ? (double)mb / (double)M : 0.0;
       // Input 0 on the steps since the last touch: the stored score first
       // decays over the gap, then takes the one-step update.
-      double prev = rec->score;
       if (tt != KVS_NEVER_TOUCHED && a.step - tt > 1)
         prev *= pow(1.0 - a.pol.alpha, (double)(a.step - tt - 1));
       const double e = a.pol.alpha * mh + (1.0 - a.pol.alpha) * prev;
       rec->score = e;
-      rec->touch_count = rec->touch_count + 1u;
+      rec->touch_count = count + 1u;
       rec->t_touch = a.step;
       if (a.classify) {
         double P;
         uint8_t tier;
-        priority_and_tier(a.pol, b, nb, e, rec->flags, &P, &tier);
+        priority_and_tier(a.pol, b, nb, e, flags, &P, &tier);
         rec->priority = P;
         rec->tier = tier;
       }
