@@ -17,7 +17,7 @@ Prints one JSON line:
   cpu_baseline   the fp64 oracle over one whole step of the same workload on
                  the host's cores (measured, with its thread counts)
   copy_probe     a 4 GiB device copy (read + write) and the library's
-                 streaming read probe over a 16 GiB buffer;
+                 streaming read probe over a 16 GiB buffer, best of four grids;
                  frac_of_read_probe = roofline.achieved / that read rate
 """
 from __future__ import annotations
@@ -32,6 +32,7 @@ import sys
 import time
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, published
+READ_PROBE_GRIDS = (256, 512, 1024, 2048)   # work-groups swept by the streaming read probe
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "paged_gqa_kv_amd", "csrc")
 # Sources a decode kernel is compiled from; a committed counter summary is used
@@ -141,7 +142,8 @@ def _copy_probe(gib: float, reps: int, read_gib: float):
     median of reps, counting bytes read plus bytes written (the method the
     Visual Reference's measurement box describes for its 87 %-of-spec figure).
     Beside it, the library's streaming read probe (kvs_stream_probe, mode 0)
-    over a read_gib-GiB buffer: the read-only rate a decode could at best reach."""
+    over a read_gib-GiB buffer at several grids, the best of them: the read-only
+    rate a decode could at best reach."""
     import torch
 
     from paged_gqa_kv_amd import api
@@ -169,12 +171,17 @@ def _copy_probe(gib: float, reps: int, read_gib: float):
     del src, dst
     nr = int(read_gib * 2**30) // 16 * 16
     rsrc = torch.empty(nr, dtype=torch.uint8, device="cuda")   # contents do not matter
-    med_read = median_s(lambda: api.stream_probe(rsrc, sink, nr, 0))
+    # 1 to 8 work-groups of 256 lanes per compute unit; the fastest counts
+    by_grid = {g: median_s(lambda g=g: api.stream_probe(rsrc, sink, nr, 0, g))
+               for g in READ_PROBE_GRIDS}
+    grid = min(by_grid, key=by_grid.get)
+    med_read = by_grid[grid]
     del rsrc, sink
     torch.cuda.empty_cache()
     return {"bytes_per_copy": 2 * n * 4, "median_s": med, "gbps": 2 * n * 4 / med / 1e9,
             "reps": reps, "read_probe_bytes": nr, "read_probe_median_s": med_read,
-            "read_probe_gbps": nr / med_read / 1e9}
+            "read_probe_gbps": nr / med_read / 1e9, "read_probe_grid": grid,
+            "read_probe_gbps_by_grid": {str(g): round(nr / t / 1e9, 1) for g, t in by_grid.items()}}
 
 
 def _cpu_baseline(m, alpha, budget_s):

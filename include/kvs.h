@@ -184,9 +184,11 @@ int kvs_set_decode_events(void* before, void* after);
  * copy of large buffers, median of several runs: Visual Reference Sec. 4 and 9,
  * measurement notes).  Not part of the decode path.
  *  mode 0 (read):  reads `bytes` from src, each wave 8 KiB chunks of 1 KiB
- *                  non-temporal loads with the grid sweeping the buffer front
- *                  to back; every lane folds what it read into one 32-bit word
- *                  written to dst (dst holds grid x 256 words).
+ *                  non-temporal loads, two chunks in flight, with the grid
+ *                  sweeping the buffer front to back; every lane folds what it
+ *                  read into one 32-bit word written to dst (dst must hold
+ *                  grid x 256 words, 2,048 x 256 for grid 0: the library
+ *                  cannot check this and writes past a shorter dst).
  *  mode 1 (copy):  copies `bytes` from src to dst.
  * bytes must be a non-zero multiple of 16; src and dst 16-byte aligned;
  * grid = number of 256-lane work-groups (0 = library choice). */

@@ -121,7 +121,20 @@ def set_decode_events(before, after) -> None:
     check(lib().kvs_set_decode_events(_p(before), _p(after)))
 
 
+PROBE_DEFAULT_GRID = 2048   # work-groups kvs_stream_probe launches for grid 0
+
+
 def stream_probe(src, dst, nbytes: int, mode: int, grid: int = 0, stream=None) -> None:
+    """kvs_stream_probe.  Where src / dst are tensors their sizes are checked
+    first: src must hold nbytes; dst nbytes (copy) or one 32-bit word per lane,
+    grid x 256 words (read)."""
+    if hasattr(src, "numel") and _nbytes(src) < nbytes:
+        raise ValueError(f"src holds {_nbytes(src)} bytes, the probe reads {nbytes}")
+    if hasattr(dst, "numel"):
+        need = nbytes if mode == 1 else (grid if grid > 0 else PROBE_DEFAULT_GRID) * 256 * 4
+        if _nbytes(dst) < need:
+            raise ValueError(f"dst holds {_nbytes(dst)} bytes, mode {mode} at grid {grid} "
+                             f"writes {need}")
     check(lib().kvs_stream_probe(_p(src), _p(dst), nbytes, mode, grid, _s(stream)))
 
 

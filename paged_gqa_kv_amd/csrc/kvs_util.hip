@@ -21,9 +21,9 @@ __global__ void __launch_bounds__(64) clear_words(uint32_t* p, int n) {
 
 // ---------------------------------------------------------------------------
 // stream probe.  Read: each wave takes 8 KiB chunks (chunk w, w + waves, ...),
-// eight 1 KiB non-temporal loads per chunk, so the whole grid sweeps the
-// buffer front to back the way a decode wave reads a tile.  Copy: grid-stride
-// 16-byte loads and stores.
+// eight 1 KiB non-temporal loads per chunk and two chunks in flight, so the
+// whole grid sweeps the buffer front to back the way a decode wave reads a
+// tile.  Copy: grid-stride 16-byte loads and stores.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) stream_read(const u4_t* __restrict__ src, size_t n16,
                                                   uint32_t* __restrict__ sink) {
@@ -32,13 +32,22 @@ __global__ void __launch_bounds__(256) stream_read(const u4_t* __restrict__ src,
   const size_t w = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const size_t nchunks = n16 / 512;
   uint32_t acc = 0;
-  for (size_t ch = w; ch < nchunks; ch += waves) {
+  for (size_t ch = w; ch < nchunks; ch += 2 * waves) {
+    // the second chunk past the end re-reads the first and is not counted
+    const bool second = ch + waves < nchunks;
     const u4_t* p = src + ch * 512 + lane;
-    u4_t v[8];
+    const u4_t* p2 = src + (second ? ch + waves : ch) * 512 + lane;
+    u4_t v[8], v2[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(p + 64 * u);
 #pragma unroll
+    for (int u = 0; u < 8; ++u) v2[u] = __builtin_nontemporal_load(p2 + 64 * u);
+#pragma unroll
     for (int u = 0; u < 8; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    if (second) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc ^= v2[u][0] ^ v2[u][1] ^ v2[u][2] ^ v2[u][3];
+    }
   }
   const size_t tid = (size_t)blockIdx.x * 256 + threadIdx.x;
   for (size_t i = nchunks * 512 + tid; i < n16; i += waves * 64) {

@@ -366,3 +366,19 @@ def test_noalloc_scratch_holds_a_layer_range_of_the_128k_step():
     assert _abi.KVS_NOALLOC_SCRATCH_BYTES == 32 << 20
     assert api.decode_workspace_bytes(shp, 1, 8192, 8192, 0, 8, 0, "fp16") <= 32 << 20
     assert api.decode_workspace_bytes(shp, 1, 8192, 8192, 0, 80, 0, "fp16") > 32 << 20
+
+
+def test_stream_probe_rejects_small_buffers_before_the_library():
+    """The binding checks tensor sizes against the probe's contract (read mode
+    writes grid x 256 words; copy mode writes nbytes) and raises before any
+    device call."""
+    import torch
+    src = torch.zeros(1024, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        api.stream_probe(src, torch.zeros(4, dtype=torch.int32), 4096, 0)          # 2048 x 256 words
+    with pytest.raises(ValueError):
+        api.stream_probe(src, torch.zeros(255, dtype=torch.int32), 4096, 0, grid=1)
+    with pytest.raises(ValueError):
+        api.stream_probe(src, torch.zeros(1023, dtype=torch.int32), 4096, 1)
+    with pytest.raises(ValueError):
+        api.stream_probe(src, torch.zeros(1024, dtype=torch.int32), 8192, 1)     # src too small
