@@ -30,6 +30,23 @@ __device__ __forceinline__ void combine_row(const CombineArgs& a, uint32_t w, in
   const int layer = a.layer_begin + lr;
   uint32_t* outp = reinterpret_cast<uint32_t*>(
       a.out + ((((size_t)s * a.num_layers + layer) * kQHeads + h) * kHeadDim));
+  const size_t base = (((size_t)s * a.n_layers + lr) * kQHeads + h) * a.n_splits;
+  const float2* orow = reinterpret_cast<const float2*>(a.opart + base * kHeadDim) + lane;
+
+  // Loads whose addresses do not depend on the sequence's length are issued
+  // before it is read: the lane's own split statistics (lane k holds split k)
+  // and the first kPre splits' statistics and partial rows.  The workspace
+  // holds n_splits of each per row, so every such load is in bounds; entries
+  // past the sequence's own splits are stale and never used.
+  constexpr int kPre = 8;
+  const float2 mine = lane < a.n_splits ? a.ml[base + lane] : make_float2(-INFINITY, 0.f);
+  float2 pv[kPre], pov[kPre];
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) {
+    const int k = min(u, a.n_splits - 1);
+    pv[u] = a.ml[base + k];
+    pov[u] = orow[(size_t)k * (kHeadDim / 2)];
+  }
 
   int r0 = 0;
   const int nb = seq_blocks(a.seq_lens, a.meta_off, s, a.max_nb, a.total_blocks, a.status,
@@ -39,38 +56,44 @@ __device__ __forceinline__ void combine_row(const CombineArgs& a, uint32_t w, in
     return;
   }
   const int nsp = (nb + a.split_blocks - 1) / a.split_blocks;
-  const size_t base = (((size_t)s * a.n_layers + lr) * kQHeads + h) * a.n_splits;
 
   float M = -INFINITY;
-  for (int k = lane; k < nsp; k += 64) M = fmaxf(M, a.ml[base + k].x);
+  if (lane < nsp) M = fmaxf(M, mine.x);
+  for (int k = lane + 64; k < nsp; k += 64) M = fmaxf(M, a.ml[base + k].x);
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, xor_f(M, m));
   double L = 0.0;
-  if (M != -INFINITY)
-    for (int k = lane; k < nsp; k += 64) {
+  if (M != -INFINITY) {
+    if (lane < nsp) L += (double)mine.y * (double)__builtin_amdgcn_exp2f(mine.x - M);
+    for (int k = lane + 64; k < nsp; k += 64) {
       const float2 v = a.ml[base + k];
       L += (double)v.y * (double)__builtin_amdgcn_exp2f(v.x - M);
     }
+  }
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) L += __shfl_xor(L, m, 64);
   const bool dead = !(L > 0.0);
   const double invL = dead ? 0.0 : 1.0 / L;
 
-  for (int k = lane; k < nsp; k += 64) {
+  if (lane < nsp)
+    a.wsplit[base + lane] = dead ? 0.f : (float)((double)__builtin_amdgcn_exp2f(mine.x - M) * invL);
+  for (int k = lane + 64; k < nsp; k += 64) {
     const float2 v = a.ml[base + k];
     a.wsplit[base + k] = dead ? 0.f : (float)((double)__builtin_amdgcn_exp2f(v.x - M) * invL);
   }
-  // Weighted sum of the partial outputs in split order.  Eight splits per
-  // round: their statistics and partial rows are all loaded before the first
-  // is used, so eight 512-byte rows are in flight per wave instead of one.
+  // Weighted sum of the partial outputs in split order: the prefetched splits
+  // first, then rounds of eight whose statistics and partial rows are all
+  // loaded before the first is used (eight 512-byte rows in flight per wave).
   float o0 = 0.f, o1 = 0.f;
   auto add_split = [&](float2 v, float2 ov) {
     const float wk = dead ? 0.f : (float)((double)__builtin_amdgcn_exp2f(v.x - M) * invL);
     o0 = fmaf(wk, ov.x, o0);
     o1 = fmaf(wk, ov.y, o1);
   };
-  const float2* orow = reinterpret_cast<const float2*>(a.opart + base * kHeadDim) + lane;
-  int k = 0;
+#pragma unroll
+  for (int u = 0; u < kPre; ++u)
+    if (u < nsp) add_split(pv[u], pov[u]);
+  int k = kPre;
   for (; k + 8 <= nsp; k += 8) {
     float2 v[8], ov[8];
 #pragma unroll
@@ -186,12 +209,25 @@ __global__ void __launch_bounds__(kMassThreads) combine_mass(CombineArgs c, Mass
   const uint32_t mw = blockIdx.x - comb_wgs;
   const int s = (int)(mw / col_groups);
   const int cg = (int)(mw % col_groups);
+  const int rows = a.n_layers * kQHeads;
+  // With one row per thread and every row's splits fitting the registers, the
+  // statistics are loaded before the sequence's length is read (in bounds:
+  // the workspace holds n_splits per row; those past the sequence's own
+  // splits are stale and skipped below).
+  const bool early = a.n_splits <= kFusedRegSplits && rows <= kMassThreads;
+  float2 pre[kFusedRegSplits];
+  {
+    // threads past the last row re-read it (unused)
+    const float2* st = c.ml + ((size_t)s * rows + min((int)threadIdx.x, rows - 1)) * a.n_splits;
+#pragma unroll
+    for (int k = 0; k < kFusedRegSplits; ++k)
+      pre[k] = early ? st[min(k, a.n_splits - 1)] : make_float2(0.f, 0.f);
+  }
   int r0 = 0;
   const int nb = seq_blocks(a.seq_lens, a.meta_off, s, a.max_nb, a.total_blocks, a.status,
                             false, &r0);
   if (nb <= 0 || cg * kMassCols >= nb) return;
   const int nsp = (nb + a.split_blocks - 1) / a.split_blocks;
-  const int rows = a.n_layers * kQHeads;
   for (int row = threadIdx.x; row < rows; row += kMassThreads) {
     const float2* st = c.ml + ((size_t)s * rows + row) * a.n_splits;
     if (nsp <= kFusedRegSplits) {
@@ -199,8 +235,13 @@ __global__ void __launch_bounds__(kMassThreads) combine_mass(CombineArgs c, Mass
       // past nsp re-read the last split and are skipped): the loops below
       // would otherwise wait for one load per split, three times over.
       float2 v[kFusedRegSplits];
+      if (early) {
 #pragma unroll
-      for (int k = 0; k < kFusedRegSplits; ++k) v[k] = st[min(k, nsp - 1)];
+        for (int k = 0; k < kFusedRegSplits; ++k) v[k] = pre[k];
+      } else {
+#pragma unroll
+        for (int k = 0; k < kFusedRegSplits; ++k) v[k] = st[min(k, nsp - 1)];
+      }
       float M = -INFINITY;
 #pragma unroll
       for (int k = 0; k < kFusedRegSplits; ++k)
