@@ -167,7 +167,14 @@ size_t kvs_kivi_block_bytes(const kvs_shape* shape);
 /* Workspace bytes kvs_score_update needs (status header + per-chunk maxima). */
 size_t kvs_score_workspace_bytes(int32_t batch, int32_t max_blocks_per_seq);
 
+/* A fixed English name for a kvs_status code ("unknown status" for any other
+ * value).  The string is static: the caller does not free it. */
 const char* kvs_status_string(int code);
+/* The message of this host thread's last status-returning call: its error
+ * if it failed, "" if it succeeded (a thread-local buffer of at most 511
+ * characters; the size helpers above return no status and leave it alone).
+ * The pointer stays valid for the thread's life; the next status-returning
+ * call on the thread rewrites the text. */
 const char* kvs_last_error(void);
 
 /* Measurement hook.  With both events non-NULL (hipEvent_t passed as void*),

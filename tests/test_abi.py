@@ -382,3 +382,13 @@ def test_stream_probe_rejects_small_buffers_before_the_library():
         api.stream_probe(src, torch.zeros(1023, dtype=torch.int32), 4096, 1)
     with pytest.raises(ValueError):
         api.stream_probe(src, torch.zeros(1024, dtype=torch.int32), 8192, 1)     # src too small
+
+
+def test_last_error_is_set_by_a_failure_and_cleared_by_a_success():
+    """kvs_last_error: the failing call's message, then "" after a call that
+    returns KVS_OK (no device work: the decode-event hook only stores handles)."""
+    with pytest.raises(Exception):
+        api.set_decode_events(1, None)
+    assert "neither" in api.last_error()
+    api.set_decode_events(None, None)
+    assert api.last_error() == ""
