@@ -1,5 +1,5 @@
 """GPU: the decode-timing hook (kvs_set_decode_events).  With events set, each
-decode form (fp16 with one or two KV heads per wave, E4M3, KIVI, paired)
+decode form (fp16 with one or two KV heads per wave, E4M3, KIVI, paired fp16 and E4M3)
 records them around its decode kernel; the results are the bits of an untimed
 call, the timed interval lies inside the call's wall time, and turning the hook
 off leaves the events alone.  Both the default events and events without the
@@ -53,13 +53,13 @@ class _Events:
 
 
 def _workload(kind):
-    if kind in ("fp16-one-head", "e4m3", "kivi2", "fp16-paired"):
+    if kind in ("fp16-one-head", "e4m3", "kivi2", "fp16-paired", "e4m3-paired"):
         lens = [700, 100, 333, 288, 1000, 40, 517]
         wl = W.custom("timing", 2, lens, seed=31, spare_blocks=8,
-                      shared_prefix_tokens=288 if kind == "fp16-paired" else 0)
+                      shared_prefix_tokens=288 if kind.endswith("paired") else 0)
     else:   # sequences that fill their splits: one wave serves two KV heads
         wl = W.custom("timing2", 2, [1024, 1024], seed=32, spare_blocks=4)
-    if kind == "e4m3":
+    if kind.startswith("e4m3"):
         wl = W.as_e4m3(wl)
     elif kind == "kivi2":
         wl = W.as_kivi2(wl)
@@ -67,14 +67,15 @@ def _workload(kind):
 
 
 def _session(m, kind, split):
-    if kind == "fp16-paired":
+    if kind.endswith("paired"):
         return DecodeSession(m, split_blocks=split, pair_role=pair_plan(m.table_host, m.blocks))
     return DecodeSession(m, split_blocks=split)
 
 
 @pytest.mark.parametrize("flags", [0, DISABLE_SYSTEM_FENCE])
 @pytest.mark.parametrize("kind,split", [("fp16-one-head", 8), ("fp16-two-heads", 16),
-                                        ("e4m3", 8), ("kivi2", 16), ("fp16-paired", 8)])
+                                        ("e4m3", 8), ("kivi2", 16), ("fp16-paired", 8),
+                                        ("e4m3-paired", 8)])
 def test_timed_decode_gives_untimed_bits(kind, split, flags):
     _case(f"{kind} split_blocks={split}, decode with and without timing events, flags={flags:#x}")
     m = _workload(kind)
